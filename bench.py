@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Benchmark of the GDN layer forward on one MI355X.
+
+One step = one call of the whole layer (short conv + SiLU, L2 norm, chunked
+gated delta rule, gated RMS norm, final state) over the Wan2.1-1.3B-shaped
+workload at 480x832, 81 frames: B=1, T=32760 (21x30x52 latent tokens), H=12,
+d=128, bf16 I/O with an fp32 state, seeded synthetic inputs already resident
+in device memory.
+
+Prints ONE JSON line on stdout.  Beside the headline tokens/s it reports:
+  roofline     -- the dominant kernel's algorithmic bytes per launch over its
+                  average duration (HIP events recorded on the launch stream
+                  around each kernel, live in this run) against the MI355X
+                  HBM peak of 8 TB/s;
+  layer        -- the whole call against the layer's algorithmic HBM floor of
+                  1288 B per token-head (q, k, v, gate in, y out in bf16, plus
+                  fp32 log a and b);
+  cpu_baseline -- the fp64 oracle (the test yardstick) timed on this host's
+                  cores on the same workload, and the parity of the last timed
+                  GPU output against it.
+Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# Algorithmic bytes per token-head of each kernel's own inputs and outputs
+# (bf16 I/O, d = 128, chunk 64).  The prep kernel reads q, k, v (768 B) and
+# log a, b (8 B) and writes the chunk record (5 matrices of 64 x 128 bf16 per
+# 64 tokens = 1280 B); the state kernel reads the record once (1280 B) and
+# writes the unnormalised output (fp32, 512 B) and partial sums of squares
+# (8 x 4 B); the norm kernel reads those and the gate (256 B) and writes y
+# (256 B).
+KERNEL_BYTES_PER_TOKEN_HEAD = {
+    "gdn_prep_kernel": 768 + 8 + 1280,
+    "gdn_state_kernel": 1280 + 512 + 32,
+    "gdn_norm_kernel": 512 + 32 + 256 + 256,
+}
+LAYER_BYTES_PER_TOKEN_HEAD = 4 * 128 * 2 + 128 * 2 + 8
+
+
+class HipEvents:
+    """Minimal hipEvent API through ctypes (events on a given stream)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        evs = (ctypes.c_void_p * n)()
+        for i in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            evs[i] = e
+        return evs
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def sync(self, e):
+        self.hip.hipEventSynchronize(e)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=1, help="workload id (default 1: T=32760 H=12 d=128)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: all available)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import gdn_inputs
+    import linear_attention_token_fwd_amd as gdn
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        return 1
+    w = gdn_inputs.WORKLOADS[args.workload]
+    log(f"workload {w.id}: {w.name}")
+    t0 = time.time()
+    inp = gdn_inputs.generate(w)
+    log(f"inputs generated in {time.time() - t0:.1f} s")
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    d = gdn.to_device(inp, dtype=dt)
+    B, T, H, D = inp["q"].shape
+    out = torch.empty((B, T, H, D), dtype=dt, device="cuda")
+    S_T = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
+    S_T_rev = torch.empty_like(S_T) if w.bidirectional else None
+    io = gdn.GDN_BF16 if w.dtype == "bf16" else gdn.GDN_F32
+    ws_bytes = (gdn.gdn_fwd_bidir_workspace_bytes if w.bidirectional else gdn.gdn_fwd_workspace_bytes)(
+        B, T, H, D, io)
+    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    lib = gdn.load()
+    p = gdn.make_params(d["q"], d["k"], d["v"], d["log_a"], d["beta"], d["gate"], d["conv_q"], d["conv_k"],
+                        d["conv_v"], d["norm_w"], d["S0"], out, S_T, workspace)
+    stream = torch.cuda.Stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    rev_ptr = ctypes.c_void_p(S_T_rev.data_ptr() if S_T_rev is not None else None)
+
+    def step():
+        if w.bidirectional:
+            st = lib.gdn_fwd_bidir(ctypes.byref(p), rev_ptr, sptr)
+        else:
+            st = lib.gdn_fwd(ctypes.byref(p), sptr)
+        if st != gdn.GDN_OK:
+            raise gdn.GdnError(st, "step")
+
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done")
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_s = B * T / (ms_per_step * 1e-3)
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step, {tokens_per_s:.4e} tokens/s")
+
+    # ---- per-kernel durations from HIP events on the launch stream
+    ev = HipEvents()
+    bid = 1 if w.bidirectional else 0
+    nl = lib.gdn_fwd_launch_count(ctypes.byref(p), bid)
+    names = [lib.gdn_fwd_launch_name(ctypes.byref(p), bid, i).decode() for i in range(nl)]
+    evs = [ev.create(nl + 1) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        st = lib.gdn_fwd_timed(ctypes.byref(p), rev_ptr, bid, evs[i], nl + 1, sptr)
+        if st != gdn.GDN_OK:
+            raise gdn.GdnError(st, "gdn_fwd_timed")
+    torch.cuda.synchronize()
+    per = {}
+    totals = []
+    for i in range(args.steps):
+        ev.sync(evs[i][nl])
+        totals.append(ev.elapsed_ms(evs[i][0], evs[i][nl]))
+        for j, nm in enumerate(names):
+            per.setdefault(nm, []).append(ev.elapsed_ms(evs[i][j], evs[i][j + 1]))
+    # a kernel launched more than once per call (two scans) is averaged per launch
+    launches_per_call = {nm: names.count(nm) for nm in set(names)}
+    kernels = {}
+    token_heads = B * T * H
+    for nm, vals in per.items():
+        per_launch_ms = float(np.mean(vals))
+        total_ms = per_launch_ms * launches_per_call[nm]
+        bytes_per_launch = KERNEL_BYTES_PER_TOKEN_HEAD[nm] * token_heads
+        kernels[nm] = {"launches_per_call": launches_per_call[nm], "avg_ms": per_launch_ms,
+                       "ms_per_call": total_ms, "bytes_per_launch": bytes_per_launch,
+                       "GBps": bytes_per_launch / (per_launch_ms * 1e-3) / 1e9}
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_call"])
+    kd = kernels[dom]
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(kd["GBps"], 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(kd["GBps"] / HBM_PEAK_GBS, 4), "traffic": None,
+                "avg_launch_ms": round(kd["avg_ms"], 5)}
+    call_ms = float(np.mean(totals))
+    layer_bytes = LAYER_BYTES_PER_TOKEN_HEAD * token_heads * (2 if w.bidirectional else 1)
+    layer = {"algorithmic_bytes": layer_bytes, "floor_ms": layer_bytes / (HBM_PEAK_GBS * 1e9) * 1e3,
+             "call_ms_events": round(call_ms, 5),
+             "frac_of_hbm_roofline": round(layer_bytes / (HBM_PEAK_GBS * 1e9) * 1e3 / ms_per_step, 4)}
+    for nm, k in kernels.items():
+        log(f"  {nm}: {k['avg_ms']:.4f} ms/launch x{k['launches_per_call']}, {k['GBps']:.0f} GB/s")
+
+    # ---- CPU baseline: the fp64 oracle on this host, same workload
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+        y_gpu = out.double().cpu().numpy()
+        st_gpu = S_T.double().cpu().numpy()
+        log("running the oracle on the host ...")
+        t1 = time.perf_counter()
+        if w.bidirectional:
+            ry, rs, _, used = oracle.inputs_for(inp, threads=args.cpu_threads, bidir=True)
+        else:
+            ry, rs, used = oracle.inputs_for(inp, threads=args.cpu_threads)
+        cpu_s = time.perf_counter() - t1
+        cpu = {"value": round(B * T / cpu_s, 2), "unit": "tokens/s", "cores": int(used), "kind": "oracle",
+               "sample": f"the whole workload ({B}x{T} tokens x {H} heads, fp64, one thread per head"
+                         f"{' and direction' if w.bidirectional else ''}), {cpu_s:.2f} s wall",
+               "host_cores_available": len(os.sched_getaffinity(0))}
+
+        def rel(a, b):
+            return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+        parity = {"y_rel_l2": rel(y_gpu, ry), "S_T_rel_l2": rel(st_gpu, rs)}
+        log(f"oracle {cpu_s:.2f} s on {used} threads; parity {parity}")
+
+    res = {
+        "metric": "GDN layer fwd tokens/s at T=32760,H=12,d=128 bf16; % of MI355X roofline",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "T": T, "H": H, "d": D, "chunk": 64,
+                   "bidirectional": w.bidirectional},
+        "roofline": roofline,
+        "layer": layer,
+        "kernels": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kernels.items()},
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -64,9 +64,12 @@ def round_bf16(a: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bf16 (ties to even); returns
     float32 holding the rounded values.  NaN/Inf are not expected here."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return (u.astype(np.uint32) << 16).view(np.float32)
+    u = a.view(np.uint32)
+    lsb = (u >> 16) & np.uint32(1)
+    r = u + np.uint32(0x7FFF)
+    r += lsb
+    r &= np.uint32(0xFFFF0000)
+    return r.view(np.float32)
 
 
 def bf16_bits(a: np.ndarray) -> np.ndarray:

@@ -1,0 +1,150 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) Gated DeltaNet layer forward.
+ *
+ * The operation.  The LinMorph project page ("Abstract" and "Why learn the
+ * initialization?") replaces the softmax self-attention of a video diffusion
+ * transformer with a Gated DeltaNet (GDN) token mixer whose parameter groups
+ * are update gates, decay terms, short convolutions and normalisation
+ * parameters; the VMonarch page (section 2, "Efficient Attention
+ * Mechanisms", ref. [57]) files GDN under linear attention with an expanded
+ * recurrent state.  One call computes, for every batch row b and head h of a
+ * flattened video token sequence of length T:
+ *
+ *   1. short convolution + SiLU on q, k and v, per channel c:
+ *        x~_t[c] = SiLU( sum_{j=0..3} w[c][j] * x_{t-3+j}[c] ),  x_{<0} = 0
+ *   2. unit-L2 queries and keys:  q^_t = q~_t / sqrt(|q~_t|^2 + eps_l2),
+ *      likewise k^_t;  v^_t = v~_t
+ *   3. the gated delta rule with state S in R^{Dv x Dk} (S_{-1} = S0):
+ *        S_t = a_t S_{t-1} (I - b_t k^_t k^_t^T) + b_t v^_t k^_t^T,
+ *        o_t = S_t q^_t,   a_t = exp(log_a_t)
+ *   4. gated RMS normalisation over the Dv channels:
+ *        y_t = o_t / sqrt(mean(o_t^2) + eps_norm) * norm_w * SiLU(gate_t)
+ *   5. S_T = the state after the last token.
+ *
+ * Layouts (row-major, contiguous, no strides):
+ *   q, k          [B, T, H, Dk]   io_dtype
+ *   v, gate, o    [B, T, H, Dv]   io_dtype
+ *   log_a, beta   [B, T, H]       float32  (log_a <= 0 expected, beta in [0,1])
+ *   conv_q, conv_k [H*Dk, 4], conv_v [H*Dv, 4]  float32; tap 3 multiplies
+ *                 the current token, tap j the token 3-j steps earlier
+ *   norm_w        [H, Dv]         float32, or NULL for all ones
+ *   S0, S_T       [B, H, Dv, Dk]  float32, S0 NULL means zeros,
+ *                 S_T NULL means not written
+ *
+ * Ownership.  Every pointer is a device pointer owned by the caller, except
+ * the params struct itself (host memory, read during the call only).  The
+ * library allocates and frees nothing and keeps no pointer after return; the
+ * caller supplies a device workspace of at least gdn_fwd_workspace_bytes()
+ * (or gdn_fwd_bidir_workspace_bytes()) bytes, 256-byte aligned, which the
+ * call may overwrite entirely.
+ *
+ * Execution.  Calls enqueue kernels on `stream` (NULL = the null stream) and
+ * return without waiting.  They keep no global state, so calls on different
+ * buffers may run concurrently; two in-flight calls must not share a
+ * workspace.
+ *
+ * Errors.  All checks run on the host before anything is enqueued; on any
+ * error nothing is launched and no output is touched.  Launch failures
+ * return GDN_ERR_HIP.  Faults inside kernels surface at the caller's next
+ * synchronisation, as usual in HIP.  No C++ exception crosses this ABI.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t; /* hipStream_t is `struct ihipStream_t *` */
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_INVALID_ARG = 1, /* NULL required pointer, bad size, non-finite or negative eps, aliasing */
+    GDN_ERR_UNSUPPORTED = 2, /* a valid request this build has no kernel for (see gdn_fwd) */
+    GDN_ERR_ALIGNMENT = 3,   /* tensors not 16-byte aligned, workspace not 256-byte aligned */
+    GDN_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required */
+    GDN_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+typedef struct gdn_fwd_params {
+    int B, T, H, Dk, Dv;      /* B, T, H >= 1; Dk == Dv */
+    gdn_dtype io_dtype;       /* dtype of q, k, v, gate and o */
+    const void *q, *k, *v;
+    const float *log_a;       /* the decay a_t in log space */
+    const float *beta;        /* the update gate b_t */
+    const void *gate;         /* output gate, SiLU-activated */
+    const float *conv_q, *conv_k, *conv_v;
+    const float *norm_w;      /* NULL: ones */
+    float eps_l2, eps_norm;   /* >= 0 and finite; 1e-6 in the shipped workloads */
+    const float *S0;          /* NULL: zero initial state */
+    void *o;                  /* output y, overwritten */
+    float *S_T;               /* final state, or NULL */
+    int reverse;              /* 0: scan t = 0..T-1; 1: scan t = T-1..0, i.e. the
+                                 layer applied to the time-reversed sequence with
+                                 its output written back in input order */
+    void *workspace;
+    size_t workspace_bytes;
+} gdn_fwd_params;
+
+/*
+ * Device workspace gdn_fwd needs for these sizes (only B, T, H, Dk, Dv and
+ * io_dtype are read).  Returns 0 if the sizes are invalid.
+ */
+size_t gdn_fwd_workspace_bytes(const gdn_fwd_params *p);
+
+/*
+ * One GDN layer forward (steps 1-5 above), in scan order given by p->reverse.
+ * Supported: io_dtype GDN_BF16 with Dk = Dv in {64, 128}, and GDN_F32 with
+ * Dk = Dv = 64; other combinations return GDN_ERR_UNSUPPORTED.  With bf16
+ * I/O the matrix products take bf16 operands with fp32 accumulation and an
+ * fp32 master state; with fp32 I/O they run in fp32 throughout.
+ */
+gdn_status gdn_fwd(const gdn_fwd_params *p, struct ihipStream_t *stream);
+
+/* Workspace for gdn_fwd_bidir (two scans' partial results at once). */
+size_t gdn_fwd_bidir_workspace_bytes(const gdn_fwd_params *p);
+
+/*
+ * Bidirectional stress variant: the whole layer run forward in time and on
+ * the time-reversed sequence (each scan with its own causal convolution and
+ * its own output normalisation, both from S0), the two outputs added in fp32
+ * and stored once into p->o.  p->reverse must be 0.  p->S_T receives the
+ * forward scan's final state and S_T_rev the reversed scan's (either may be
+ * NULL).
+ */
+gdn_status gdn_fwd_bidir(const gdn_fwd_params *p, float *S_T_rev,
+                         struct ihipStream_t *stream);
+
+/*
+ * Measurement aids.  A call is a fixed short sequence of kernel launches on
+ * one stream; gdn_fwd_launch_count() says how many (bidirectional != 0 for
+ * gdn_fwd_bidir), or -1 for invalid or unsupported sizes, and
+ * gdn_fwd_launch_name() names launch i (static string, NULL if out of range).
+ * gdn_fwd_timed() does exactly what gdn_fwd (bidirectional == 0) or
+ * gdn_fwd_bidir (bidirectional != 0; S_T_rev as there) does, and in addition
+ * records events[i] on the stream right before launch i and events[count]
+ * after the last one, so each kernel's duration is the elapsed time between
+ * consecutive events.  events: n_events >= count + 1 caller-created HIP
+ * events (hipEvent_t is `struct ihipEvent_t *`); otherwise
+ * GDN_ERR_INVALID_ARG and nothing is launched.
+ */
+struct ihipEvent_t;
+int gdn_fwd_launch_count(const gdn_fwd_params *p, int bidirectional);
+const char *gdn_fwd_launch_name(const gdn_fwd_params *p, int bidirectional, int i);
+gdn_status gdn_fwd_timed(const gdn_fwd_params *p, float *S_T_rev, int bidirectional,
+                         struct ihipEvent_t **events, int n_events,
+                         struct ihipStream_t *stream);
+
+/* Static, human-readable text for a status code. */
+const char *gdn_status_string(gdn_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

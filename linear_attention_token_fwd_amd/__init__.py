@@ -1,0 +1,218 @@
+"""Python binding of libgdn.so, the gfx950 Gated DeltaNet layer forward.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+behind the C ABI of ``include/gdn.h``; torch supplies device memory and the
+stream.  The names match the C entry points.  If the library has not been
+built (``python -m linear_attention_token_fwd_amd.build``) every entry point
+raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_ALIGNMENT, GDN_ERR_WORKSPACE, GDN_ERR_HIP = range(6)
+GDN_F32, GDN_BF16 = 0, 1
+
+EXPORTS = ("gdn_fwd", "gdn_fwd_bidir", "gdn_fwd_workspace_bytes", "gdn_fwd_bidir_workspace_bytes",
+           "gdn_fwd_launch_count", "gdn_fwd_launch_name", "gdn_fwd_timed", "gdn_status_string")
+
+
+class GdnFwdParams(ctypes.Structure):
+    """Mirror of ``gdn_fwd_params`` in include/gdn.h."""
+    _fields_ = [
+        ("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int),
+        ("Dk", ctypes.c_int), ("Dv", ctypes.c_int), ("io_dtype", ctypes.c_int),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("log_a", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("gate", ctypes.c_void_p),
+        ("conv_q", ctypes.c_void_p), ("conv_k", ctypes.c_void_p), ("conv_v", ctypes.c_void_p),
+        ("norm_w", ctypes.c_void_p), ("eps_l2", ctypes.c_float), ("eps_norm", ctypes.c_float),
+        ("S0", ctypes.c_void_p), ("o", ctypes.c_void_p), ("S_T", ctypes.c_void_p),
+        ("reverse", ctypes.c_int), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {gdn_status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def load(path: str | None = None):
+    """Load libgdn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"libgdn.so not built at {p}; run python -m linear_attention_token_fwd_amd.build")
+    lib = ctypes.CDLL(p)
+    P = ctypes.POINTER(GdnFwdParams)
+    lib.gdn_fwd.argtypes = [P, ctypes.c_void_p]
+    lib.gdn_fwd.restype = ctypes.c_int
+    lib.gdn_fwd_bidir.argtypes = [P, ctypes.c_void_p, ctypes.c_void_p]
+    lib.gdn_fwd_bidir.restype = ctypes.c_int
+    lib.gdn_fwd_workspace_bytes.argtypes = [P]
+    lib.gdn_fwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdn_fwd_bidir_workspace_bytes.argtypes = [P]
+    lib.gdn_fwd_bidir_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdn_fwd_launch_count.argtypes = [P, ctypes.c_int]
+    lib.gdn_fwd_launch_count.restype = ctypes.c_int
+    lib.gdn_fwd_launch_name.argtypes = [P, ctypes.c_int, ctypes.c_int]
+    lib.gdn_fwd_launch_name.restype = ctypes.c_char_p
+    lib.gdn_fwd_timed.argtypes = [P, ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_void_p),
+                                  ctypes.c_int, ctypes.c_void_p]
+    lib.gdn_fwd_timed.restype = ctypes.c_int
+    lib.gdn_status_string.argtypes = [ctypes.c_int]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def gdn_status_string(status: int) -> str:
+    return load().gdn_status_string(int(status)).decode()
+
+
+def _sizes(B, T, H, D, dtype) -> GdnFwdParams:
+    p = GdnFwdParams()
+    p.B, p.T, p.H, p.Dk, p.Dv = B, T, H, D, D
+    p.io_dtype = dtype
+    return p
+
+
+def gdn_fwd_workspace_bytes(B: int, T: int, H: int, D: int, io_dtype: int = GDN_BF16) -> int:
+    return load().gdn_fwd_workspace_bytes(ctypes.byref(_sizes(B, T, H, D, io_dtype)))
+
+
+def gdn_fwd_bidir_workspace_bytes(B: int, T: int, H: int, D: int, io_dtype: int = GDN_BF16) -> int:
+    return load().gdn_fwd_bidir_workspace_bytes(ctypes.byref(_sizes(B, T, H, D, io_dtype)))
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def make_params(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, out, S_T,
+                workspace, eps_l2=1e-6, eps_norm=1e-6, reverse=False) -> GdnFwdParams:
+    """Fill the params struct from torch tensors (no checks beyond shape
+    reading: the library validates everything)."""
+    import torch
+    B, T, H, D = q.shape
+    p = GdnFwdParams()
+    p.B, p.T, p.H, p.Dk, p.Dv = B, T, H, D, v.shape[3]
+    p.io_dtype = GDN_BF16 if q.dtype == torch.bfloat16 else GDN_F32
+    p.q, p.k, p.v, p.gate = _ptr(q), _ptr(k), _ptr(v), _ptr(gate)
+    p.log_a, p.beta = _ptr(log_a), _ptr(beta)
+    p.conv_q, p.conv_k, p.conv_v = _ptr(conv_q), _ptr(conv_k), _ptr(conv_v)
+    p.norm_w, p.S0 = _ptr(norm_w), _ptr(S0)
+    p.eps_l2, p.eps_norm = eps_l2, eps_norm
+    p.o, p.S_T = _ptr(out), _ptr(S_T)
+    p.reverse = 1 if reverse else 0
+    p.workspace = _ptr(workspace)
+    p.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return p
+
+
+def _check(t, name, dtype, shape):
+    import torch
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _prepare(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, out, S_T):
+    import torch
+    B, T, H, D = q.shape
+    io = q.dtype
+    if io not in (torch.bfloat16, torch.float32):
+        raise TypeError("q, k, v, gate must be bfloat16 or float32")
+    f32 = torch.float32
+    for t, name, dt, shp in ((q, "q", io, (B, T, H, D)), (k, "k", io, (B, T, H, D)),
+                             (v, "v", io, (B, T, H, D)), (gate, "gate", io, (B, T, H, D)),
+                             (log_a, "log_a", f32, (B, T, H)), (beta, "beta", f32, (B, T, H)),
+                             (conv_q, "conv_q", f32, (H * D, 4)), (conv_k, "conv_k", f32, (H * D, 4)),
+                             (conv_v, "conv_v", f32, (H * D, 4)), (norm_w, "norm_w", f32, (H, D)),
+                             (S0, "S0", f32, (B, H, D, D)), (out, "out", io, (B, T, H, D)),
+                             (S_T, "S_T", f32, (B, H, D, D))):
+        _check(t, name, dt, shp)
+    if out is None:
+        out = torch.empty((B, T, H, D), dtype=io, device=q.device)
+    return out
+
+
+def gdn_fwd(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w=None, S0=None,
+            eps_l2=1e-6, eps_norm=1e-6, reverse=False, out=None, S_T=None, want_state=True,
+            workspace=None, stream=None):
+    """One GDN layer forward on device tensors.  Returns (out, S_T)."""
+    import torch
+    lib = load()
+    out = _prepare(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, out, S_T)
+    B, T, H, D = q.shape
+    if S_T is None and want_state:
+        S_T = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+    need = gdn_fwd_workspace_bytes(B, T, H, D, GDN_BF16 if q.dtype == torch.bfloat16 else GDN_F32)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    p = make_params(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, out, S_T,
+                    workspace, eps_l2, eps_norm, reverse)
+    s = (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
+    st = lib.gdn_fwd(ctypes.byref(p), ctypes.c_void_p(s))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_fwd")
+    return out, S_T
+
+
+def gdn_fwd_bidir(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w=None, S0=None,
+                  eps_l2=1e-6, eps_norm=1e-6, out=None, S_T=None, S_T_rev=None, want_state=True,
+                  workspace=None, stream=None):
+    """Forward and time-reversed scans, outputs added.  Returns (out, S_T, S_T_rev)."""
+    import torch
+    lib = load()
+    out = _prepare(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, out, S_T)
+    B, T, H, D = q.shape
+    _check(S_T_rev, "S_T_rev", torch.float32, (B, H, D, D))
+    if want_state:
+        if S_T is None:
+            S_T = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+        if S_T_rev is None:
+            S_T_rev = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+    need = gdn_fwd_bidir_workspace_bytes(B, T, H, D, GDN_BF16 if q.dtype == torch.bfloat16 else GDN_F32)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    p = make_params(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, out, S_T,
+                    workspace, eps_l2, eps_norm, False)
+    s = (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
+    st = lib.gdn_fwd_bidir(ctypes.byref(p), ctypes.c_void_p(_ptr(S_T_rev)), ctypes.c_void_p(s))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_fwd_bidir")
+    return out, S_T, S_T_rev
+
+
+def to_device(inp: dict, device="cuda", dtype=None):
+    """Move a seeded input dict (float32 numpy arrays holding exact values) to
+    device tensors: q, k, v, gate in the workload's I/O dtype, the rest fp32."""
+    import torch
+    out = {}
+    for key, val in inp.items():
+        if val is None:
+            out[key] = None
+            continue
+        t = torch.from_numpy(val)
+        if key in ("q", "k", "v", "gate") and dtype is not None:
+            t = t.to(dtype)
+        out[key] = t.to(device).contiguous()
+    return out

@@ -248,5 +248,7 @@ int oracle_gdn_fwd(int B, long T, int H, int Dk, int Dv, const float *q,
         free(raw); free(tmp); free(qh); free(kh); free(vh); free(g);
         free(la); free(be); free(S); free(w4); free(nw);
     }
+    if (used > ntask)
+        used = (int)ntask; /* threads beyond the task count stay idle */
     return failed ? -1 : used;
 }
