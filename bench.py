@@ -41,15 +41,44 @@ def log(msg):
 # (bf16 I/O, d = 128, chunk 64).  The prep kernel reads q, k, v (768 B) and
 # log a, b (8 B) and writes the chunk record (5 matrices of 64 x 128 bf16 per
 # 64 tokens = 1280 B); the state kernel reads the record once (1280 B) and
-# writes the unnormalised output (fp32, 512 B) and partial sums of squares
-# (8 x 4 B); the norm kernel reads those and the gate (256 B) and writes y
-# (256 B).
+# writes the unnormalised output (fp32, 512 B); the norm kernel reads that
+# and the gate (256 B) and writes y (256 B).
 KERNEL_BYTES_PER_TOKEN_HEAD = {
     "gdn_prep_kernel": 768 + 8 + 1280,
-    "gdn_state_kernel": 1280 + 512 + 32,
-    "gdn_norm_kernel": 512 + 32 + 256 + 256,
+    "gdn_state_kernel": 1280 + 512,
+    "gdn_norm_kernel": 512 + 256 + 256,
 }
 LAYER_BYTES_PER_TOKEN_HEAD = 4 * 128 * 2 + 128 * 2 + 8
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "linear_attention_token_fwd_amd", "csrc")
+
+
+def csrc_hash() -> str:
+    """sha256 over the HIP sources, to tell whether a stored profile still
+    describes the kernels being run."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(kernel: str, workload_tag: str):
+    """HBM bytes per dispatch of `kernel` from the committed rocprofv3 summary
+    (FETCH_SIZE + WRITE_SIZE counters, copy-calibrated), or None if there is
+    none or it was taken on different kernel sources."""
+    path = os.path.join(HERE, "profiles", f"gdn_kernels_{workload_tag}.txt")
+    if not os.path.exists(path):
+        return None
+    src, val = None, None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("source_sha256:"):
+                src = line.split(":", 1)[1].strip()
+            if line.startswith(f"traffic_bytes[{kernel}]:"):
+                val = float(line.split(":", 1)[1])
+    return val if src == csrc_hash() else None
 
 
 class HipEvents:
@@ -91,6 +120,9 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=1, help="workload id (default 1: T=32760 H=12 d=128)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: all available)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of 1 GiB (read 1 GiB, write 1 GiB) three times, to "
+                         "calibrate the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
@@ -106,6 +138,15 @@ def main() -> int:
     if not torch.cuda.is_available():
         log("no GPU visible")
         return 1
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "dispatches": 3}), flush=True)
+        return 0
     w = gdn_inputs.WORKLOADS[args.workload]
     log(f"workload {w.id}: {w.name}")
     t0 = time.time()
@@ -183,8 +224,11 @@ def main() -> int:
                        "GBps": bytes_per_launch / (per_launch_ms * 1e-3) / 1e9}
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_call"])
     kd = kernels[dom]
+    tag = f"T{T}_H{H}_d{D}_{w.dtype}" + ("_bidir" if w.bidirectional else "")
+    traffic = profiled_traffic(dom, tag)
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(kd["GBps"], 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(kd["GBps"] / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(kd["GBps"] / HBM_PEAK_GBS, 4),
+                "traffic": None if traffic is None else round(traffic),
                 "avg_launch_ms": round(kd["avg_ms"], 5)}
     call_ms = float(np.mean(totals))
     layer_bytes = LAYER_BYTES_PER_TOKEN_HEAD * token_heads * (2 if w.bidirectional else 1)

@@ -18,7 +18,7 @@ constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t rec, gC, ows, ps, total;  // byte offsets (total = size)
+    size_t rec, gC, ows, total;  // byte offsets (total = size)
 };
 
 int n_chunks(int T) { return (T + gdn::kChunk - 1) / gdn::kChunk; }
@@ -36,8 +36,6 @@ Layout layout(const gdn_fwd_params *p, int scans) {
     off += round_up(B * H * NC * sizeof(float));
     L.ows = off;
     off += scans * round_up(B * H * NC * 64 * D * sizeof(float));
-    L.ps = off;
-    off += scans * round_up(B * H * (D / 16) * NC * 64 * sizeof(float));
     L.total = off;
     return L;
 }
@@ -141,10 +139,10 @@ struct Plan {
     }
 };
 
-// One scan: prep + state.  ows/ps receive that scan's unnormalised output.
+// One scan: prep + state.  ows receives that scan's unnormalised output.
 template <class T, int D>
 gdn_status plan_scan(Plan &plan, const gdn_fwd_params *p, int reverse, const float *S0, float *S_T, float *ows,
-                     float *ps, char *ws, const Layout &L) {
+                     char *ws, const Layout &L) {
     const int NC = n_chunks(p->T);
     gdn::PrepArgs pa;
     pa.B = p->B; pa.T = p->T; pa.H = p->H; pa.NC = NC; pa.reverse = reverse;
@@ -163,18 +161,18 @@ gdn_status plan_scan(Plan &plan, const gdn_fwd_params *p, int reverse, const flo
     sa.B = p->B; sa.T = p->T; sa.H = p->H; sa.NC = NC;
     sa.rec = ws + L.rec;
     sa.gC = reinterpret_cast<const float *>(ws + L.gC);
-    sa.S0 = S0; sa.S_T = S_T; sa.ows = ows; sa.ps = ps;
-    plan.add(reinterpret_cast<const void *>(&gdn::gdn_state_kernel<T, D>), dim3(D / 16, p->H, p->B),
+    sa.S0 = S0; sa.S_T = S_T; sa.ows = ows;
+    const int used = p->B * p->H * (D / 16);
+    plan.add(reinterpret_cast<const void *>(&gdn::gdn_state_kernel<T, D>), dim3((used + 7) / 8 * 8),
              dim3(gdn::kThreads), 0, sa);
     return GDN_OK;
 }
 
 template <class T, int D>
-void plan_norm(Plan &plan, const gdn_fwd_params *p, int reverse, const float *ows, const float *ps,
-               const float *ows2, const float *ps2) {
+void plan_norm(Plan &plan, const gdn_fwd_params *p, int reverse, const float *ows, const float *ows2) {
     gdn::NormArgs na;
     na.B = p->B; na.T = p->T; na.H = p->H; na.NC = n_chunks(p->T); na.reverse = reverse;
-    na.ows = ows; na.ps = ps; na.ows2 = ows2; na.ps2 = ps2;
+    na.ows = ows; na.ows2 = ows2;
     na.gate = p->gate; na.norm_w = p->norm_w; na.eps = p->eps_norm; na.out = p->o;
     constexpr int tok_per_block = gdn::kThreads / (D / 8);
     plan.add(reinterpret_cast<const void *>(&gdn::gdn_norm_kernel<T, D>),
@@ -186,20 +184,17 @@ gdn_status plan_fwd(Plan &plan, const gdn_fwd_params *p, const float *S_T_rev, b
     const Layout L = layout(p, bidir ? 2 : 1);
     char *ws = static_cast<char *>(p->workspace);
     float *ows = reinterpret_cast<float *>(ws + L.ows);
-    float *ps = reinterpret_cast<float *>(ws + L.ps);
     const size_t ows_bytes = round_up((size_t)p->B * p->H * n_chunks(p->T) * 64 * D * sizeof(float));
-    const size_t ps_bytes = round_up((size_t)p->B * p->H * (D / 16) * n_chunks(p->T) * 64 * sizeof(float));
-    gdn_status st = plan_scan<T, D>(plan, p, bidir ? 0 : p->reverse, p->S0, p->S_T, ows, ps, ws, L);
+    gdn_status st = plan_scan<T, D>(plan, p, bidir ? 0 : p->reverse, p->S0, p->S_T, ows, ws, L);
     if (st != GDN_OK) return st;
     if (!bidir) {
-        plan_norm<T, D>(plan, p, p->reverse, ows, ps, nullptr, nullptr);
+        plan_norm<T, D>(plan, p, p->reverse, ows, nullptr);
         return GDN_OK;
     }
     float *ows2 = reinterpret_cast<float *>(ws + L.ows + ows_bytes);
-    float *ps2 = reinterpret_cast<float *>(ws + L.ps + ps_bytes);
-    st = plan_scan<T, D>(plan, p, 1, p->S0, const_cast<float *>(S_T_rev), ows2, ps2, ws, L);
+    st = plan_scan<T, D>(plan, p, 1, p->S0, const_cast<float *>(S_T_rev), ows2, ws, L);
     if (st != GDN_OK) return st;
-    plan_norm<T, D>(plan, p, 0, ows, ps, ows2, ps2);
+    plan_norm<T, D>(plan, p, 0, ows, ows2);
     return GDN_OK;
 }
 

@@ -63,13 +63,12 @@ struct StateArgs {
     const float *S0;  // [B][H][D][D] or null
     float *S_T;       // [B][H][D][D] or null
     float *ows;       // [B][H][NC*64][D] unnormalised o, scan order
-    float *ps;        // [B][H][D/16][NC*64] partial sums of o^2 per 16 channels
 };
 
 struct NormArgs {
     int B, T, H, NC, reverse;
-    const float *ows, *ps;      // first (or only) scan
-    const float *ows2, *ps2;    // time-reversed scan, or null
+    const float *ows;           // first (or only) scan
+    const float *ows2;          // time-reversed scan, or null
     const void *gate;
     const float *norm_w;        // [H][D] or null
     float eps;
@@ -123,82 +122,137 @@ __device__ __forceinline__ float row_frag(const float *row, int kb, int g) {
 }
 
 // ====================================================================== prep
+// 16 x 16 x 16 products (one 16-token block of the triangular solve).  A K=16
+// fragment holds, per lane (r, g), the 4 values k = 4g + e (e = 0..3): one
+// bf16 16x16x16 instruction, or four fp32 16x16x4 instructions.
+template <class T> struct K16;
+template <> struct K16<bf16> {
+    typedef bf16x4 frag;
+    static __device__ __forceinline__ floatx4 mma(const frag &a, const frag &b, const floatx4 &c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ frag from4(const floatx4 &x) {
+        return bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+    }
+};
+template <> struct K16<float> {
+    typedef floatx4 frag;
+    static __device__ __forceinline__ floatx4 mma(const frag &a, const frag &b, floatx4 c) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], c, 0, 0, 0);
+        return c;
+    }
+    static __device__ __forceinline__ frag from4(const floatx4 &x) { return x; }
+};
+
+// 8 raw input values of one token row, kept packed until used
+template <class T> struct Raw8;
+template <> struct Raw8<bf16> {
+    uint4 u;
+    __device__ __forceinline__ void load(const bf16 *p) { u = *reinterpret_cast<const uint4 *>(p); }
+    __device__ __forceinline__ float get(int i) const {
+        const uint32_t w = (&u.x)[i >> 1];
+        return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+};
+template <> struct Raw8<float> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const float *p) {
+        a = reinterpret_cast<const float4 *>(p)[0];
+        b = reinterpret_cast<const float4 *>(p)[1];
+    }
+    __device__ __forceinline__ float get(int i) const { return i < 4 ? (&a.x)[i] : (&b.x)[i - 4]; }
+};
+
 template <class T, int D> struct PrepSmem {
-    static constexpr int LDX = D + (sizeof(T) == 2 ? 8 : 4);   // q^, k^, v^ rows
+    static constexpr int LDX = D + (sizeof(T) == 2 ? 8 : 4);   // q^, k^, v^ rows (later W, Q' staging)
     static constexpr int LDA = 64 + 4;                          // fp32 A rows
-    static constexpr int LDP = 64 + (sizeof(T) == 2 ? 8 : 4);   // P rows
-    static constexpr int LDT = 64 + (sizeof(T) == 2 ? 8 : 4);   // [W | U~]^T rows
+    static constexpr int LDP = 64 + (sizeof(T) == 2 ? 8 : 4);   // P rows (P reuses the A storage)
+    static constexpr int LDTD = 16 + 4;                         // diagonal inverse rows
     T Qs[64 * LDX];
     T Ks[64 * LDX];
     T Vs[64 * LDX];
-    float As[64 * LDA];
-    T Ps[64 * LDP];
-    T XsT[2 * D * LDT];
-    float g[64], b[64], dk[64];
+    float Am[64 * LDA];
+    float Td[4 * 16 * LDTD];
+    float g[64], b[64], dk[64], eg[64];
+    __device__ T *P() { return reinterpret_cast<T *>(Am); }
 };
 
+// Short conv + SiLU (+ L2 normalisation for q and k) of the chunk's 64 scan
+// positions into LDS.  Thread layout: G = D/8 threads per token row (8
+// channels each); each thread owns RUN consecutive tokens and loads its
+// RUN + 3 input rows (3 rows of causal history) once, all loads issued before
+// any is used.
 template <class T, int D>
-__device__ __forceinline__ void prologue_tensor(const PrepArgs &a, const T *x, const float *w, T *dst,
-                                                bool normalize, int c, int h, int b) {
-    constexpr int G = D / 8;           // threads per token (8 channels each)
-    constexpr int TPP = kThreads / G;  // tokens per pass
+__device__ __forceinline__ void prologue(const PrepArgs &a, PrepSmem<T, D> &sm, int c, int h, int b) {
+    constexpr int G = D / 8;
+    constexpr int RUN = 64 / (kThreads / G);
+    constexpr int ROWS = RUN + 3;
     constexpr int LDX = PrepSmem<T, D>::LDX;
-    const int tid = threadIdx.x;
-    const int cg = tid % G, tr = tid / G;
-    float wt[8][4];
+    const int tid = threadIdx.x, cg = tid % G, run = tid / G;
+    const int s0 = c * 64 + run * RUN;
+    const T *src[3] = {static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v)};
+    const float *wsrc[3] = {a.conv_q, a.conv_k, a.conv_v};
+    T *dst[3] = {sm.Qs, sm.Ks, sm.Vs};
+    Raw8<T> raw[3][ROWS];
+    bool rv[ROWS];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        float4 wv = reinterpret_cast<const float4 *>(w)[(size_t)h * D + 8 * cg + i];
-        wt[i][0] = wv.x; wt[i][1] = wv.y; wt[i][2] = wv.z; wt[i][3] = wv.w;
+    for (int rr = 0; rr < ROWS; ++rr) {
+        const int sp = s0 - 3 + rr;
+        rv[rr] = sp >= 0 && sp < a.T;
+        int si = a.reverse ? a.T - 1 - sp : sp;
+        si = si < 0 ? 0 : (si >= a.T ? a.T - 1 : si);
+        const size_t off = (((size_t)b * a.T + si) * a.H + h) * D + 8 * cg;
+#pragma unroll
+        for (int x = 0; x < 3; ++x) raw[x][rr].load(src[x] + off);
     }
 #pragma unroll
-    for (int pass = 0; pass < 64 / TPP; ++pass) {
-        const int r = pass * TPP + tr;
-        const int s = c * 64 + r;
-        float acc[8];
+    for (int x = 0; x < 3; ++x) {
+        float wt[8][4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-        const bool valid = s < a.T;
-        if (valid) {
+        for (int i = 0; i < 8; ++i) {
+            float4 wv = reinterpret_cast<const float4 *>(wsrc[x])[(size_t)h * D + 8 * cg + i];
+            wt[i][0] = wv.x; wt[i][1] = wv.y; wt[i][2] = wv.z; wt[i][3] = wv.w;
+        }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int sp = s - 3 + j;
-                if (sp >= 0) {
-                    const int src = a.reverse ? a.T - 1 - sp : sp;
-                    float xv[8];
-                    load8(x + (((size_t)b * a.T + src) * a.H + h) * D + 8 * cg, xv);
+        for (int r = 0; r < RUN; ++r) {
+            const bool valid = s0 + r < a.T;
+            float acc[8];
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) acc[i] += wt[i][j] * xv[i];
-                }
+            for (int i = 0; i < 8; ++i) {
+                float s = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) s += rv[r + j] ? wt[i][j] * raw[x][r + j].get(i) : 0.f;
+                acc[i] = valid ? silu(s) : 0.f;
             }
+            if (x < 2) {
+                float ss = 0.f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] = silu(acc[i]);
+                for (int i = 0; i < 8; ++i) ss += acc[i] * acc[i];
+#pragma unroll
+                for (int m = 1; m < G; m <<= 1) ss += __shfl_xor(ss, m, 64);
+                const float inv = valid ? 1.0f / sqrtf(ss + a.eps_l2) : 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] *= inv;
+            }
+            T *row = dst[x] + (run * RUN + r) * LDX + 8 * cg;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) row[i] = (T)acc[i];
         }
-        if (normalize) {
-            float ss = 0.f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) ss += acc[i] * acc[i];
-#pragma unroll
-            for (int m = 1; m < G; m <<= 1) ss += __shfl_xor(ss, m, 64);
-            const float inv = valid ? 1.0f / sqrtf(ss + a.eps_l2) : 0.f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] *= inv;
-        }
-        T *row = dst + r * LDX + 8 * cg;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) row[i] = (T)acc[i];
     }
 }
 
 template <class T, int D>
-__global__ __launch_bounds__(kThreads) void gdn_prep_kernel(PrepArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void gdn_prep_kernel(PrepArgs a) {
     typedef Mfma<T> M;
     typedef typename M::frag frag;
+    typedef K16<T> K;
+    typedef typename K::frag kfrag;
     constexpr int KPL = M::KPL;
     constexpr int KBD = D / (4 * KPL);  // fragments over K = D
     constexpr int KBC = 16 / KPL;       // fragments over K = 64
-    constexpr int NT = D / 16;
     constexpr int MT = D / 64;
+    constexpr int NCT = D / 32;         // 16-column tiles of [W | U~] per wave
     typedef PrepSmem<T, D> SM;
     extern __shared__ __align__(16) unsigned char smem_raw[];
     SM &sm = *reinterpret_cast<SM *>(smem_raw);
@@ -206,7 +260,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(PrepArgs a) {
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, n = lane % 16, g = lane / 16;
 
-    // ---- gates: b, cumulative log decay g within the chunk
+    // ---- gates: b and the cumulative log decay g inside the chunk
     if (tid < 64) {
         const int s = c * 64 + tid;
         const bool valid = s < a.T;
@@ -220,131 +274,171 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(PrepArgs a) {
         }
         sm.g[tid] = la;
         sm.b[tid] = be;
+        sm.eg[tid] = expf(la);
+        sm.dk[tid] = expf(__shfl(la, 63, 64) - la);
     }
-    // ---- prologue
-    prologue_tensor<T, D>(a, static_cast<const T *>(a.q), a.conv_q, sm.Qs, true, c, h, b);
-    prologue_tensor<T, D>(a, static_cast<const T *>(a.k), a.conv_k, sm.Ks, true, c, h, b);
-    prologue_tensor<T, D>(a, static_cast<const T *>(a.v), a.conv_v, sm.Vs, false, c, h, b);
+    prologue<T, D>(a, sm, c, h, b);
     __syncthreads();
-    if (tid < 64) sm.dk[tid] = expf(sm.g[63] - sm.g[tid]);
 
-    // ---- K K^T and Q K^T for rows 16w..16w+15 (this wave), all 64 columns
+    // ---- A = strictly lower (b_i e^{g_i - g_j} k_i . k_j), rows 16w.. of this wave
     {
-        floatx4 accK[4], accQ[4];
+        floatx4 acc[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) { accK[t] = zero4(); accQ[t] = zero4(); }
-        const T *arowK = sm.Ks + (16 * w + n) * SM::LDX;
-        const T *arowQ = sm.Qs + (16 * w + n) * SM::LDX;
+        for (int t = 0; t < 4; ++t) acc[t] = zero4();
+        const T *arow = sm.Ks + (16 * w + n) * SM::LDX;
 #pragma unroll
         for (int kb = 0; kb < KBD; ++kb) {
-            frag aK = row_frag(arowK, kb, g);
-            frag aQ = row_frag(arowQ, kb, g);
+            frag fa = row_frag(arow, kb, g);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                frag bK = row_frag(sm.Ks + (16 * t + n) * SM::LDX, kb, g);
-                accK[t] = M::mma(aK, bK, accK[t]);
-                accQ[t] = M::mma(aQ, bK, accQ[t]);
-            }
+            for (int t = 0; t < 4; ++t)
+                if (t <= w) acc[t] = M::mma(fa, row_frag(sm.Ks + (16 * t + n) * SM::LDX, kb, g), acc[t]);
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int i = 16 * w + 4 * g + ii, j = 16 * t + n;
-                const float gi = sm.g[i], gj = sm.g[j];
-                const float dec = (j <= i) ? expf(gi - gj) : 0.f;
-                sm.As[i * SM::LDA + j] = (j < i) ? sm.b[i] * dec * accK[t][ii] : 0.f;
-                sm.Ps[i * SM::LDP + j] = (T)(dec * accQ[t][ii]);
+                sm.Am[i * SM::LDA + j] = (j < i) ? sm.b[i] * expf(sm.g[i] - sm.g[j]) * acc[t][ii] : 0.f;
             }
         }
     }
     __syncthreads();
 
-    // ---- forward substitution: column tid of (I + A) X = [diag(b e^g) K | diag(b) V]
-    if (tid < 2 * D) {
-        float x[64];
-        const bool isK = tid < D;
-        const int cc = isK ? tid : tid - D;
+    // ---- inverse of the unit lower diagonal block (I + A_ww), column n on lanes 0..15
+    if (g == 0) {
+        float x[16];
 #pragma unroll
-        for (int i = 0; i < 64; ++i) {
-            const float rhs = isK ? to_f(sm.Ks[i * SM::LDX + cc]) * expf(sm.g[i])
-                                  : to_f(sm.Vs[i * SM::LDX + cc]);
-            x[i] = sm.b[i] * rhs;
+        for (int r = 0; r < 16; ++r) x[r] = (r == n) ? 1.f : 0.f;
+        const float *ab = sm.Am + (16 * w) * SM::LDA + 16 * w;
+#pragma unroll
+        for (int r = 1; r < 16; ++r) {
+            float acc = x[r];
+#pragma unroll
+            for (int j = 0; j < r; ++j) acc -= ab[r * SM::LDA + j] * x[j];
+            x[r] = acc;
         }
 #pragma unroll
-        for (int i = 1; i < 64; ++i) {
-            const float *arow = sm.As + i * SM::LDA;
-            float acc = x[i];
-#pragma unroll
-            for (int j = 0; j < i; ++j) acc -= arow[j] * x[j];
-            x[i] = acc;
-        }
-        T *dst = sm.XsT + tid * SM::LDT;
-#pragma unroll
-        for (int i = 0; i < 64; ++i) dst[i] = (T)x[i];
+        for (int r = 0; r < 16; ++r) sm.Td[(w * 16 + r) * SM::LDTD + n] = x[r];
     }
     __syncthreads();
 
-    // ---- Q' = e^g Q - P W and O0 = P U~ for rows 16w.. (C tiles over D columns)
-    floatx4 accW[NT], accU[NT];
+    // ---- blocked solve (I + A) X = R, R = [diag(b e^g) K | diag(b) V], on this
+    // wave's NCT column tiles; block row I: X_I = Tinv_I (R_I - sum_{J<I} A_IJ X_J)
+    floatx4 X[4][NCT];
+    kfrag Xf[4][NCT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) { accW[t] = zero4(); accU[t] = zero4(); }
-    {
-        const T *prow = sm.Ps + (16 * w + n) * SM::LDP;
+    for (int I = 0; I < 4; ++I) {
+        kfrag aIJ[4];
 #pragma unroll
-        for (int kb = 0; kb < KBC; ++kb) {
-            frag aP = row_frag(prow, kb, g);
+        for (int J = 0; J < I; ++J) {
+            const float *p = sm.Am + (16 * I + n) * SM::LDA + 16 * J + 4 * g;
+            floatx4 v = *reinterpret_cast<const floatx4 *>(p);
+            aIJ[J] = K::from4(-v);
+        }
+        const kfrag tI = K::from4(*reinterpret_cast<const floatx4 *>(sm.Td + (16 * I + n) * SM::LDTD + 4 * g));
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                frag bW = row_frag(sm.XsT + (16 * t + n) * SM::LDT, kb, g);
-                frag bU = row_frag(sm.XsT + (D + 16 * t + n) * SM::LDT, kb, g);
-                accW[t] = M::mma(aP, bW, accW[t]);
-                accU[t] = M::mma(aP, bU, accU[t]);
+        for (int ct = 0; ct < NCT; ++ct) {
+            const int col = (D / 2) * w + 16 * ct + n;
+            floatx4 acc;
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int t = 16 * I + 4 * g + ii;
+                acc[ii] = col < D ? sm.b[t] * sm.eg[t] * to_f(sm.Ks[t * SM::LDX + col])
+                                  : sm.b[t] * to_f(sm.Vs[t * SM::LDX + col - D]);
             }
-        }
-    }
-    T *rec = static_cast<T *>(a.rec) + (((size_t)b * a.H + h) * a.NC + c) * (size_t)Rec<D>::SIZE;
-    // O0 and U~ in C-tile order: [vb][w][lane][4], tokens 16w + 4g + ii, channel 16 vb + n
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        store4(rec + Rec<D>::O0 + ((t * 4 + w) * 64 + lane) * 4, accU[t]);
-        const T *src = sm.XsT + (D + 16 * t + n) * SM::LDT + 16 * w + 4 * g;
-        floatx4 u = floatx4{to_f(src[0]), to_f(src[1]), to_f(src[2]), to_f(src[3])};
-        store4(rec + Rec<D>::UT + ((t * 4 + w) * 64 + lane) * 4, u);
-    }
-    // Q' = e^{g_r} q_r - (P W)_r, written back over this wave's own rows of Qs
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            const int r = 16 * w + 4 * g + ii, col = 16 * t + n;
-            accW[t][ii] = expf(sm.g[r]) * to_f(sm.Qs[r * SM::LDX + col]) - accW[t][ii];
+            for (int J = 0; J < I; ++J) acc = K::mma(aIJ[J], Xf[J][ct], acc);
+            X[I][ct] = K::mma(tI, K::from4(acc), zero4());
+            Xf[I][ct] = K::from4(X[I][ct]);
         }
     }
     __syncthreads();
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            const int r = 16 * w + 4 * g + ii, col = 16 * t + n;
-            sm.Qs[r * SM::LDX + col] = (T)accW[t][ii];
-        }
-    }
-    __syncthreads();
-    // QP and WN as A fragments: rows 16w + n, K = key channels in chained order
+
+    // ---- P = lower-inclusive (e^{g_r - g_j} q_r . k_j), rows 16w.., into the A storage
     {
-        const T *qrow = sm.Qs + (16 * w + n) * SM::LDX;
+        floatx4 acc[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[t] = zero4();
+        const T *arow = sm.Qs + (16 * w + n) * SM::LDX;
 #pragma unroll
         for (int kb = 0; kb < KBD; ++kb) {
-            frag fq = row_frag(qrow, kb, g);
-            frag fw;
+            frag fa = row_frag(arow, kb, g);
 #pragma unroll
-            for (int j = 0; j < KPL; ++j) {
-                const int kk = kchain(kb * KPL + j, g);
-                fset(fw, j, -to_f(sm.XsT[kk * SM::LDT + 16 * w + n]));
+            for (int t = 0; t < 4; ++t)
+                if (t <= w) acc[t] = M::mma(fa, row_frag(sm.Ks + (16 * t + n) * SM::LDX, kb, g), acc[t]);
+        }
+        T *P = sm.P();
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int i = 16 * w + 4 * g + ii, j = 16 * t + n;
+                P[i * SM::LDP + j] = (T)((j <= i) ? expf(sm.g[i] - sm.g[j]) * acc[t][ii] : 0.f);
             }
-            *reinterpret_cast<frag *>(rec + Rec<D>::QP + ((w * KBD + kb) * 64 + lane) * KPL) = fq;
-            *reinterpret_cast<frag *>(rec + Rec<D>::WN + ((w * KBD + kb) * 64 + lane) * KPL) = fw;
+        }
+    }
+    __syncthreads();
+
+    // ---- P X on this wave's columns: Q' = e^g Q - P W (W columns), O0 = P U~
+    T *rec = static_cast<T *>(a.rec) + (((size_t)b * a.H + h) * a.NC + c) * (size_t)Rec<D>::SIZE;
+    {
+        const T *P = sm.P();
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+            frag pf[KBC];
+#pragma unroll
+            for (int kb = 0; kb < KBC; ++kb) pf[kb] = row_frag(P + (16 * R + n) * SM::LDP, kb, g);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const int col = (D / 2) * w + 16 * ct + n;
+                floatx4 acc = zero4();
+#pragma unroll
+                for (int kb = 0; kb < KBC; ++kb) {
+                    frag xb;
+#pragma unroll
+                    for (int j = 0; j < KPL; ++j) {
+                        const int e = kb * KPL + j;  // token block e/4, row 4g + e%4
+                        fset(xb, j, X[e >> 2][ct][e & 3]);
+                    }
+                    acc = M::mma(pf[kb], xb, acc);
+                }
+                if (col < D) {
+                    // Q' rows 16R + 4g + ii, staged in Qs over the q^ values it replaces
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) {
+                        const int t = 16 * R + 4 * g + ii;
+                        const float qv = sm.eg[t] * to_f(sm.Qs[t * SM::LDX + col]) - acc[ii];
+                        sm.Qs[t * SM::LDX + col] = (T)qv;
+                    }
+                } else {
+                    const int vb = (col - D) / 16;
+                    store4(rec + Rec<D>::O0 + ((vb * 4 + R) * 64 + lane) * 4, acc);
+                    store4(rec + Rec<D>::UT + ((vb * 4 + R) * 64 + lane) * 4, X[R][ct]);
+                }
+            }
+        }
+        // -W staged row-major in Vs (v^ is no longer needed)
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const int col = (D / 2) * w + 16 * ct + n;
+                if (col < D) {
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) sm.Vs[(16 * I + 4 * g + ii) * SM::LDX + col] = (T)(-X[I][ct][ii]);
+                }
+            }
+    }
+    __syncthreads();
+
+    // ---- QP and WN as A fragments: rows = tokens 16w + n, K = key channels (chained)
+    {
+        const T *qrow = sm.Qs + (16 * w + n) * SM::LDX;
+        const T *wrow = sm.Vs + (16 * w + n) * SM::LDX;
+#pragma unroll
+        for (int kb = 0; kb < KBD; ++kb) {
+            *reinterpret_cast<frag *>(rec + Rec<D>::QP + ((w * KBD + kb) * 64 + lane) * KPL) = row_frag(qrow, kb, g);
+            *reinterpret_cast<frag *>(rec + Rec<D>::WN + ((w * KBD + kb) * 64 + lane) * KPL) = row_frag(wrow, kb, g);
         }
     }
     // DKT: A fragments of (D K)^T, rows = key channel w*D/4 + 16 mt + n, K = tokens
@@ -362,7 +456,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(PrepArgs a) {
             *reinterpret_cast<frag *>(rec + Rec<D>::DKT + (((w * MT + mt) * KBC + kb) * 64 + lane) * KPL) = f;
         }
     }
-    if (tid == 0) a.gC[((size_t)b * a.H + h) * a.NC + c] = expf(sm.g[63]);
+    if (tid == 0) a.gC[((size_t)b * a.H + h) * a.NC + c] = sm.eg[63];
 }
 
 // ===================================================================== state
@@ -373,22 +467,68 @@ template <class T, int D> struct StateSmem {
     T Ux[64 * LDS_U];  // U as B fragments, per lane
 };
 
+// One chunk's operands for one wave of a state workgroup, in registers.
+template <class T, int D> struct ChunkOps {
+    typedef typename Mfma<T>::frag frag;
+    static constexpr int KPL = Mfma<T>::KPL;
+    static constexpr int KBD = D / (4 * KPL);
+    static constexpr int KBC = 16 / KPL;
+    static constexpr int MT = D / 64;
+    frag wn[KBD], qp[KBD], dk[MT][KBC];
+    floatx4 ut, o0;
+    float gc;
+    __device__ __forceinline__ void load(const T *rec, const float *gcp, int vb, int w, int lane) {
+#pragma unroll
+        for (int kb = 0; kb < KBD; ++kb) {
+            wn[kb] = *reinterpret_cast<const frag *>(rec + Rec<D>::WN + ((w * KBD + kb) * 64 + lane) * KPL);
+            qp[kb] = *reinterpret_cast<const frag *>(rec + Rec<D>::QP + ((w * KBD + kb) * 64 + lane) * KPL);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int kb = 0; kb < KBC; ++kb)
+                dk[mt][kb] = *reinterpret_cast<const frag *>(
+                    rec + Rec<D>::DKT + (((w * MT + mt) * KBC + kb) * 64 + lane) * KPL);
+        ut = load4(rec + Rec<D>::UT + ((vb * 4 + w) * 64 + lane) * 4);
+        o0 = load4(rec + Rec<D>::O0 + ((vb * 4 + w) * 64 + lane) * 4);
+        gc = *gcp;
+    }
+};
+
+// Workgroup placement: launched as a 1-D grid whose size is a multiple of 8.
+// Consecutive workgroup ids go to different XCDs (round robin), so id L is
+// mapped to position p = (L % 8) * per + L / 8 of the head-major list of
+// (batch*head, value block) pairs: the value blocks of one head then sit on
+// one XCD (two at most) and share its L2 for the head's chunk records.
+__device__ __forceinline__ bool xcd_position(int L, int nwg_used, int nwg_launched, int &p) {
+    const int per = nwg_launched / 8;
+    p = (L % 8) * per + L / 8;
+    return p < nwg_used;
+}
+
+// One workgroup owns a block of 16 value channels of one head.  Wave w
+// computes U and O for tokens 16w..16w+15 (K = all key channels) and updates
+// the key-channel rows w*D/4.. of S^T (K = all tokens); S^T and U are
+// exchanged through LDS once per chunk each.
 template <class T, int D>
 __global__ __launch_bounds__(kThreads) void gdn_state_kernel(StateArgs a) {
     typedef Mfma<T> M;
     typedef typename M::frag frag;
+    typedef ChunkOps<T, D> Ops;
     constexpr int KPL = M::KPL;
-    constexpr int KBD = D / (4 * KPL);
-    constexpr int KBC = 16 / KPL;
-    constexpr int MT = D / 64;
+    constexpr int KBD = Ops::KBD;
+    constexpr int KBC = Ops::KBC;
+    constexpr int MT = Ops::MT;
     constexpr int NV = D / 16;
     typedef StateSmem<T, D> SM;
     __shared__ SM sm;
 
-    const int vb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    int p;
+    if (!xcd_position(blockIdx.x, a.B * a.H * NV, gridDim.x, p)) return;
+    const int vb = p % NV;
+    const size_t bh = p / NV;
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, n = lane % 16, g = lane / 16;
     const int vcol = 16 * vb + n;
-    const size_t bh = (size_t)b * a.H + h;
 
     // S^T slice: rows (key channels) w*D/4 + 16 mt + 4g + ii, column vcol
     floatx4 S[MT];
@@ -400,11 +540,11 @@ __global__ __launch_bounds__(kThreads) void gdn_state_kernel(StateArgs a) {
             S[mt] = zero4();
     }
     const T *rec0 = static_cast<const T *>(a.rec) + bh * a.NC * (size_t)Rec<D>::SIZE;
+    const float *gc0 = a.gC + bh * a.NC;
     T *sx = sm.Sx + lane * SM::LDS_S;
     T *ux = sm.Ux + lane * SM::LDS_U;
 
-    for (int c = 0; c < a.NC; ++c) {
-        const T *rec = rec0 + (size_t)c * Rec<D>::SIZE;
+    auto step = [&](const Ops &f, int c) {
         // publish this wave's part of S^T (elements e = 4 (w MT + mt) + ii)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -415,14 +555,11 @@ __global__ __launch_bounds__(kThreads) void gdn_state_kernel(StateArgs a) {
 #pragma unroll
         for (int kb = 0; kb < KBD; ++kb) sB[kb] = *reinterpret_cast<const frag *>(sx + kb * KPL);
         // U = U~ + WN S^T and O = O0 + Q' S^T for tokens 16w..16w+15
-        floatx4 u = load4(rec + Rec<D>::UT + ((vb * 4 + w) * 64 + lane) * 4);
-        floatx4 o = load4(rec + Rec<D>::O0 + ((vb * 4 + w) * 64 + lane) * 4);
+        floatx4 u = f.ut, o = f.o0;
 #pragma unroll
         for (int kb = 0; kb < KBD; ++kb) {
-            frag fw = *reinterpret_cast<const frag *>(rec + Rec<D>::WN + ((w * KBD + kb) * 64 + lane) * KPL);
-            frag fq = *reinterpret_cast<const frag *>(rec + Rec<D>::QP + ((w * KBD + kb) * 64 + lane) * KPL);
-            u = M::mma(fw, sB[kb], u);
-            o = M::mma(fq, sB[kb], o);
+            u = M::mma(f.wn[kb], sB[kb], u);
+            o = M::mma(f.qp[kb], sB[kb], o);
         }
         // publish U (elements e = 4 w + ii)
 #pragma unroll
@@ -431,29 +568,36 @@ __global__ __launch_bounds__(kThreads) void gdn_state_kernel(StateArgs a) {
         frag uB[KBC];
 #pragma unroll
         for (int kb = 0; kb < KBC; ++kb) uB[kb] = *reinterpret_cast<const frag *>(ux + kb * KPL);
-        const float gc = a.gC[bh * a.NC + c];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            S[mt] *= gc;
+            S[mt] *= f.gc;
 #pragma unroll
-            for (int kb = 0; kb < KBC; ++kb) {
-                frag fd = *reinterpret_cast<const frag *>(
-                    rec + Rec<D>::DKT + (((w * MT + mt) * KBC + kb) * 64 + lane) * KPL);
-                S[mt] = M::mma(fd, uB[kb], S[mt]);
-            }
+            for (int kb = 0; kb < KBC; ++kb) S[mt] = M::mma(f.dk[mt][kb], uB[kb], S[mt]);
         }
-        // unnormalised output and its partial sum of squares over these 16 channels
+        // unnormalised output (the normalisation pass reduces over all channels)
         const int s0 = c * 64 + 16 * w + 4 * g;
         float *orow = a.ows + (bh * (size_t)a.NC * 64 + s0) * D + vcol;
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            orow[(size_t)ii * D] = o[ii];
-            float ss = o[ii] * o[ii];
-#pragma unroll
-            for (int m = 1; m < 16; m <<= 1) ss += __shfl_xor(ss, m, 64);
-            if (n == ii) a.ps[(bh * NV + vb) * (size_t)a.NC * 64 + s0 + ii] = ss;
-        }
+        for (int ii = 0; ii < 4; ++ii) orow[(size_t)ii * D] = o[ii];
+    };
+
+    // two register sets: chunk c+1's operands load while chunk c computes.  The
+    // loads are unconditional (the index is clamped to the last chunk) and the
+    // loop has no early exit, so no branch merges different loads in flight.
+    Ops A, B;
+    const int last = a.NC - 1;
+    auto at = [&](int cc) { return rec0 + (size_t)min(cc, last) * Rec<D>::SIZE; };
+    auto gat = [&](int cc) { return gc0 + min(cc, last); };
+    A.load(at(0), gat(0), vb, w, lane);
+    const int pairs = a.NC / 2;
+    for (int i = 0; i < pairs; ++i) {
+        const int c = 2 * i;
+        B.load(at(c + 1), gat(c + 1), vb, w, lane);
+        step(A, c);
+        A.load(at(c + 2), gat(c + 2), vb, w, lane);
+        step(B, c + 1);
     }
+    if (a.NC & 1) step(A, a.NC - 1);
     if (a.S_T) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -465,11 +609,11 @@ __global__ __launch_bounds__(kThreads) void gdn_state_kernel(StateArgs a) {
 template <class T, int D>
 __global__ __launch_bounds__(kThreads) void gdn_norm_kernel(NormArgs a) {
     constexpr int G = D / 8;
-    constexpr int NV = D / 16;
     const int tid = threadIdx.x, cg = tid % G;
-    const int t = blockIdx.x * (kThreads / G) + tid / G;  // input (output) token
+    const int t0 = blockIdx.x * (kThreads / G) + tid / G;  // input (output) token
+    const bool live = t0 < a.T;
+    const int t = live ? t0 : a.T - 1;  // idle threads still take part in the shuffles
     const int h = blockIdx.y, b = blockIdx.z;
-    if (t >= a.T) return;
     const size_t bh = (size_t)b * a.H + h;
     const size_t L = (size_t)a.NC * 64;
     float wv[8], gv[8], y[8];
@@ -481,18 +625,19 @@ __global__ __launch_bounds__(kThreads) void gdn_norm_kernel(NormArgs a) {
     for (int pass = 0; pass < (a.ows2 ? 2 : 1); ++pass) {
         const bool rev = pass == 0 ? a.reverse != 0 : true;
         const float *ows = pass == 0 ? a.ows : a.ows2;
-        const float *ps = pass == 0 ? a.ps : a.ps2;
         const int s = rev ? a.T - 1 - t : t;  // scan position of this token
-        float ss = 0.f;
-#pragma unroll
-        for (int vb = 0; vb < NV; ++vb) ss += ps[(bh * NV + vb) * L + s];
-        const float inv = 1.0f / sqrtf(ss / D + a.eps);
         float ov[8];
         load8(ows + (bh * L + s) * D + 8 * cg, ov);
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss += ov[i] * ov[i];
+#pragma unroll
+        for (int m = 1; m < G; m <<= 1) ss += __shfl_xor(ss, m, 64);
+        const float inv = 1.0f / sqrtf(ss / D + a.eps);
 #pragma unroll
         for (int i = 0; i < 8; ++i) y[i] += ov[i] * inv * gv[i];
     }
-    store8(static_cast<T *>(a.out) + (((size_t)b * a.T + t) * a.H + h) * D + 8 * cg, y);
+    if (live) store8(static_cast<T *>(a.out) + (((size_t)b * a.T + t) * a.H + h) * D + 8 * cg, y);
 }
 
 }  // namespace gdn
