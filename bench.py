@@ -38,15 +38,16 @@ def log(msg):
 
 
 # Algorithmic bytes per token-head of each kernel's own inputs and outputs
-# (bf16 I/O, d = 128, chunk 64).  The prep kernel reads q, k, v (768 B) and
-# log a, b (8 B) and writes the chunk record (5 matrices of 64 x 128 bf16 per
-# 64 tokens = 1280 B); the state kernel reads the record once (1280 B) and
-# writes the unnormalised output (fp32, 512 B); the norm kernel reads that
-# and the gate (256 B) and writes y (256 B).
+# (bf16 I/O, d = 128, chunk 64).  prep reads q, k, v (768 B) and log a, b
+# (8 B) and writes the chunk record (5 matrices of 64 x 128 bf16 per 64 tokens
+# = 1280 B); state reads the record's -W, (D K)^T and U~ (768 B) and writes
+# the chunk-entry state (8 value blocks x 4 KB per 64 tokens = 512 B); out
+# reads Q', O0 (512 B), the entry state (512 B) and the gate (256 B) and
+# writes y (256 B).
 KERNEL_BYTES_PER_TOKEN_HEAD = {
     "gdn_prep_kernel": 768 + 8 + 1280,
-    "gdn_state_kernel": 1280 + 512,
-    "gdn_norm_kernel": 512 + 256 + 256,
+    "gdn_state_kernel": 768 + 512,
+    "gdn_out_kernel": 512 + 512 + 256 + 256,
 }
 LAYER_BYTES_PER_TOKEN_HEAD = 4 * 128 * 2 + 128 * 2 + 8
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -192,36 +193,42 @@ def main() -> int:
     tokens_per_s = B * T / (ms_per_step * 1e-3)
     log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step, {tokens_per_s:.4e} tokens/s")
 
-    # ---- per-kernel durations from HIP events on the launch stream
+    # ---- per-kernel durations from HIP events recorded on each launch's stream
     ev = HipEvents()
     bid = 1 if w.bidirectional else 0
     nl = lib.gdn_fwd_launch_count(ctypes.byref(p), bid)
     names = [lib.gdn_fwd_launch_name(ctypes.byref(p), bid, i).decode() for i in range(nl)]
-    evs = [ev.create(nl + 1) for _ in range(args.steps)]
+    reps = min(args.steps, 20)
+    evs = [ev.create(2 * nl) for _ in range(reps)]
     torch.cuda.synchronize()
-    for i in range(args.steps):
-        st = lib.gdn_fwd_timed(ctypes.byref(p), rev_ptr, bid, evs[i], nl + 1, sptr)
+    for i in range(reps):
+        st = lib.gdn_fwd_timed(ctypes.byref(p), rev_ptr, bid, evs[i], 2 * nl, sptr)
         if st != gdn.GDN_OK:
             raise gdn.GdnError(st, "gdn_fwd_timed")
     torch.cuda.synchronize()
-    per = {}
-    totals = []
-    for i in range(args.steps):
-        ev.sync(evs[i][nl])
-        totals.append(ev.elapsed_ms(evs[i][0], evs[i][nl]))
+    per_launch = {}   # kernel -> list of single-launch durations (ms)
+    per_call = {}     # kernel -> list of summed durations per call (ms)
+    for i in range(reps):
+        tot = {}
         for j, nm in enumerate(names):
-            per.setdefault(nm, []).append(ev.elapsed_ms(evs[i][j], evs[i][j + 1]))
-    # a kernel launched more than once per call (two scans) is averaged per launch
+            ev.sync(evs[i][2 * j + 1])
+            dms = ev.elapsed_ms(evs[i][2 * j], evs[i][2 * j + 1])
+            per_launch.setdefault(nm, []).append(dms)
+            tot[nm] = tot.get(nm, 0.0) + dms
+        for nm, v in tot.items():
+            per_call.setdefault(nm, []).append(v)
     launches_per_call = {nm: names.count(nm) for nm in set(names)}
     kernels = {}
-    token_heads = B * T * H
-    for nm, vals in per.items():
-        per_launch_ms = float(np.mean(vals))
-        total_ms = per_launch_ms * launches_per_call[nm]
-        bytes_per_launch = KERNEL_BYTES_PER_TOKEN_HEAD[nm] * token_heads
+    token_heads = B * T * H * (2 if w.bidirectional else 1)
+    for nm in per_launch:
+        per_launch_ms = float(np.mean(per_launch[nm]))
+        call_ms = float(np.mean(per_call[nm]))
+        bytes_per_call = KERNEL_BYTES_PER_TOKEN_HEAD[nm] * token_heads
+        if nm == "gdn_out_kernel" and w.bidirectional:  # + fp32 accumulator write and read
+            bytes_per_call += 2 * 512 * B * T * H
         kernels[nm] = {"launches_per_call": launches_per_call[nm], "avg_ms": per_launch_ms,
-                       "ms_per_call": total_ms, "bytes_per_launch": bytes_per_launch,
-                       "GBps": bytes_per_launch / (per_launch_ms * 1e-3) / 1e9}
+                       "ms_per_call": call_ms, "bytes_per_launch": bytes_per_call / launches_per_call[nm],
+                       "GBps": bytes_per_call / (call_ms * 1e-3) / 1e9}
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_call"])
     kd = kernels[dom]
     tag = f"T{T}_H{H}_d{D}_{w.dtype}" + ("_bidir" if w.bidirectional else "")
@@ -230,13 +237,13 @@ def main() -> int:
                 "unit": "GB/s", "frac": round(kd["GBps"] / HBM_PEAK_GBS, 4),
                 "traffic": None if traffic is None else round(traffic),
                 "avg_launch_ms": round(kd["avg_ms"], 5)}
-    call_ms = float(np.mean(totals))
+    call_ms = ms_per_step
     layer_bytes = LAYER_BYTES_PER_TOKEN_HEAD * token_heads * (2 if w.bidirectional else 1)
     layer = {"algorithmic_bytes": layer_bytes, "floor_ms": layer_bytes / (HBM_PEAK_GBS * 1e9) * 1e3,
-             "call_ms_events": round(call_ms, 5),
              "frac_of_hbm_roofline": round(layer_bytes / (HBM_PEAK_GBS * 1e9) * 1e3 / ms_per_step, 4)}
     for nm, k in kernels.items():
-        log(f"  {nm}: {k['avg_ms']:.4f} ms/launch x{k['launches_per_call']}, {k['GBps']:.0f} GB/s")
+        log(f"  {nm}: {k['avg_ms']:.4f} ms/launch x{k['launches_per_call']} = {k['ms_per_call']:.4f} ms/call, "
+            f"{k['GBps']:.0f} GB/s")
 
     # ---- CPU baseline: the fp64 oracle on this host, same workload
     cpu = None

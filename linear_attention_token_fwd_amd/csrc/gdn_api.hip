@@ -5,6 +5,9 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <vector>
 
 #include "../../include/gdn.h"
 #include "kernels.hpp"
@@ -18,25 +21,31 @@ constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t rec, gC, ows, total;  // byte offsets (total = size)
+    // per scan: chunk records, e^{g_C}, chunk-entry states, two state hand-off buffers;
+    // then, for two scans, one fp32 accumulator for the sum of their outputs
+    size_t rec, gC, sc, smid, per_scan, acc, total;  // byte offsets within a scan's block, sizes
 };
 
 int n_chunks(int T) { return (T + gdn::kChunk - 1) / gdn::kChunk; }
 
 size_t elem_size(gdn_dtype d) { return d == GDN_BF16 ? 2 : 4; }
 
-// scans = number of scans whose partial outputs are alive at once (1 or 2)
+// scans = number of scans whose buffers are alive at once (1 or 2)
 Layout layout(const gdn_fwd_params *p, int scans) {
-    const size_t B = p->B, H = p->H, D = p->Dk, NC = n_chunks(p->T);
+    const size_t B = p->B, T = p->T, H = p->H, D = p->Dk, NC = n_chunks(p->T), es = elem_size(p->io_dtype);
     Layout L;
     size_t off = 0;
     L.rec = off;
-    off += round_up(B * H * NC * 320 * D * elem_size(p->io_dtype));
+    off += round_up(B * H * NC * 320 * D * es);
     L.gC = off;
     off += round_up(B * H * NC * sizeof(float));
-    L.ows = off;
-    off += scans * round_up(B * H * NC * 64 * D * sizeof(float));
-    L.total = off;
+    L.sc = off;
+    off += round_up(B * H * NC * 16 * D * es * (D / 16));
+    L.smid = off;
+    off += 2 * round_up(B * H * D * D * sizeof(float));
+    L.per_scan = off;
+    L.acc = scans * off;
+    L.total = L.acc + (scans == 2 ? round_up(B * T * H * D * sizeof(float)) : 0);
     return L;
 }
 
@@ -109,103 +118,253 @@ gdn_status validate(const gdn_fwd_params *p, const float *S_T_rev, int scans) {
     return GDN_OK;
 }
 
-// A call is a short fixed sequence of kernel launches on one stream.
+// A call is a fixed plan of kernel launches spread over up to four streams:
+// stream 0 is the caller's, streams 1-3 belong to the library (one set per
+// device, created on first use, default priority).  Events order the streams:
+// every library stream first waits for the caller's stream at the start of
+// the call, and the caller's stream finally waits for every library stream,
+// so the call behaves as one stream-ordered operation on the caller's stream.
+constexpr int kStreams = 4;
+
 struct Launch {
     const void *fn;
     dim3 grid, block;
     size_t smem;
-    unsigned char args[256];
+    unsigned char args[160];
+    const char *name;
+};
+
+struct Op {
+    enum Kind { LAUNCH, RECORD, WAIT } kind;
+    int stream;
+    int event;  // plan-local event index for RECORD / WAIT, launch index for LAUNCH
 };
 
 struct Plan {
-    Launch l[8];
-    int n = 0;
-    template <class Args> void add(const void *fn, dim3 grid, dim3 block, size_t smem, const Args &a) {
+    std::vector<Op> ops;
+    std::vector<Launch> launches;
+    int n_events = 0;
+    template <class Args>
+    void launch(int stream, const char *name, const void *fn, dim3 grid, dim3 block, size_t smem, const Args &a) {
         static_assert(sizeof(Args) <= sizeof(Launch::args), "kernel arguments too large");
-        Launch &L = l[n++];
-        L.fn = fn; L.grid = grid; L.block = block; L.smem = smem;
+        Launch L;
+        L.fn = fn; L.grid = grid; L.block = block; L.smem = smem; L.name = name;
         memcpy(L.args, &a, sizeof(Args));
+        ops.push_back(Op{Op::LAUNCH, stream, (int)launches.size()});
+        launches.push_back(L);
     }
-    // events: NULL, or n + 1 events recorded before each launch and after the last
-    gdn_status run(hipStream_t s, hipEvent_t *events) const {
-        for (int i = 0; i < n; ++i) {
-            if (events && hipEventRecord(events[i], s) != hipSuccess) return GDN_ERR_HIP;
-            void *kargs[] = {const_cast<unsigned char *>(l[i].args)};
-            if (hipLaunchKernel(l[i].fn, l[i].grid, l[i].block, kargs, l[i].smem, s) != hipSuccess)
-                return GDN_ERR_HIP;
-        }
-        if (events && hipEventRecord(events[n], s) != hipSuccess) return GDN_ERR_HIP;
-        return GDN_OK;
+    int record(int stream) {
+        ops.push_back(Op{Op::RECORD, stream, n_events});
+        return n_events++;
     }
+    void wait(int stream, int event) { ops.push_back(Op{Op::WAIT, stream, event}); }
 };
 
-// One scan: prep + state.  ows receives that scan's unnormalised output.
+struct DeviceRes {
+    hipStream_t streams[kStreams] = {};
+    std::vector<hipEvent_t> events;
+};
+
+std::mutex g_mutex;
+std::map<int, DeviceRes> g_res;
+
+// Caller holds g_mutex.
+gdn_status device_res(int n_events, DeviceRes *&out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GDN_ERR_HIP;
+    DeviceRes &r = g_res[dev];
+    for (int i = 1; i < kStreams; ++i)
+        if (!r.streams[i] && hipStreamCreateWithFlags(&r.streams[i], hipStreamNonBlocking) != hipSuccess)
+            return GDN_ERR_HIP;
+    while ((int)r.events.size() < n_events) {
+        hipEvent_t e;
+        if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return GDN_ERR_HIP;
+        r.events.push_back(e);
+    }
+    out = &r;
+    return GDN_OK;
+}
+
+// timing: NULL, or 2 events per launch recorded right before and right after it
+gdn_status run_plan(const Plan &plan, hipStream_t caller, hipEvent_t *timing) {
+    std::lock_guard<std::mutex> lock(g_mutex);
+    DeviceRes *r = nullptr;
+    gdn_status st = device_res(plan.n_events, r);
+    if (st != GDN_OK) return st;
+    hipStream_t streams[kStreams];
+    streams[0] = caller;
+    for (int i = 1; i < kStreams; ++i) streams[i] = r->streams[i];
+    for (const Op &op : plan.ops) {
+        hipStream_t s = streams[op.stream];
+        if (op.kind == Op::RECORD) {
+            if (hipEventRecord(r->events[op.event], s) != hipSuccess) return GDN_ERR_HIP;
+        } else if (op.kind == Op::WAIT) {
+            if (hipStreamWaitEvent(s, r->events[op.event], 0) != hipSuccess) return GDN_ERR_HIP;
+        } else {
+            const Launch &L = plan.launches[op.event];
+            if (timing && hipEventRecord(timing[2 * op.event], s) != hipSuccess) return GDN_ERR_HIP;
+            void *kargs[] = {const_cast<unsigned char *>(L.args)};
+            if (hipLaunchKernel(L.fn, L.grid, L.block, kargs, L.smem, s) != hipSuccess) return GDN_ERR_HIP;
+            if (timing && hipEventRecord(timing[2 * op.event + 1], s) != hipSuccess) return GDN_ERR_HIP;
+        }
+    }
+    return GDN_OK;
+}
+
+// Chunk ranges of a scan: ~64 chunks each, at most 16.
+int n_ranges(int NC) {
+    int R = (NC + 63) / 64;
+    return R < 1 ? 1 : (R > 16 ? 16 : R);
+}
+int range_begin(int NC, int R, int i) { return (int)((long long)NC * i / R); }
+
+// Dynamic LDS of the state kernel: its operand ring, and at least 96 KB so
+// that no prep workgroup (up to 75 KB of LDS) shares its CU.
+template <class T, int D> constexpr size_t state_lds() {
+    return gdn::StateRing<T, D>::BYTES > 96 * 1024 ? gdn::StateRing<T, D>::BYTES : 96 * 1024;
+}
+
+struct ScanBufs {
+    char *rec, *sc;
+    float *gC, *smid[2];
+};
+
+ScanBufs scan_bufs(const gdn_fwd_params *p, const Layout &L, int scan) {
+    char *base = static_cast<char *>(p->workspace) + (size_t)scan * L.per_scan;
+    ScanBufs b;
+    b.rec = base + L.rec;
+    b.sc = base + L.sc;
+    b.gC = reinterpret_cast<float *>(base + L.gC);
+    const size_t sbytes = round_up((size_t)p->B * p->H * p->Dk * p->Dk * sizeof(float));
+    b.smid[0] = reinterpret_cast<float *>(base + L.smid);
+    b.smid[1] = reinterpret_cast<float *>(base + L.smid + sbytes);
+    return b;
+}
+
 template <class T, int D>
-gdn_status plan_scan(Plan &plan, const gdn_fwd_params *p, int reverse, const float *S0, float *S_T, float *ows,
-                     char *ws, const Layout &L) {
-    const int NC = n_chunks(p->T);
+gdn::PrepArgs prep_args(const gdn_fwd_params *p, int reverse, const ScanBufs &sb, int c_begin) {
     gdn::PrepArgs pa;
-    pa.B = p->B; pa.T = p->T; pa.H = p->H; pa.NC = NC; pa.reverse = reverse;
+    pa.B = p->B; pa.T = p->T; pa.H = p->H; pa.NC = n_chunks(p->T); pa.reverse = reverse;
+    pa.c_begin = c_begin;
     pa.q = p->q; pa.k = p->k; pa.v = p->v;
     pa.log_a = p->log_a; pa.beta = p->beta;
     pa.conv_q = p->conv_q; pa.conv_k = p->conv_k; pa.conv_v = p->conv_v;
     pa.eps_l2 = p->eps_l2;
-    pa.rec = ws + L.rec;
-    pa.gC = reinterpret_cast<float *>(ws + L.gC);
-    const size_t smem = sizeof(gdn::PrepSmem<T, D>);
-    const void *prep = reinterpret_cast<const void *>(&gdn::gdn_prep_kernel<T, D>);
-    if (hipFuncSetAttribute(prep, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
-        return GDN_ERR_HIP;
-    plan.add(prep, dim3(NC, p->H, p->B), dim3(gdn::kThreads), smem, pa);
+    pa.rec = sb.rec;
+    pa.gC = sb.gC;
+    return pa;
+}
+
+template <class T, int D>
+gdn::StateArgs state_args(const gdn_fwd_params *p, const ScanBufs &sb, int c0, int c1, const float *S_in,
+                          float *S_out) {
     gdn::StateArgs sa;
-    sa.B = p->B; sa.T = p->T; sa.H = p->H; sa.NC = NC;
-    sa.rec = ws + L.rec;
-    sa.gC = reinterpret_cast<const float *>(ws + L.gC);
-    sa.S0 = S0; sa.S_T = S_T; sa.ows = ows;
-    const int used = p->B * p->H * (D / 16);
-    plan.add(reinterpret_cast<const void *>(&gdn::gdn_state_kernel<T, D>), dim3((used + 7) / 8 * 8),
-             dim3(gdn::kThreads), 0, sa);
-    return GDN_OK;
+    sa.B = p->B; sa.T = p->T; sa.H = p->H; sa.NC = n_chunks(p->T);
+    sa.c_begin = c0; sa.c_end = c1;
+    sa.rec = sb.rec; sa.gC = sb.gC;
+    sa.S_in = S_in; sa.S_out = S_out; sa.sc = sb.sc;
+    return sa;
 }
 
 template <class T, int D>
-void plan_norm(Plan &plan, const gdn_fwd_params *p, int reverse, const float *ows, const float *ows2) {
-    gdn::NormArgs na;
-    na.B = p->B; na.T = p->T; na.H = p->H; na.NC = n_chunks(p->T); na.reverse = reverse;
-    na.ows = ows; na.ows2 = ows2;
-    na.gate = p->gate; na.norm_w = p->norm_w; na.eps = p->eps_norm; na.out = p->o;
-    constexpr int tok_per_block = gdn::kThreads / (D / 8);
-    plan.add(reinterpret_cast<const void *>(&gdn::gdn_norm_kernel<T, D>),
-             dim3((p->T + tok_per_block - 1) / tok_per_block, p->H, p->B), dim3(gdn::kThreads), 0, na);
+gdn::OutArgs out_args(const gdn_fwd_params *p, int reverse, const ScanBufs &sb, int c0, int mode, float *acc) {
+    gdn::OutArgs oa;
+    oa.B = p->B; oa.T = p->T; oa.H = p->H; oa.NC = n_chunks(p->T); oa.reverse = reverse;
+    oa.c_begin = c0; oa.mode = mode;
+    oa.rec = sb.rec; oa.sc = sb.sc;
+    oa.gate = p->gate; oa.norm_w = p->norm_w; oa.eps = p->eps_norm;
+    oa.out = p->o; oa.acc = acc;
+    return oa;
 }
 
+// One scan's range-pipelined launches: preps on `prep_stream`, the state
+// chain on `state_stream` (range i waits for prep i), and the output of each
+// range on `out_stream` (waits for state i).  out_mode: see OutArgs.
 template <class T, int D>
-gdn_status plan_fwd(Plan &plan, const gdn_fwd_params *p, const float *S_T_rev, bool bidir) {
-    const Layout L = layout(p, bidir ? 2 : 1);
-    char *ws = static_cast<char *>(p->workspace);
-    float *ows = reinterpret_cast<float *>(ws + L.ows);
-    const size_t ows_bytes = round_up((size_t)p->B * p->H * n_chunks(p->T) * 64 * D * sizeof(float));
-    gdn_status st = plan_scan<T, D>(plan, p, bidir ? 0 : p->reverse, p->S0, p->S_T, ows, ws, L);
-    if (st != GDN_OK) return st;
-    if (!bidir) {
-        plan_norm<T, D>(plan, p, p->reverse, ows, nullptr);
-        return GDN_OK;
+void plan_scan(Plan &plan, const gdn_fwd_params *p, int reverse, const ScanBufs &sb, float *S_T, int prep_stream,
+               int state_stream, int out_stream, int out_mode, float *acc) {
+    const int NC = n_chunks(p->T), R = n_ranges(NC);
+    const void *prep = reinterpret_cast<const void *>(&gdn::gdn_prep_kernel<T, D>);
+    const void *state = reinterpret_cast<const void *>(&gdn::gdn_state_kernel<T, D>);
+    const void *out = reinterpret_cast<const void *>(&gdn::gdn_out_kernel<T, D>);
+    std::vector<int> prep_done(R), state_done(R);
+    for (int i = 0; i < R; ++i) {
+        const int c0 = range_begin(NC, R, i), c1 = range_begin(NC, R, i + 1);
+        plan.launch(prep_stream, "gdn_prep_kernel", prep, dim3(c1 - c0, p->H, p->B), dim3(gdn::kThreads),
+                    sizeof(gdn::PrepSmem<T, D>), prep_args<T, D>(p, reverse, sb, c0));
+        prep_done[i] = plan.record(prep_stream);
     }
-    float *ows2 = reinterpret_cast<float *>(ws + L.ows + ows_bytes);
-    st = plan_scan<T, D>(plan, p, 1, p->S0, const_cast<float *>(S_T_rev), ows2, ws, L);
-    if (st != GDN_OK) return st;
-    plan_norm<T, D>(plan, p, 0, ows, ows2);
+    const int used = p->B * p->H * (D / 16);
+    for (int i = 0; i < R; ++i) {
+        const int c0 = range_begin(NC, R, i), c1 = range_begin(NC, R, i + 1);
+        const float *S_in = i == 0 ? p->S0 : sb.smid[(i - 1) & 1];
+        float *S_out = i == R - 1 ? S_T : sb.smid[i & 1];
+        plan.wait(state_stream, prep_done[i]);
+        plan.launch(state_stream, "gdn_state_kernel", state, dim3((used + 7) / 8 * 8), dim3(gdn::kStateThreads),
+                    state_lds<T, D>(), state_args<T, D>(p, sb, c0, c1, S_in, S_out));
+        state_done[i] = plan.record(state_stream);
+    }
+    for (int i = 0; i < R; ++i) {
+        const int c0 = range_begin(NC, R, i), c1 = range_begin(NC, R, i + 1);
+        plan.wait(out_stream, state_done[i]);
+        plan.launch(out_stream, "gdn_out_kernel", out, dim3(c1 - c0, p->H, p->B), dim3(gdn::kThreads),
+                    sizeof(gdn::OutSmem<T, D>), out_args<T, D>(p, reverse, sb, c0, out_mode, acc));
+    }
+}
+
+template <class T, int D>
+gdn_status plan_fwd(Plan &plan, const gdn_fwd_params *p, float *S_T_rev, bool bidir) {
+    const Layout L = layout(p, bidir ? 2 : 1);
+    const int start = plan.record(0);
+    for (int s = 1; s < kStreams; ++s) plan.wait(s, start);
+    if (!bidir) {
+        plan_scan<T, D>(plan, p, p->reverse, scan_bufs(p, L, 0), p->S_T, 1, 0, 2, 0, nullptr);
+    } else {
+        // the two directions are independent: forward chain on stream 0,
+        // reversed chain on stream 3, preps on stream 1; the outputs run on
+        // stream 2, the reversed scan's after all of the forward scan's
+        float *acc = reinterpret_cast<float *>(static_cast<char *>(p->workspace) + L.acc);
+        plan_scan<T, D>(plan, p, 0, scan_bufs(p, L, 0), p->S_T, 1, 0, 2, 1, acc);
+        plan_scan<T, D>(plan, p, 1, scan_bufs(p, L, 1), S_T_rev, 1, 3, 2, 2, acc);
+    }
+    for (int s = 1; s < kStreams; ++s) plan.wait(0, plan.record(s));
     return GDN_OK;
 }
 
-gdn_status make_plan(Plan &plan, const gdn_fwd_params *p, const float *S_T_rev, bool bidir) {
+gdn_status make_plan(Plan &plan, const gdn_fwd_params *p, float *S_T_rev, bool bidir) {
     if (p->io_dtype == GDN_BF16 && p->Dk == 128) return plan_fwd<bf16, 128>(plan, p, S_T_rev, bidir);
     if (p->io_dtype == GDN_BF16 && p->Dk == 64) return plan_fwd<bf16, 64>(plan, p, S_T_rev, bidir);
     if (p->io_dtype == GDN_F32 && p->Dk == 64) return plan_fwd<float, 64>(plan, p, S_T_rev, bidir);
     return GDN_ERR_UNSUPPORTED;
 }
 
-gdn_status call(const gdn_fwd_params *p, const float *S_T_rev, bool bidir, hipEvent_t *events, int n_events,
+// Kernel attributes (dynamic LDS above 64 KB), set once per process.
+gdn_status set_attributes() {
+    static std::once_flag once;
+    static gdn_status result = GDN_OK;
+    std::call_once(once, [] {
+        struct A {
+            const void *fn;
+            size_t lds;
+        } attrs[] = {
+            {reinterpret_cast<const void *>(&gdn::gdn_prep_kernel<bf16, 128>), sizeof(gdn::PrepSmem<bf16, 128>)},
+            {reinterpret_cast<const void *>(&gdn::gdn_prep_kernel<bf16, 64>), sizeof(gdn::PrepSmem<bf16, 64>)},
+            {reinterpret_cast<const void *>(&gdn::gdn_prep_kernel<float, 64>), sizeof(gdn::PrepSmem<float, 64>)},
+            {reinterpret_cast<const void *>(&gdn::gdn_state_kernel<bf16, 128>), state_lds<bf16, 128>()},
+            {reinterpret_cast<const void *>(&gdn::gdn_state_kernel<bf16, 64>), state_lds<bf16, 64>()},
+            {reinterpret_cast<const void *>(&gdn::gdn_state_kernel<float, 64>), state_lds<float, 64>()},
+            {reinterpret_cast<const void *>(&gdn::gdn_out_kernel<bf16, 128>), sizeof(gdn::OutSmem<bf16, 128>)},
+            {reinterpret_cast<const void *>(&gdn::gdn_out_kernel<bf16, 64>), sizeof(gdn::OutSmem<bf16, 64>)},
+            {reinterpret_cast<const void *>(&gdn::gdn_out_kernel<float, 64>), sizeof(gdn::OutSmem<float, 64>)},
+        };
+        for (const A &a : attrs)
+            if (hipFuncSetAttribute(a.fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)a.lds) != hipSuccess)
+                result = GDN_ERR_HIP;
+    });
+    return result;
+}
+
+gdn_status call(const gdn_fwd_params *p, float *S_T_rev, bool bidir, hipEvent_t *timing, int n_timing,
                 hipStream_t s) {
     gdn_status st = validate(p, S_T_rev, bidir ? 2 : 1);
     if (st != GDN_OK) return st;
@@ -213,8 +372,10 @@ gdn_status call(const gdn_fwd_params *p, const float *S_T_rev, bool bidir, hipEv
     Plan plan;
     st = make_plan(plan, p, S_T_rev, bidir);
     if (st != GDN_OK) return st;
-    if (events && n_events < plan.n + 1) return GDN_ERR_INVALID_ARG;
-    return plan.run(s, events);
+    if (timing && n_timing < 2 * (int)plan.launches.size()) return GDN_ERR_INVALID_ARG;
+    st = set_attributes();
+    if (st != GDN_OK) return st;
+    return run_plan(plan, s, timing);
 }
 
 }  // namespace
@@ -249,7 +410,13 @@ gdn_status gdn_fwd_bidir(const gdn_fwd_params *p, float *S_T_rev, struct ihipStr
 
 int gdn_fwd_launch_count(const gdn_fwd_params *p, int bidirectional) {
     if (!sizes_ok(p) || !supported(p)) return -1;
-    return bidirectional ? 5 : 3;
+    try {
+        Plan plan;
+        if (make_plan(plan, p, nullptr, bidirectional != 0) != GDN_OK) return -1;
+        return (int)plan.launches.size();
+    } catch (...) {
+        return -1;
+    }
 }
 
 gdn_status gdn_fwd_timed(const gdn_fwd_params *p, float *S_T_rev, int bidirectional, struct ihipEvent_t **events,
@@ -263,12 +430,15 @@ gdn_status gdn_fwd_timed(const gdn_fwd_params *p, float *S_T_rev, int bidirectio
 }
 
 const char *gdn_fwd_launch_name(const gdn_fwd_params *p, int bidirectional, int i) {
-    static const char *uni[] = {"gdn_prep_kernel", "gdn_state_kernel", "gdn_norm_kernel"};
-    static const char *bi[] = {"gdn_prep_kernel", "gdn_state_kernel", "gdn_prep_kernel", "gdn_state_kernel",
-                               "gdn_norm_kernel"};
-    const int n = gdn_fwd_launch_count(p, bidirectional);
-    if (i < 0 || i >= n) return nullptr;
-    return bidirectional ? bi[i] : uni[i];
+    if (!sizes_ok(p) || !supported(p)) return nullptr;
+    try {
+        Plan plan;
+        if (make_plan(plan, p, nullptr, bidirectional != 0) != GDN_OK) return nullptr;
+        if (i < 0 || i >= (int)plan.launches.size()) return nullptr;
+        return plan.launches[i].name;  // points at a string literal
+    } catch (...) {
+        return nullptr;
+    }
 }
 
 const char *gdn_status_string(gdn_status s) {

@@ -3,20 +3,22 @@
 // The layer (LinMorph project page, "Why learn the initialization?": short
 // convolutions, update gates, decay terms, normalisation parameters; the
 // gated delta rule of the GDN paper, ref. [57] of the VMonarch page, section
-// 2) runs as three launches per scan:
+// 2) runs as three kernels per scan:
 //
 //   prep  : one workgroup per (chunk of 64 tokens, head, batch row), all in
 //           parallel.  Short conv + SiLU, L2 normalisation, cumulative log
 //           decay g, the decayed strictly-lower matrix A (b * K K^T), the
-//           solve (I + A) [W | U~] = [diag(b e^g) K | diag(b) V] by forward
-//           substitution, and the state-independent products
-//           Q' = diag(e^g) Q - P W and O0 = P U~ with P = (Q K^T o decay),
-//           all written to a per-chunk record in MFMA fragment order.
+//           solve (I + A) [W | U~] = [diag(b e^g) K | diag(b) V], and the
+//           state-independent products Q' = diag(e^g) Q - P W and O0 = P U~
+//           with P = (Q K^T o decay), all written to a per-chunk record in
+//           MFMA fragment order.
 //   state : one workgroup per (16 value channels, head, batch row), walking
 //           the chunks in order with its slice of the fp32 state in
-//           registers:  U = U~ - W S^T,  O = O0 + Q' S^T,
-//                       S^T <- e^{g_C} S^T + (D K)^T U,  D = diag(e^{g_C - g}).
-//   norm  : gated RMS normalisation of O over all value channels.
+//           registers:  U = U~ - W S^T,  S^T <- e^{g_C} S^T + (D K)^T U,
+//           D = diag(e^{g_C - g}); it exports each chunk's entry state.
+//   out   : one workgroup per (chunk, head, batch row), all in parallel:
+//           O = O0 + Q' S^T with the chunk's entry state, then the gated RMS
+//           normalisation over all value channels.
 //
 // The chunked form reproduces the token-by-token recurrence exactly up to
 // rounding: inside a chunk, with S0 the entry state, the step is
@@ -26,6 +28,8 @@
 // exit state e^{g_C} S0 + U^T D K.  A partial last chunk is padded with
 // q = k = v = 0, b = 0, log a = 0, which leaves the state unchanged.
 #pragma once
+#include <type_traits>
+
 #include "frag.hpp"
 
 namespace gdn {
@@ -49,6 +53,7 @@ template <int D> struct Rec {
 
 struct PrepArgs {
     int B, T, H, NC, reverse;
+    int c_begin;  // first chunk of this launch (chunk = c_begin + blockIdx.x)
     const void *q, *k, *v;
     const float *log_a, *beta, *conv_q, *conv_k, *conv_v;
     float eps_l2;
@@ -58,21 +63,34 @@ struct PrepArgs {
 
 struct StateArgs {
     int B, T, H, NC;
+    int c_begin, c_end;  // chunks [c_begin, c_end) of the scan
     const void *rec;
     const float *gC;
-    const float *S0;  // [B][H][D][D] or null
-    float *S_T;       // [B][H][D][D] or null
-    float *ows;       // [B][H][NC*64][D] unnormalised o, scan order
+    const float *S_in;   // [B][H][D][D] state entering chunk c_begin, or null (zeros)
+    float *S_out;        // [B][H][D][D] state after chunk c_end - 1, or null
+    void *sc;            // [B][H][NC][D/16 value blocks] chunk-entry S^T as B fragments
 };
 
-struct NormArgs {
+// S^T at the entry of each chunk, as B fragments over the key channels: per
+// (batch, head, chunk, value block) KBD fragments of 64 lanes x KPL values.
+template <class T, int D> struct ScLayout {
+    static constexpr int KPL = Mfma<T>::KPL;
+    static constexpr int KBD = D / (4 * KPL);
+    static constexpr int PER_VB = KBD * 64 * KPL;  // = 16 * D elements
+    static constexpr int PER_CHUNK = (D / 16) * PER_VB;
+};
+
+struct OutArgs {
     int B, T, H, NC, reverse;
-    const float *ows;           // first (or only) scan
-    const float *ows2;          // time-reversed scan, or null
+    int c_begin;        // chunk = c_begin + blockIdx.x
+    int mode;           // 0: write y; 1: write this scan's y to acc (fp32); 2: y = acc + this scan's y
+    const void *rec;    // chunk records (QP, O0)
+    const void *sc;     // chunk-entry states
     const void *gate;
-    const float *norm_w;        // [H][D] or null
+    const float *norm_w;  // [H][D] or null
     float eps;
-    void *out;
+    void *out;          // y [B][T][H][D] (modes 0, 2)
+    float *acc;         // [B][T][H][D] fp32 (modes 1, 2)
 };
 
 // 8 consecutive values as float
@@ -257,7 +275,7 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_prep_kernel(PrepArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     SM &sm = *reinterpret_cast<SM *>(smem_raw);
 
-    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int c = a.c_begin + blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, n = lane % 16, g = lane / 16;
 
     // ---- gates: b and the cumulative log decay g inside the chunk
@@ -465,35 +483,32 @@ template <class T, int D> struct StateSmem {
     static constexpr int LDS_U = 16 + (sizeof(T) == 2 ? 8 : 4);
     T Sx[64 * LDS_S];  // S^T as B fragments, per lane
     T Ux[64 * LDS_U];  // U as B fragments, per lane
+    float gcs[4];      // e^{g_C} of the chunks in the ring slots
+    uint32_t sink[64]; // destination of the L2 prefetch loads (never read)
 };
 
-// One chunk's operands for one wave of a state workgroup, in registers.
-template <class T, int D> struct ChunkOps {
-    typedef typename Mfma<T>::frag frag;
-    static constexpr int KPL = Mfma<T>::KPL;
-    static constexpr int KBD = D / (4 * KPL);
-    static constexpr int KBC = 16 / KPL;
-    static constexpr int MT = D / 64;
-    frag wn[KBD], qp[KBD], dk[MT][KBC];
-    floatx4 ut, o0;
-    float gc;
-    __device__ __forceinline__ void load(const T *rec, const float *gcp, int vb, int w, int lane) {
-#pragma unroll
-        for (int kb = 0; kb < KBD; ++kb) {
-            wn[kb] = *reinterpret_cast<const frag *>(rec + Rec<D>::WN + ((w * KBD + kb) * 64 + lane) * KPL);
-            qp[kb] = *reinterpret_cast<const frag *>(rec + Rec<D>::QP + ((w * KBD + kb) * 64 + lane) * KPL);
-        }
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int kb = 0; kb < KBC; ++kb)
-                dk[mt][kb] = *reinterpret_cast<const frag *>(
-                    rec + Rec<D>::DKT + (((w * MT + mt) * KBC + kb) * 64 + lane) * KPL);
-        ut = load4(rec + Rec<D>::UT + ((vb * 4 + w) * 64 + lane) * 4);
-        o0 = load4(rec + Rec<D>::O0 + ((vb * 4 + w) * 64 + lane) * 4);
-        gc = *gcp;
-    }
+// Ring of chunk operands in LDS (dynamic shared memory): 3 slots, each the
+// record's -W and (D K)^T (head-wide) and the workgroup's own U~ block, copied
+// verbatim so fragments keep the record's layout.
+template <class T, int D> struct StateRing {
+    static constexpr int WN_E = 64 * D;          // elements
+    static constexpr int DK_E = 64 * D;
+    static constexpr int UT_E = 4 * 64 * 4;      // one value block of U~
+    static constexpr int SLOT_E = WN_E + DK_E + UT_E;
+    static constexpr int SLOT_BYTES = SLOT_E * (int)sizeof(T);
+    static constexpr int N16 = SLOT_BYTES / 16;  // 16-byte units per slot
+    static constexpr int NDMA = N16 / 64;        // copy instructions per chunk (64 lanes x 16 B)
+    static constexpr int SLOTS = 3;
+    static constexpr int BYTES = SLOTS * SLOT_BYTES;
+    static_assert(N16 % 64 == 0, "slot must be a whole number of wave copies");
 };
+
+constexpr int kStateThreads = kThreads + 192;  // 4 compute waves, 2 copy waves, 1 prefetch + export wave
+constexpr int kL2Ahead = 8;                    // chunks the L2 prefetch wave runs ahead
+
+// s_waitcnt immediate for "at most n vector memory operations outstanding"
+// (gfx9 encoding; the LDS and export counters are left unconstrained).
+constexpr unsigned vmcnt_imm(unsigned n) { return (n & 0xFu) | ((n >> 4) << 14) | (0x7u << 4) | (0xFu << 8); }
 
 // Workgroup placement: launched as a 1-D grid whose size is a multiple of 8.
 // Consecutive workgroup ids go to different XCDs (round robin), so id L is
@@ -506,22 +521,66 @@ __device__ __forceinline__ bool xcd_position(int L, int nwg_used, int nwg_launch
     return p < nwg_used;
 }
 
-// One workgroup owns a block of 16 value channels of one head.  Wave w
-// computes U and O for tokens 16w..16w+15 (K = all key channels) and updates
-// the key-channel rows w*D/4.. of S^T (K = all tokens); S^T and U are
-// exchanged through LDS once per chunk each.
+// L2 prefetch: touch one 128-byte line per lane of the part of chunk record
+// `rec` this workgroup will copy: the head-wide -W and (D K)^T regions are
+// split over the head's NV workgroups (they share the XCD's L2), and each
+// workgroup touches its own U~ block.  The loads land in a scratch LDS word
+// that is never read.
 template <class T, int D>
-__global__ __launch_bounds__(kThreads) void gdn_state_kernel(StateArgs a) {
+__device__ __forceinline__ void touch_record(const T *rec, int vb, int lane, uint32_t *sink) {
+    constexpr int NV = D / 16;
+    constexpr int line = 128;
+    constexpr int region_lines = 64 * D * (int)sizeof(T) / line;  // one 64 x D matrix
+    constexpr int per_wg = 2 * region_lines / NV;
+    constexpr int own_lines = 4 * 64 * 4 * (int)sizeof(T) / line;
+    constexpr int n_touch = per_wg + own_lines;
+    const char *base = reinterpret_cast<const char *>(rec);
+#pragma unroll
+    for (int k0 = 0; k0 < n_touch; k0 += 64) {
+        const int k = k0 + lane;
+        if (k < n_touch) {
+            size_t off;
+            if (k < per_wg) {
+                const int l = vb + NV * k;  // line among -W, then (D K)^T
+                off = l < region_lines ? (size_t)Rec<D>::WN * sizeof(T) + (size_t)l * line
+                                       : (size_t)Rec<D>::DKT * sizeof(T) + (size_t)(l - region_lines) * line;
+            } else {
+                off = (size_t)(Rec<D>::UT + vb * 4 * 64 * 4) * sizeof(T) + (size_t)(k - per_wg) * line;
+            }
+            __builtin_amdgcn_global_load_lds(base + off, sink, 4, 0, 0);
+        }
+    }
+}
+
+// One workgroup owns a block of 16 value channels of one head.
+//   Compute wave w (0..3): U for tokens 16w..16w+15 (K = all key channels),
+//   then the key-channel rows w*D/4.. of S^T (K = all tokens).  S^T and U are
+//   exchanged through LDS once per chunk each (two barriers per chunk).  The
+//   compute waves touch no global memory inside the chunk loop.
+//   Copy waves (4, 5): keep the LDS ring two chunks ahead with direct-to-LDS
+//   copies (each wave half of every slot; one issuing wave alone cannot
+//   keep up), and each waits for its half of the next chunk before the
+//   second barrier of the current one.
+//   Wave 6: touches the records kL2Ahead chunks ahead so that the copies hit
+//   L2, and stores each chunk's entry state (read back from the S^T exchange
+//   buffer) for the output kernel.
+//   Waves 4-6 use bare barriers, so their memory operations are never waited
+//   for by the compute waves' fences.  Every wave passes 1 + 2 * chunks
+//   barriers.
+template <class T, int D>
+__global__ __launch_bounds__(kStateThreads) void gdn_state_kernel(StateArgs a) {
     typedef Mfma<T> M;
     typedef typename M::frag frag;
-    typedef ChunkOps<T, D> Ops;
+    typedef StateRing<T, D> RG;
     constexpr int KPL = M::KPL;
-    constexpr int KBD = Ops::KBD;
-    constexpr int KBC = Ops::KBC;
-    constexpr int MT = Ops::MT;
+    constexpr int KBD = D / (4 * KPL);
+    constexpr int KBC = 16 / KPL;
+    constexpr int MT = D / 64;
     constexpr int NV = D / 16;
     typedef StateSmem<T, D> SM;
     __shared__ SM sm;
+    extern __shared__ __align__(16) unsigned char ring_raw[];
+    T *ring = reinterpret_cast<T *>(ring_raw);
 
     int p;
     if (!xcd_position(blockIdx.x, a.B * a.H * NV, gridDim.x, p)) return;
@@ -529,115 +588,243 @@ __global__ __launch_bounds__(kThreads) void gdn_state_kernel(StateArgs a) {
     const size_t bh = p / NV;
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, n = lane % 16, g = lane / 16;
     const int vcol = 16 * vb + n;
+    const T *rec0 = static_cast<const T *>(a.rec) + bh * a.NC * (size_t)Rec<D>::SIZE;
+    const int n_ch = a.c_end - a.c_begin;
 
-    // S^T slice: rows (key channels) w*D/4 + 16 mt + 4g + ii, column vcol
+    if (w == 6) {
+        // ---- L2 prefetch and entry-state export
+        for (int c = a.c_begin; c < min(a.c_begin + kL2Ahead, a.c_end); ++c)
+            touch_record<T, D>(rec0 + (size_t)c * Rec<D>::SIZE, vb, lane, sm.sink);
+        __builtin_amdgcn_s_barrier();  // barrier 0
+        const T *sx = sm.Sx + lane * SM::LDS_S;
+        for (int c = a.c_begin; c < a.c_end; ++c) {
+            __builtin_amdgcn_s_barrier();  // barrier 1: S^T of chunk c published
+            if (c + kL2Ahead < a.c_end)
+                touch_record<T, D>(rec0 + (size_t)(c + kL2Ahead) * Rec<D>::SIZE, vb, lane, sm.sink);
+            T *scp = static_cast<T *>(a.sc) + ((bh * a.NC + c) * NV + vb) * (size_t)ScLayout<T, D>::PER_VB;
+#pragma unroll
+            for (int kb = 0; kb < KBD; ++kb)
+                *reinterpret_cast<frag *>(scp + (kb * 64 + lane) * KPL) =
+                    *reinterpret_cast<const frag *>(sx + kb * KPL);
+            __builtin_amdgcn_s_barrier();  // barrier 2 (S^T is rewritten after it)
+        }
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        return;
+    }
+    if (w == 4 || w == 5) {
+        // ---- copy waves: wave 4 copies units [0, H4) of each slot, wave 5 the rest and e^{g_C}
+        constexpr int H4 = RG::NDMA / 2;
+        auto copy_range = [&](const char *rec, char *slot, auto i0c, auto i1c) {
+            constexpr int I0 = decltype(i0c)::value, I1 = decltype(i1c)::value;
+#pragma unroll
+            for (int i = I0; i < I1; ++i) {
+                const int u = i * 64 + lane;  // 16-byte unit of the slot
+                size_t src;
+                if (i * 64 < RG::WN_E * (int)sizeof(T) / 16)
+                    src = (size_t)Rec<D>::WN * sizeof(T) + (size_t)u * 16;
+                else if (i * 64 < (RG::WN_E + RG::DK_E) * (int)sizeof(T) / 16)
+                    src = (size_t)Rec<D>::DKT * sizeof(T) + (size_t)(u - RG::WN_E * (int)sizeof(T) / 16) * 16;
+                else
+                    src = (size_t)(Rec<D>::UT + vb * RG::UT_E) * sizeof(T) +
+                          (size_t)(u - (RG::WN_E + RG::DK_E) * (int)sizeof(T) / 16) * 16;
+                __builtin_amdgcn_global_load_lds(rec + src, slot + i * 1024, 16, 0, 0);
+            }
+        };
+        auto copy_chunk = [&](int c) {
+            const char *rec = reinterpret_cast<const char *>(rec0 + (size_t)c * Rec<D>::SIZE);
+            char *slot = reinterpret_cast<char *>(ring + ((c - a.c_begin) % RG::SLOTS) * RG::SLOT_E);
+            if (w == 4) {
+                copy_range(rec, slot, std::integral_constant<int, 0>(), std::integral_constant<int, H4>());
+            } else {
+                copy_range(rec, slot, std::integral_constant<int, H4>(), std::integral_constant<int, RG::NDMA>());
+                if (lane == 0)
+                    __builtin_amdgcn_global_load_lds(a.gC + bh * a.NC + c, &sm.gcs[(c - a.c_begin) % RG::SLOTS], 4,
+                                                     0, 0);
+            }
+        };
+        // per chunk this wave issues H4 (wave 4) or NDMA - H4 + 1 (wave 5) copies
+        copy_chunk(a.c_begin);
+        if (n_ch > 1) {
+            copy_chunk(a.c_begin + 1);
+            if (w == 4)
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(H4));
+            else
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(RG::NDMA - H4 + 1));
+        } else {
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        }
+        __builtin_amdgcn_s_barrier();  // barrier 0: chunk c_begin is in its slot
+        for (int c = a.c_begin; c < a.c_end; ++c) {
+            __builtin_amdgcn_s_barrier();  // barrier 1: the slot of chunk c-1 is free
+            if (c + 2 < a.c_end) {
+                copy_chunk(c + 2);
+                // this wave's part of chunk c+1 lands before barrier 2
+                if (w == 4)
+                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(H4));
+                else
+                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(RG::NDMA - H4 + 1));
+            } else {
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            }
+            __builtin_amdgcn_s_barrier();  // barrier 2
+        }
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        return;
+    }
+
+    // ---- compute waves.  S^T slice: rows (key channels) w*D/4 + 16 mt + 4g + ii, column vcol
     floatx4 S[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        if (a.S0)
-            S[mt] = *reinterpret_cast<const floatx4 *>(a.S0 + (bh * D + vcol) * D + w * (D / 4) + 16 * mt + 4 * g);
+        if (a.S_in)
+            S[mt] = *reinterpret_cast<const floatx4 *>(a.S_in + (bh * D + vcol) * D + w * (D / 4) + 16 * mt + 4 * g);
         else
             S[mt] = zero4();
     }
-    const T *rec0 = static_cast<const T *>(a.rec) + bh * a.NC * (size_t)Rec<D>::SIZE;
-    const float *gc0 = a.gC + bh * a.NC;
     T *sx = sm.Sx + lane * SM::LDS_S;
     T *ux = sm.Ux + lane * SM::LDS_U;
-
-    auto step = [&](const Ops &f, int c) {
+    __syncthreads();  // barrier 0
+    for (int c = a.c_begin; c < a.c_end; ++c) {
+        // this chunk's operands: its slot is complete since the previous barrier
+        const T *slot = ring + ((c - a.c_begin) % RG::SLOTS) * RG::SLOT_E;
+        frag wn[KBD], dk[MT][KBC];
+#pragma unroll
+        for (int kb = 0; kb < KBD; ++kb) wn[kb] = *reinterpret_cast<const frag *>(slot + ((w * KBD + kb) * 64 + lane) * KPL);
+        floatx4 u = load4(slot + RG::WN_E + RG::DK_E + (w * 64 + lane) * 4);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int kb = 0; kb < KBC; ++kb)
+                dk[mt][kb] = *reinterpret_cast<const frag *>(slot + RG::WN_E +
+                                                             (((w * MT + mt) * KBC + kb) * 64 + lane) * KPL);
+        const float gc = sm.gcs[(c - a.c_begin) % RG::SLOTS];
         // publish this wave's part of S^T (elements e = 4 (w MT + mt) + ii)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) sx[4 * (w * MT + mt) + ii] = (T)S[mt][ii];
-        __syncthreads();
+        __syncthreads();  // barrier 1
         frag sB[KBD];
 #pragma unroll
         for (int kb = 0; kb < KBD; ++kb) sB[kb] = *reinterpret_cast<const frag *>(sx + kb * KPL);
-        // U = U~ + WN S^T and O = O0 + Q' S^T for tokens 16w..16w+15
-        floatx4 u = f.ut, o = f.o0;
+        // U = U~ + WN S^T for tokens 16w..16w+15
 #pragma unroll
-        for (int kb = 0; kb < KBD; ++kb) {
-            u = M::mma(f.wn[kb], sB[kb], u);
-            o = M::mma(f.qp[kb], sB[kb], o);
-        }
+        for (int kb = 0; kb < KBD; ++kb) u = M::mma(wn[kb], sB[kb], u);
         // publish U (elements e = 4 w + ii)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) ux[4 * w + ii] = (T)u[ii];
-        __syncthreads();
+        __syncthreads();  // barrier 2
         frag uB[KBC];
 #pragma unroll
         for (int kb = 0; kb < KBC; ++kb) uB[kb] = *reinterpret_cast<const frag *>(ux + kb * KPL);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            S[mt] *= f.gc;
+            S[mt] *= gc;
 #pragma unroll
-            for (int kb = 0; kb < KBC; ++kb) S[mt] = M::mma(f.dk[mt][kb], uB[kb], S[mt]);
+            for (int kb = 0; kb < KBC; ++kb) S[mt] = M::mma(dk[mt][kb], uB[kb], S[mt]);
         }
-        // unnormalised output (the normalisation pass reduces over all channels)
-        const int s0 = c * 64 + 16 * w + 4 * g;
-        float *orow = a.ows + (bh * (size_t)a.NC * 64 + s0) * D + vcol;
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) orow[(size_t)ii * D] = o[ii];
-    };
-
-    // two register sets: chunk c+1's operands load while chunk c computes.  The
-    // loads are unconditional (the index is clamped to the last chunk) and the
-    // loop has no early exit, so no branch merges different loads in flight.
-    Ops A, B;
-    const int last = a.NC - 1;
-    auto at = [&](int cc) { return rec0 + (size_t)min(cc, last) * Rec<D>::SIZE; };
-    auto gat = [&](int cc) { return gc0 + min(cc, last); };
-    A.load(at(0), gat(0), vb, w, lane);
-    const int pairs = a.NC / 2;
-    for (int i = 0; i < pairs; ++i) {
-        const int c = 2 * i;
-        B.load(at(c + 1), gat(c + 1), vb, w, lane);
-        step(A, c);
-        A.load(at(c + 2), gat(c + 2), vb, w, lane);
-        step(B, c + 1);
     }
-    if (a.NC & 1) step(A, a.NC - 1);
-    if (a.S_T) {
+    if (a.S_out) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-            *reinterpret_cast<floatx4 *>(a.S_T + (bh * D + vcol) * D + w * (D / 4) + 16 * mt + 4 * g) = S[mt];
+            *reinterpret_cast<floatx4 *>(a.S_out + (bh * D + vcol) * D + w * (D / 4) + 16 * mt + 4 * g) = S[mt];
     }
 }
 
-// ====================================================================== norm
+// ======================================================================= out
+template <class T, int D> struct OutSmem {
+    static constexpr int LDO = D + 4;  // fp32 rows of O
+    T sc[ScLayout<T, D>::PER_CHUNK];  // entry state of every value block, as B fragments
+    float Os[64 * LDO];
+};
+
 template <class T, int D>
-__global__ __launch_bounds__(kThreads) void gdn_norm_kernel(NormArgs a) {
-    constexpr int G = D / 8;
-    const int tid = threadIdx.x, cg = tid % G;
-    const int t0 = blockIdx.x * (kThreads / G) + tid / G;  // input (output) token
-    const bool live = t0 < a.T;
-    const int t = live ? t0 : a.T - 1;  // idle threads still take part in the shuffles
-    const int h = blockIdx.y, b = blockIdx.z;
+__global__ __launch_bounds__(kThreads, 2) void gdn_out_kernel(OutArgs a) {
+    typedef Mfma<T> M;
+    typedef typename M::frag frag;
+    typedef ScLayout<T, D> SL;
+    constexpr int KPL = M::KPL;
+    constexpr int KBD = D / (4 * KPL);
+    constexpr int NV = D / 16;
+    typedef OutSmem<T, D> SM;
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    SM &sm = *reinterpret_cast<SM *>(smem_raw);
+
+    const int c = a.c_begin + blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, n = lane % 16, g = lane / 16;
     const size_t bh = (size_t)b * a.H + h;
-    const size_t L = (size_t)a.NC * 64;
-    float wv[8], gv[8], y[8];
+
+    // stage the chunk-entry state of all value blocks
+    {
+        const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const T *>(a.sc) +
+                                                           (bh * a.NC + c) * (size_t)SL::PER_CHUNK);
+        uint4 *dst = reinterpret_cast<uint4 *>(sm.sc);
+        constexpr int N16 = SL::PER_CHUNK * (int)sizeof(T) / 16;
+#pragma unroll
+        for (int i = tid; i < N16; i += kThreads) dst[i] = src[i];
+    }
+    const T *rec = static_cast<const T *>(a.rec) + (bh * a.NC + c) * (size_t)Rec<D>::SIZE;
+    frag qp[KBD];
+#pragma unroll
+    for (int kb = 0; kb < KBD; ++kb)
+        qp[kb] = *reinterpret_cast<const frag *>(rec + Rec<D>::QP + ((w * KBD + kb) * 64 + lane) * KPL);
+    floatx4 o[NV];
+#pragma unroll
+    for (int vb = 0; vb < NV; ++vb) o[vb] = load4(rec + Rec<D>::O0 + ((vb * 4 + w) * 64 + lane) * 4);
+    __syncthreads();
+    // O = O0 + Q' S^T for tokens 16w.., all value channels
+#pragma unroll
+    for (int vb = 0; vb < NV; ++vb) {
+#pragma unroll
+        for (int kb = 0; kb < KBD; ++kb)
+            o[vb] = M::mma(qp[kb], *reinterpret_cast<const frag *>(sm.sc + ((vb * KBD + kb) * 64 + lane) * KPL),
+                           o[vb]);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) sm.Os[(16 * w + 4 * g + ii) * SM::LDO + 16 * vb + n] = o[vb][ii];
+    }
+    __syncthreads();
+
+    // gated RMS normalisation: G threads per token row, 8 channels each
+    constexpr int G = D / 8;
+    constexpr int TPP = kThreads / G;
+    const int cg = tid % G;
+    float wv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) wv[i] = a.norm_w ? a.norm_w[h * D + 8 * cg + i] : 1.f;
-    load8(static_cast<const T *>(a.gate) + (((size_t)b * a.T + t) * a.H + h) * D + 8 * cg, gv);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) { gv[i] = wv[i] * silu(gv[i]); y[i] = 0.f; }
-    for (int pass = 0; pass < (a.ows2 ? 2 : 1); ++pass) {
-        const bool rev = pass == 0 ? a.reverse != 0 : true;
-        const float *ows = pass == 0 ? a.ows : a.ows2;
-        const int s = rev ? a.T - 1 - t : t;  // scan position of this token
+    for (int pass = 0; pass < 64 / TPP; ++pass) {
+        const int r = pass * TPP + tid / G;
+        const int s = c * 64 + r;
+        const bool live = s < a.T;
+        const int t = a.reverse ? a.T - 1 - (live ? s : a.T - 1) : (live ? s : a.T - 1);
+        const float *orow = sm.Os + r * SM::LDO + 8 * cg;
         float ov[8];
-        load8(ows + (bh * L + s) * D + 8 * cg, ov);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ov[i] = orow[i];
         float ss = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) ss += ov[i] * ov[i];
 #pragma unroll
         for (int m = 1; m < G; m <<= 1) ss += __shfl_xor(ss, m, 64);
         const float inv = 1.0f / sqrtf(ss / D + a.eps);
+        if (!live) continue;
+        const size_t off = (((size_t)b * a.T + t) * a.H + h) * D + 8 * cg;
+        float gv[8], y[8];
+        load8(static_cast<const T *>(a.gate) + off, gv);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) y[i] += ov[i] * inv * gv[i];
+        for (int i = 0; i < 8; ++i) y[i] = ov[i] * inv * wv[i] * silu(gv[i]);
+        if (a.mode == 1) {
+            store8(a.acc + off, y);
+        } else {
+            if (a.mode == 2) {
+                float prev[8];
+                load8(a.acc + off, prev);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) y[i] += prev[i];
+            }
+            store8(static_cast<T *>(a.out) + off, y);
+        }
     }
-    if (live) store8(static_cast<T *>(a.out) + (((size_t)b * a.T + t) * a.H + h) * D + 8 * cg, y);
 }
 
 }  // namespace gdn
