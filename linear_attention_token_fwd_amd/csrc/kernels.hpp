@@ -316,7 +316,7 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_prep_kernel(PrepArgs a) {
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int i = 16 * w + 4 * g + ii, j = 16 * t + n;
-                sm.Am[i * SM::LDA + j] = (j < i) ? sm.b[i] * expf(sm.g[i] - sm.g[j]) * acc[t][ii] : 0.f;
+                sm.Am[i * SM::LDA + j] = (j < i) ? sm.b[i] * __expf(sm.g[i] - sm.g[j]) * acc[t][ii] : 0.f;
             }
         }
     }
@@ -344,6 +344,10 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_prep_kernel(PrepArgs a) {
     // wave's NCT column tiles; block row I: X_I = Tinv_I (R_I - sum_{J<I} A_IJ X_J)
     floatx4 X[4][NCT];
     kfrag Xf[4][NCT];
+    // waves 0, 1 own the columns of diag(b e^g) K (W), waves 2, 3 those of diag(b) V (U~)
+    const bool wave_k = w < 2;
+    const T *rsrc = wave_k ? sm.Ks : sm.Vs;
+    const int col0 = (D / 2) * (w & 1);  // first column of this wave inside K or V
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
         kfrag aIJ[4];
@@ -354,19 +358,23 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_prep_kernel(PrepArgs a) {
             aIJ[J] = K::from4(-v);
         }
         const kfrag tI = K::from4(*reinterpret_cast<const floatx4 *>(sm.Td + (16 * I + n) * SM::LDTD + 4 * g));
+        float scale[4];
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int t = 16 * I + 4 * g + ii;
+            scale[ii] = wave_k ? sm.b[t] * sm.eg[t] : sm.b[t];
+        }
+        floatx4 acc[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+                acc[ct][ii] = scale[ii] * to_f(rsrc[(16 * I + 4 * g + ii) * SM::LDX + col0 + 16 * ct + n]);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-            const int col = (D / 2) * w + 16 * ct + n;
-            floatx4 acc;
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int t = 16 * I + 4 * g + ii;
-                acc[ii] = col < D ? sm.b[t] * sm.eg[t] * to_f(sm.Ks[t * SM::LDX + col])
-                                  : sm.b[t] * to_f(sm.Vs[t * SM::LDX + col - D]);
-            }
-#pragma unroll
-            for (int J = 0; J < I; ++J) acc = K::mma(aIJ[J], Xf[J][ct], acc);
-            X[I][ct] = K::mma(tI, K::from4(acc), zero4());
+            for (int J = 0; J < I; ++J) acc[ct] = K::mma(aIJ[J], Xf[J][ct], acc[ct]);
+            X[I][ct] = K::mma(tI, K::from4(acc[ct]), zero4());
             Xf[I][ct] = K::from4(X[I][ct]);
         }
     }
@@ -391,7 +399,7 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_prep_kernel(PrepArgs a) {
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int i = 16 * w + 4 * g + ii, j = 16 * t + n;
-                P[i * SM::LDP + j] = (T)((j <= i) ? expf(sm.g[i] - sm.g[j]) * acc[t][ii] : 0.f);
+                P[i * SM::LDP + j] = (T)((j <= i) ? __expf(sm.g[i] - sm.g[j]) * acc[t][ii] : 0.f);
             }
         }
     }
@@ -408,7 +416,6 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_prep_kernel(PrepArgs a) {
             for (int kb = 0; kb < KBC; ++kb) pf[kb] = row_frag(P + (16 * R + n) * SM::LDP, kb, g);
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
-                const int col = (D / 2) * w + 16 * ct + n;
                 floatx4 acc = zero4();
 #pragma unroll
                 for (int kb = 0; kb < KBC; ++kb) {
@@ -420,8 +427,9 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_prep_kernel(PrepArgs a) {
                     }
                     acc = M::mma(pf[kb], xb, acc);
                 }
-                if (col < D) {
+                if (wave_k) {
                     // Q' rows 16R + 4g + ii, staged in Qs over the q^ values it replaces
+                    const int col = col0 + 16 * ct + n;
 #pragma unroll
                     for (int ii = 0; ii < 4; ++ii) {
                         const int t = 16 * R + 4 * g + ii;
@@ -429,23 +437,22 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_prep_kernel(PrepArgs a) {
                         sm.Qs[t * SM::LDX + col] = (T)qv;
                     }
                 } else {
-                    const int vb = (col - D) / 16;
+                    const int vb = (col0 + 16 * ct) / 16;
                     store4(rec + Rec<D>::O0 + ((vb * 4 + R) * 64 + lane) * 4, acc);
                     store4(rec + Rec<D>::UT + ((vb * 4 + R) * 64 + lane) * 4, X[R][ct]);
                 }
             }
         }
         // -W staged row-major in Vs (v^ is no longer needed)
+        if (wave_k) {
 #pragma unroll
-        for (int I = 0; I < 4; ++I)
+            for (int I = 0; I < 4; ++I)
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                const int col = (D / 2) * w + 16 * ct + n;
-                if (col < D) {
+                for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-                    for (int ii = 0; ii < 4; ++ii) sm.Vs[(16 * I + 4 * g + ii) * SM::LDX + col] = (T)(-X[I][ct][ii]);
-                }
-            }
+                    for (int ii = 0; ii < 4; ++ii)
+                        sm.Vs[(16 * I + 4 * g + ii) * SM::LDX + col0 + 16 * ct + n] = (T)(-X[I][ct][ii]);
+        }
     }
     __syncthreads();
 
