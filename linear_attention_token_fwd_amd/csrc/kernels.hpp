@@ -128,6 +128,18 @@ __device__ __forceinline__ floatx4 load4(const bf16 *p) {
     return floatx4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
 }
 __device__ __forceinline__ floatx4 load4(const float *p) { return *reinterpret_cast<const floatx4 *>(p); }
+// the same in two steps: the load, and the widening to fp32 when it is used
+template <class T> struct Vec4;
+template <> struct Vec4<bf16> {
+    typedef bf16x4 type;
+    static __device__ __forceinline__ floatx4 widen(const type &v) {
+        return floatx4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+    }
+};
+template <> struct Vec4<float> {
+    typedef floatx4 type;
+    static __device__ __forceinline__ floatx4 widen(const type &v) { return v; }
+};
 
 // Fragment kb of a row-major row (k contiguous) in tile-chained K order.
 __device__ __forceinline__ bf16x8 row_frag(const bf16 *row, int kb, int g) {
@@ -485,18 +497,34 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_prep_kernel(PrepArgs a) {
 }
 
 // ===================================================================== state
-template <class T, int D> struct StateSmem {
-    static constexpr int LDS_S = D / 4 + (sizeof(T) == 2 ? 8 : 4);
-    static constexpr int LDS_U = 16 + (sizeof(T) == 2 ? 8 : 4);
-    T Sx[64 * LDS_S];  // S^T as B fragments, per lane
-    T Ux[64 * LDS_U];  // U as B fragments, per lane
-    float gcs[4];      // e^{g_C} of the chunks in the ring slots
-    uint32_t sink[64]; // destination of the L2 prefetch loads (never read)
-};
+// Barriers that do not wait for vector memory.  The compiler fences and
+// scheduling barriers keep it from moving memory accesses (or any other
+// instruction) across the barrier; lds_barrier() also waits for this wave's
+// LDS accesses so that its LDS writes are visible after it.
+__device__ __forceinline__ void bare_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// s_waitcnt immediate for "at most n vector memory operations outstanding"
+// (gfx9 encoding; the LDS and export counters are left unconstrained).
+constexpr unsigned vmcnt_imm(unsigned n) { return (n & 0xFu) | ((n >> 4) << 14) | (0x7u << 4) | (0xFu << 8); }
+constexpr unsigned kLgkm0 = 0xF | (0x3u << 14) | (0x7u << 4);  // lgkmcnt(0), others unconstrained
+__device__ __forceinline__ void lds_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(kLgkm0);
+    bare_barrier();
+}
 
-// Ring of chunk operands in LDS (dynamic shared memory): 3 slots, each the
-// record's -W and (D K)^T (head-wide) and the workgroup's own U~ block, copied
-// verbatim so fragments keep the record's layout.
+// Ring of chunk operands in LDS (dynamic shared memory): each slot holds the
+// record's -W and (D K)^T (head-wide) and the workgroup's own U~ block,
+// copied verbatim so fragments keep the record's layout.  Every read of chunk
+// c's slot lies between the barriers of chunks c-1 and c, so after the
+// barrier of chunk c-1 the copy of chunk c+AHEAD may go into chunk c-1's
+// slot: the ring has AHEAD + 1 slots, four (copies run three chunks ahead)
+// where they fit in LDS, else three.
 template <class T, int D> struct StateRing {
     static constexpr int WN_E = 64 * D;          // elements
     static constexpr int DK_E = 64 * D;
@@ -505,17 +533,21 @@ template <class T, int D> struct StateRing {
     static constexpr int SLOT_BYTES = SLOT_E * (int)sizeof(T);
     static constexpr int N16 = SLOT_BYTES / 16;  // 16-byte units per slot
     static constexpr int NDMA = N16 / 64;        // copy instructions per chunk (64 lanes x 16 B)
-    static constexpr int SLOTS = 3;
+    static constexpr int SLOTS = 4 * SLOT_BYTES <= 140 * 1024 ? 4 : 3;
+    static constexpr int AHEAD = SLOTS - 1;
     static constexpr int BYTES = SLOTS * SLOT_BYTES;
     static_assert(N16 % 64 == 0, "slot must be a whole number of wave copies");
 };
 
-constexpr int kStateThreads = kThreads + 192;  // 4 compute waves, 2 copy waves, 1 prefetch + export wave
-constexpr int kL2Ahead = 8;                    // chunks the L2 prefetch wave runs ahead
+template <class T, int D> struct StateSmem {
+    floatx4 Up[2][2][4][64];  // [chunk parity][wave][token tile][lane] partial U, fp32
+    T zut[StateRing<T, D>::UT_E];  // zeros: wave 1's stand-in for U~ (wave 0 starts its partial from U~)
+    float gcs[StateRing<T, D>::SLOTS];  // e^{g_C} of the chunks in the ring slots
+    uint32_t sink[64];                  // destination of the L2 prefetch loads (never read)
+};
 
-// s_waitcnt immediate for "at most n vector memory operations outstanding"
-// (gfx9 encoding; the LDS and export counters are left unconstrained).
-constexpr unsigned vmcnt_imm(unsigned n) { return (n & 0xFu) | ((n >> 4) << 14) | (0x7u << 4) | (0xFu << 8); }
+constexpr int kStateThreads = 5 * 64;  // 2 compute waves, 2 copy waves, 1 L2 prefetch wave
+constexpr int kL2Ahead = 8;            // chunks the L2 prefetch wave runs ahead
 
 // Workgroup placement: launched as a 1-D grid whose size is a multiple of 8.
 // Consecutive workgroup ids go to different XCDs (round robin), so id L is
@@ -559,30 +591,30 @@ __device__ __forceinline__ void touch_record(const T *rec, int vb, int lane, uin
     }
 }
 
-// One workgroup owns a block of 16 value channels of one head.
-//   Compute wave w (0..3): U for tokens 16w..16w+15 (K = all key channels),
-//   then the key-channel rows w*D/4.. of S^T (K = all tokens).  S^T and U are
-//   exchanged through LDS once per chunk each (two barriers per chunk).  The
-//   compute waves touch no global memory inside the chunk loop.
-//   Copy waves (4, 5): keep the LDS ring two chunks ahead with direct-to-LDS
-//   copies (each wave half of every slot; one issuing wave alone cannot
-//   keep up), and each waits for its half of the next chunk before the
-//   second barrier of the current one.
-//   Wave 6: touches the records kL2Ahead chunks ahead so that the copies hit
-//   L2, and stores each chunk's entry state (read back from the S^T exchange
-//   buffer) for the output kernel.
-//   Waves 4-6 use bare barriers, so their memory operations are never waited
-//   for by the compute waves' fences.  Every wave passes 1 + 2 * chunks
-//   barriers.
+// One workgroup owns a block of 16 value channels of one head, and walks the
+// chunks [c_begin, c_end) with one barrier per chunk.
+//   Compute waves 0, 1: wave w keeps the key-channel half w of S^T (fp32, in
+//   registers).  Per chunk it forms the partial U_w = -W[:, half w] S^T[half w]
+//   for all 64 tokens, exchanges it with the other wave through LDS (double
+//   buffered by chunk parity), adds U~, and updates its own half,
+//   S^T <- e^{g_C} S^T + (D K)^T[half w] U.  It also stores its half of the
+//   chunk-entry state for the output kernel.  No S^T exchange is needed.
+//   Copy waves 2, 3: keep the LDS ring AHEAD chunks ahead with direct-to-LDS
+//   copies (half of every slot each); chunk c+1's slot is complete before the
+//   barrier of chunk c.
+//   Wave 4: touches the records kL2Ahead chunks ahead so that the copies hit
+//   L2.
+//   Every wave passes 1 + chunks barriers.
 template <class T, int D>
 __global__ __launch_bounds__(kStateThreads) void gdn_state_kernel(StateArgs a) {
     typedef Mfma<T> M;
     typedef typename M::frag frag;
     typedef StateRing<T, D> RG;
     constexpr int KPL = M::KPL;
-    constexpr int KBD = D / (4 * KPL);
-    constexpr int KBC = 16 / KPL;
-    constexpr int MT = D / 64;
+    constexpr int KBD = D / (4 * KPL);  // fragments over K = D (key channels)
+    constexpr int KBH = KBD / 2;        // ... over one half
+    constexpr int KBC = 16 / KPL;       // fragments over K = 64 (tokens)
+    constexpr int MH = D / 32;          // 16-row tiles of S^T per half
     constexpr int NV = D / 16;
     typedef StateSmem<T, D> SM;
     __shared__ SM sm;
@@ -598,29 +630,23 @@ __global__ __launch_bounds__(kStateThreads) void gdn_state_kernel(StateArgs a) {
     const T *rec0 = static_cast<const T *>(a.rec) + bh * a.NC * (size_t)Rec<D>::SIZE;
     const int n_ch = a.c_end - a.c_begin;
 
-    if (w == 6) {
-        // ---- L2 prefetch and entry-state export
+    if (w == 4) {
+        // ---- L2 prefetch
         for (int c = a.c_begin; c < min(a.c_begin + kL2Ahead, a.c_end); ++c)
             touch_record<T, D>(rec0 + (size_t)c * Rec<D>::SIZE, vb, lane, sm.sink);
-        __builtin_amdgcn_s_barrier();  // barrier 0
-        const T *sx = sm.Sx + lane * SM::LDS_S;
+        bare_barrier();  // barrier 0
         for (int c = a.c_begin; c < a.c_end; ++c) {
-            __builtin_amdgcn_s_barrier();  // barrier 1: S^T of chunk c published
             if (c + kL2Ahead < a.c_end)
                 touch_record<T, D>(rec0 + (size_t)(c + kL2Ahead) * Rec<D>::SIZE, vb, lane, sm.sink);
-            T *scp = static_cast<T *>(a.sc) + ((bh * a.NC + c) * NV + vb) * (size_t)ScLayout<T, D>::PER_VB;
-#pragma unroll
-            for (int kb = 0; kb < KBD; ++kb)
-                *reinterpret_cast<frag *>(scp + (kb * 64 + lane) * KPL) =
-                    *reinterpret_cast<const frag *>(sx + kb * KPL);
-            __builtin_amdgcn_s_barrier();  // barrier 2 (S^T is rewritten after it)
+            bare_barrier();  // barrier of chunk c
         }
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         return;
     }
-    if (w == 4 || w == 5) {
-        // ---- copy waves: wave 4 copies units [0, H4) of each slot, wave 5 the rest and e^{g_C}
-        constexpr int H4 = RG::NDMA / 2;
+    if (w == 2 || w == 3) {
+        // ---- copy waves: wave 2 copies units [0, H2) of each slot, wave 3 the rest and e^{g_C}
+        constexpr int H2 = RG::NDMA / 2;
+        constexpr int N2 = H2, N3 = RG::NDMA - H2 + 1;  // copy instructions per chunk
         auto copy_range = [&](const char *rec, char *slot, auto i0c, auto i1c) {
             constexpr int I0 = decltype(i0c)::value, I1 = decltype(i1c)::value;
 #pragma unroll
@@ -639,102 +665,153 @@ __global__ __launch_bounds__(kStateThreads) void gdn_state_kernel(StateArgs a) {
         };
         auto copy_chunk = [&](int c) {
             const char *rec = reinterpret_cast<const char *>(rec0 + (size_t)c * Rec<D>::SIZE);
-            char *slot = reinterpret_cast<char *>(ring + ((c - a.c_begin) % RG::SLOTS) * RG::SLOT_E);
-            if (w == 4) {
-                copy_range(rec, slot, std::integral_constant<int, 0>(), std::integral_constant<int, H4>());
+            const int sl = (c - a.c_begin) % RG::SLOTS;
+            char *slot = reinterpret_cast<char *>(ring + sl * RG::SLOT_E);
+            if (w == 2) {
+                copy_range(rec, slot, std::integral_constant<int, 0>(), std::integral_constant<int, H2>());
             } else {
-                copy_range(rec, slot, std::integral_constant<int, H4>(), std::integral_constant<int, RG::NDMA>());
-                if (lane == 0)
-                    __builtin_amdgcn_global_load_lds(a.gC + bh * a.NC + c, &sm.gcs[(c - a.c_begin) % RG::SLOTS], 4,
-                                                     0, 0);
+                copy_range(rec, slot, std::integral_constant<int, H2>(), std::integral_constant<int, RG::NDMA>());
+                if (lane == 0) __builtin_amdgcn_global_load_lds(a.gC + bh * a.NC + c, &sm.gcs[sl], 4, 0, 0);
             }
         };
-        // per chunk this wave issues H4 (wave 4) or NDMA - H4 + 1 (wave 5) copies
-        copy_chunk(a.c_begin);
-        if (n_ch > 1) {
-            copy_chunk(a.c_begin + 1);
-            if (w == 4)
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm(H4));
+        // leave the copies of the newest AHEAD - 1 chunks in flight
+        auto wait_older_chunks = [&]() {
+            if (w == 2)
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm((RG::AHEAD - 1) * N2));
             else
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm(RG::NDMA - H4 + 1));
-        } else {
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm((RG::AHEAD - 1) * N3));
+        };
+        for (int j = 0; j < RG::AHEAD && j < n_ch; ++j) copy_chunk(a.c_begin + j);
+        if (n_ch >= RG::AHEAD)
+            wait_older_chunks();  // chunk c_begin landed
+        else
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        }
-        __builtin_amdgcn_s_barrier();  // barrier 0: chunk c_begin is in its slot
+        bare_barrier();  // barrier 0
         for (int c = a.c_begin; c < a.c_end; ++c) {
-            __builtin_amdgcn_s_barrier();  // barrier 1: the slot of chunk c-1 is free
-            if (c + 2 < a.c_end) {
-                copy_chunk(c + 2);
-                // this wave's part of chunk c+1 lands before barrier 2
-                if (w == 4)
-                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(H4));
-                else
-                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(RG::NDMA - H4 + 1));
+            // the slot of chunk c+AHEAD-SLOTS = c-1 is free: its last reads preceded the previous barrier
+            if (c + RG::AHEAD < a.c_end) {
+                copy_chunk(c + RG::AHEAD);
+                wait_older_chunks();  // chunk c+1 landed
             } else {
                 __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
             }
-            __builtin_amdgcn_s_barrier();  // barrier 2
+            bare_barrier();  // barrier of chunk c: chunk c+1's slot is complete
         }
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         return;
     }
 
-    // ---- compute waves.  S^T slice: rows (key channels) w*D/4 + 16 mt + 4g + ii, column vcol
-    floatx4 S[MT];
+    // ---- compute waves.  S^T half w: rows (key channels) (D/2) w + 16 mt + 4g + ii, column vcol.
+    // Operands that do not depend on the exchange are read from LDS ahead of
+    // use: -W and U~ of chunk c+1 right after the barrier of chunk c (its slot
+    // is complete then), (D K)^T and e^{g_C} of chunk c at the top of chunk c.
+    floatx4 S[MH];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        if (a.S_in)
-            S[mt] = *reinterpret_cast<const floatx4 *>(a.S_in + (bh * D + vcol) * D + w * (D / 4) + 16 * mt + 4 * g);
-        else
-            S[mt] = zero4();
+    for (int mt = 0; mt < MH; ++mt)
+        S[mt] = a.S_in ? *reinterpret_cast<const floatx4 *>(a.S_in + (bh * D + vcol) * D + (D / 2) * w + 16 * mt + 4 * g)
+                       : zero4();
+    T *sc_base = static_cast<T *>(a.sc) + (bh * a.NC * NV + vb) * (size_t)ScLayout<T, D>::PER_VB;
+    frag wf[4][KBH];                   // -W fragments (token tile tt, this half's key channels)
+    typename Vec4<T>::type ut_raw[4];  // start of the partial U: U~ on wave 0, zeros on wave 1
+    auto read_next = [&](const T *slot) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int kb = 0; kb < KBH; ++kb)
+                wf[tt][kb] = *reinterpret_cast<const frag *>(slot + ((tt * KBD + w * KBH + kb) * 64 + lane) * KPL);
+        const T *utp = w == 0 ? slot + RG::WN_E + RG::DK_E : sm.zut;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+            ut_raw[tt] = *reinterpret_cast<const typename Vec4<T>::type *>(utp + (tt * 64 + lane) * 4);
+    };
+    floatx4 up[4];
+    // bf16: U~ enters the partial through the matrix unit, as I16 U~ (exact in
+    // fp32), with an identity A operand on wave 0 and zeros on wave 1 (whose
+    // U~ stand-in is zeros as well); fp32: U~ is the accumulator's start.
+    typename K16<T>::frag ident;
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ident[i] = (T)((w == 0 && n == 4 * g + i) ? 1.f : 0.f);
     }
-    T *sx = sm.Sx + lane * SM::LDS_S;
-    T *ux = sm.Ux + lane * SM::LDS_U;
-    __syncthreads();  // barrier 0
+    auto start_partial = [&]() {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            if constexpr (sizeof(T) == 2)
+                up[tt] = K16<T>::mma(ident, ut_raw[tt], zero4());
+            else
+                up[tt] = Vec4<T>::widen(ut_raw[tt]);
+        }
+    };
+    for (int i = lane + 64 * w; i < RG::UT_E; i += 128) sm.zut[i] = (T)0.f;
+    lds_barrier();  // barrier 0: chunk c_begin is in its slot, zut cleared
+    read_next(ring);
     for (int c = a.c_begin; c < a.c_end; ++c) {
-        // this chunk's operands: its slot is complete since the previous barrier
-        const T *slot = ring + ((c - a.c_begin) % RG::SLOTS) * RG::SLOT_E;
-        frag wn[KBD], dk[MT][KBC];
+        const int sl = (c - a.c_begin) % RG::SLOTS;
+        const T *slot = ring + sl * RG::SLOT_E;
+        const int par = c & 1;
+        // this chunk's (D K)^T rows of half w and e^{g_C}, used after the barrier
+        frag dkf[MH][KBC];
 #pragma unroll
-        for (int kb = 0; kb < KBD; ++kb) wn[kb] = *reinterpret_cast<const frag *>(slot + ((w * KBD + kb) * 64 + lane) * KPL);
-        floatx4 u = load4(slot + RG::WN_E + RG::DK_E + (w * 64 + lane) * 4);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MH; ++mt)
 #pragma unroll
             for (int kb = 0; kb < KBC; ++kb)
-                dk[mt][kb] = *reinterpret_cast<const frag *>(slot + RG::WN_E +
-                                                             (((w * MT + mt) * KBC + kb) * 64 + lane) * KPL);
-        const float gc = sm.gcs[(c - a.c_begin) % RG::SLOTS];
-        // publish this wave's part of S^T (elements e = 4 (w MT + mt) + ii)
+                dkf[mt][kb] = *reinterpret_cast<const frag *>(slot + RG::WN_E + (((MH * w + mt) * KBC + kb) * 64 + lane) * KPL);
+        const float gc = sm.gcs[sl];
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_sched_barrier(0);
+        // S^T half w as B fragments over its key channels (tile-chained order)
+        frag sB[KBH];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int kb = 0; kb < KBH; ++kb)
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) sx[4 * (w * MT + mt) + ii] = (T)S[mt][ii];
-        __syncthreads();  // barrier 1
-        frag sB[KBD];
+            for (int j = 0; j < KPL; ++j) {
+                const int e = kb * KPL + j;
+                fset(sB[kb], j, S[e >> 2][e & 3]);
+            }
+        // export the chunk-entry state (fragments kb = w KBH ..)
+        T *scp = sc_base + (size_t)c * NV * ScLayout<T, D>::PER_VB;
 #pragma unroll
-        for (int kb = 0; kb < KBD; ++kb) sB[kb] = *reinterpret_cast<const frag *>(sx + kb * KPL);
-        // U = U~ + WN S^T for tokens 16w..16w+15
+        for (int kb = 0; kb < KBH; ++kb)
+            *reinterpret_cast<frag *>(scp + ((w * KBH + kb) * 64 + lane) * KPL) = sB[kb];
+        // partial U over this half (plus U~ on wave 0), all 4 token tiles
+        start_partial();
 #pragma unroll
-        for (int kb = 0; kb < KBD; ++kb) u = M::mma(wn[kb], sB[kb], u);
-        // publish U (elements e = 4 w + ii)
+        for (int tt = 0; tt < 4; ++tt) {
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) ux[4 * w + ii] = (T)u[ii];
-        __syncthreads();  // barrier 2
+            for (int kb = 0; kb < KBH; ++kb) up[tt] = M::mma(wf[tt][kb], sB[kb], up[tt]);
+            *reinterpret_cast<floatx4 *>(&sm.Up[par][w][tt][lane]) = up[tt];
+        }
+        lds_barrier();  // barrier of chunk c: partials published, chunk c+1's slot complete
+        floatx4 other[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) other[tt] = *reinterpret_cast<const floatx4 *>(&sm.Up[par][1 - w][tt][lane]);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);  // keep the exchange reads ahead of the prefetch below
+        // (after the last chunk this reads a stale slot; the values are not used)
+        read_next(ring + ((c + 1 - a.c_begin) % RG::SLOTS) * RG::SLOT_E);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);  // the reads stay in this iteration
+        floatx4 u[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) u[tt] = up[tt] + other[tt];
+#pragma unroll
+        for (int mt = 0; mt < MH; ++mt) S[mt] *= gc;
+        // U as B fragments over the tokens
         frag uB[KBC];
 #pragma unroll
-        for (int kb = 0; kb < KBC; ++kb) uB[kb] = *reinterpret_cast<const frag *>(ux + kb * KPL);
+        for (int kb = 0; kb < KBC; ++kb)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            S[mt] *= gc;
+            for (int j = 0; j < KPL; ++j) {
+                const int e = kb * KPL + j;
+                fset(uB[kb], j, u[e >> 2][e & 3]);
+            }
+        // S^T half w <- e^{g_C} S^T + (D K)^T[half w] U
 #pragma unroll
-            for (int kb = 0; kb < KBC; ++kb) S[mt] = M::mma(dk[mt][kb], uB[kb], S[mt]);
-        }
+        for (int kb = 0; kb < KBC; ++kb)
+#pragma unroll
+            for (int mt = 0; mt < MH; ++mt) S[mt] = M::mma(dkf[mt][kb], uB[kb], S[mt]);
     }
     if (a.S_out) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-            *reinterpret_cast<floatx4 *>(a.S_out + (bh * D + vcol) * D + w * (D / 4) + 16 * mt + 4 * g) = S[mt];
+        for (int mt = 0; mt < MH; ++mt)
+            *reinterpret_cast<floatx4 *>(a.S_out + (bh * D + vcol) * D + (D / 2) * w + 16 * mt + 4 * g) = S[mt];
     }
 }
 
