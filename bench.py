@@ -44,22 +44,38 @@ def log(msg):
 # the chunk-entry state (8 value blocks x 4 KB per 64 tokens = 512 B); out
 # reads Q', O0 (512 B), the entry state (512 B) and the gate (256 B) and
 # writes y (256 B).
-KERNEL_BYTES_PER_TOKEN_HEAD = {
-    "gdn_prep_kernel": 768 + 8 + 1280,
-    "gdn_state_kernel": 768 + 512,
-    "gdn_out_kernel": 512 + 512 + 256 + 256,
-}
-LAYER_BYTES_PER_TOKEN_HEAD = 4 * 128 * 2 + 128 * 2 + 8
+def kernel_bytes_per_token_head(D: int, es: int) -> dict:
+    """Algorithmic HBM bytes per token-head of each kernel's own contract
+    (es = bytes per I/O element; states and gates are fp32):
+      prep : q, k, v in (3 D es), log a and b in (8), the chunk record out
+             (-W, Q', (D K)^T, U~, O0: 5 D es per token);
+      state: -W, (D K)^T, U~ in (3 D es), the chunk-entry state out
+             (D x D per 64 tokens: D^2 es / 64);
+      out  : Q', O0 in (2 D es), chunk-entry state in (D^2 es / 64),
+             gate in and y out (2 D es)."""
+    return {
+        "gdn_prep_kernel": 3 * D * es + 8 + 5 * D * es,
+        "gdn_state_kernel": 3 * D * es + D * D * es // 64,
+        "gdn_out_kernel": 2 * D * es + D * D * es // 64 + 2 * D * es,
+    }
+
+
+def layer_bytes_per_token_head(D: int, es: int) -> int:
+    """The layer's own floor: q, k, v, gate in and y out, log a and b in."""
+    return 5 * D * es + 8
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "linear_attention_token_fwd_amd", "csrc")
 
 
+KERNEL_SOURCES = ("frag.hpp", "kernels.hpp")
+
+
 def csrc_hash() -> str:
-    """sha256 over the HIP sources, to tell whether a stored profile still
-    describes the kernels being run."""
+    """sha256 over the kernel sources (device code only), to tell whether a
+    stored profile still describes the kernels being run."""
     import hashlib
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in KERNEL_SOURCES:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
@@ -218,14 +234,15 @@ def main() -> int:
         for nm, v in tot.items():
             per_call.setdefault(nm, []).append(v)
     launches_per_call = {nm: names.count(nm) for nm in set(names)}
+    es = 2 if w.dtype == "bf16" else 4
     kernels = {}
     token_heads = B * T * H * (2 if w.bidirectional else 1)
     for nm in per_launch:
         per_launch_ms = float(np.mean(per_launch[nm]))
         call_ms = float(np.mean(per_call[nm]))
-        bytes_per_call = KERNEL_BYTES_PER_TOKEN_HEAD[nm] * token_heads
+        bytes_per_call = kernel_bytes_per_token_head(D, es)[nm] * token_heads
         if nm == "gdn_out_kernel" and w.bidirectional:  # + fp32 accumulator write and read
-            bytes_per_call += 2 * 512 * B * T * H
+            bytes_per_call += 2 * 4 * D * B * T * H
         kernels[nm] = {"launches_per_call": launches_per_call[nm], "avg_ms": per_launch_ms,
                        "ms_per_call": call_ms, "bytes_per_launch": bytes_per_call / launches_per_call[nm],
                        "GBps": bytes_per_call / (call_ms * 1e-3) / 1e9}
@@ -233,12 +250,13 @@ def main() -> int:
     kd = kernels[dom]
     tag = f"T{T}_H{H}_d{D}_{w.dtype}" + ("_bidir" if w.bidirectional else "")
     traffic = profiled_traffic(dom, tag)
-    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(kd["GBps"], 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(kd["GBps"] / HBM_PEAK_GBS, 4),
+    achieved = kd["bytes_per_launch"] / (kd["avg_ms"] * 1e-3) / 1e9  # algorithmic bytes per launch / avg launch
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": None if traffic is None else round(traffic),
                 "avg_launch_ms": round(kd["avg_ms"], 5)}
     call_ms = ms_per_step
-    layer_bytes = LAYER_BYTES_PER_TOKEN_HEAD * token_heads * (2 if w.bidirectional else 1)
+    layer_bytes = layer_bytes_per_token_head(D, es) * B * T * H
     layer = {"algorithmic_bytes": layer_bytes, "floor_ms": layer_bytes / (HBM_PEAK_GBS * 1e9) * 1e3,
              "frac_of_hbm_roofline": round(layer_bytes / (HBM_PEAK_GBS * 1e9) * 1e3 / ms_per_step, 4)}
     for nm, k in kernels.items():

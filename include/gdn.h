@@ -38,10 +38,13 @@
  * (or gdn_fwd_bidir_workspace_bytes()) bytes, 256-byte aligned, which the
  * call may overwrite entirely.
  *
- * Execution.  Calls enqueue kernels on `stream` (NULL = the null stream) and
- * return without waiting.  They keep no global state, so calls on different
- * buffers may run concurrently; two in-flight calls must not share a
- * workspace.
+ * Execution.  A call is ordered on `stream` (NULL = the null stream) like a
+ * single operation and returns without waiting: its kernels run on `stream`
+ * and on up to three library streams per device (created on first use and
+ * kept, default priority), which wait for `stream` at the start of the call
+ * and which `stream` waits for at its end.  Calls from several host threads
+ * are enqueued one at a time (a lock); their work may then share the library
+ * streams.  Two in-flight calls must not share a workspace.
  *
  * Errors.  All checks run on the host before anything is enqueued; on any
  * error nothing is launched and no output is touched.  Launch failures
@@ -121,17 +124,19 @@ gdn_status gdn_fwd_bidir(const gdn_fwd_params *p, float *S_T_rev,
                          struct ihipStream_t *stream);
 
 /*
- * Measurement aids.  A call is a fixed short sequence of kernel launches on
- * one stream; gdn_fwd_launch_count() says how many (bidirectional != 0 for
+ * Measurement aids.  A call is a fixed sequence of kernel launches (a range
+ * of chunks per launch, spread over the streams above);
+ * gdn_fwd_launch_count() says how many (bidirectional != 0 for
  * gdn_fwd_bidir), or -1 for invalid or unsupported sizes, and
  * gdn_fwd_launch_name() names launch i (static string, NULL if out of range).
  * gdn_fwd_timed() does exactly what gdn_fwd (bidirectional == 0) or
  * gdn_fwd_bidir (bidirectional != 0; S_T_rev as there) does, and in addition
- * records events[i] on the stream right before launch i and events[count]
- * after the last one, so each kernel's duration is the elapsed time between
- * consecutive events.  events: n_events >= count + 1 caller-created HIP
- * events (hipEvent_t is `struct ihipEvent_t *`); otherwise
- * GDN_ERR_INVALID_ARG and nothing is launched.
+ * records events[2i] right before launch i and events[2i+1] right after it,
+ * on the stream that launch runs on, so launch i's duration is the elapsed
+ * time between those two events.  events: n_events >= 2 * count
+ * caller-created HIP events with timing enabled (hipEvent_t is
+ * `struct ihipEvent_t *`); otherwise GDN_ERR_INVALID_ARG and nothing is
+ * launched.
  */
 struct ihipEvent_t;
 int gdn_fwd_launch_count(const gdn_fwd_params *p, int bidirectional);

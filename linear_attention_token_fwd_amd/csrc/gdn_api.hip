@@ -118,13 +118,14 @@ gdn_status validate(const gdn_fwd_params *p, const float *S_T_rev, int scans) {
     return GDN_OK;
 }
 
-// A call is a fixed plan of kernel launches spread over up to five streams:
-// stream 0 is the caller's, streams 1-4 belong to the library (one set per
-// device, created on first use, default priority).  Events order the streams:
+// A call is a fixed plan of kernel launches spread over up to four streams:
+// stream 0 is the caller's, streams 1-3 belong to the library (one set per
+// device, created on first use, default priority).  (A process gets four
+// hardware queues by default, so more streams would only share them.)  Events order the streams:
 // every library stream first waits for the caller's stream at the start of
 // the call, and the caller's stream finally waits for every library stream,
 // so the call behaves as one stream-ordered operation on the caller's stream.
-constexpr int kStreams = 5;
+constexpr int kStreams = 4;
 
 struct Launch {
     const void *fn;
@@ -320,13 +321,13 @@ gdn_status plan_fwd(Plan &plan, const gdn_fwd_params *p, float *S_T_rev, bool bi
     if (!bidir) {
         plan_scan<T, D>(plan, p, p->reverse, scan_bufs(p, L, 0), p->S_T, 1, 0, 2, 0, nullptr);
     } else {
-        // the two directions are independent: forward chain on stream 0 fed by
-        // preps on stream 1, reversed chain on stream 3 fed by preps on
-        // stream 4; the outputs run on stream 2, the reversed scan's after
-        // all of the forward scan's (they add into its fp32 sum)
+        // the two directions are independent: forward chain on stream 0,
+        // reversed chain on stream 3, all preps on stream 1; the outputs run
+        // on stream 2, the reversed scan's after all of the forward scan's
+        // (they add into its fp32 sum)
         float *acc = reinterpret_cast<float *>(static_cast<char *>(p->workspace) + L.acc);
         plan_scan<T, D>(plan, p, 0, scan_bufs(p, L, 0), p->S_T, 1, 0, 2, 1, acc);
-        plan_scan<T, D>(plan, p, 1, scan_bufs(p, L, 1), S_T_rev, 4, 3, 2, 2, acc);
+        plan_scan<T, D>(plan, p, 1, scan_bufs(p, L, 1), S_T_rev, 1, 3, 2, 2, acc);
     }
     for (int s = 1; s < kStreams; ++s) plan.wait(0, plan.record(s));
     return GDN_OK;

@@ -543,11 +543,9 @@ template <class T, int D> struct StateSmem {
     floatx4 Up[2][2][4][64];  // [chunk parity][wave][token tile][lane] partial U, fp32
     T zut[StateRing<T, D>::UT_E];  // zeros: wave 1's stand-in for U~ (wave 0 starts its partial from U~)
     float gcs[StateRing<T, D>::SLOTS];  // e^{g_C} of the chunks in the ring slots
-    uint32_t sink[64];                  // destination of the L2 prefetch loads (never read)
 };
 
-constexpr int kStateThreads = 5 * 64;  // 2 compute waves, 2 copy waves, 1 L2 prefetch wave
-constexpr int kL2Ahead = 8;            // chunks the L2 prefetch wave runs ahead
+constexpr int kStateThreads = 4 * 64;  // 2 compute waves, 2 copy waves
 
 // Workgroup placement: launched as a 1-D grid whose size is a multiple of 8.
 // Consecutive workgroup ids go to different XCDs (round robin), so id L is
@@ -558,37 +556,6 @@ __device__ __forceinline__ bool xcd_position(int L, int nwg_used, int nwg_launch
     const int per = nwg_launched / 8;
     p = (L % 8) * per + L / 8;
     return p < nwg_used;
-}
-
-// L2 prefetch: touch one 128-byte line per lane of the part of chunk record
-// `rec` this workgroup will copy: the head-wide -W and (D K)^T regions are
-// split over the head's NV workgroups (they share the XCD's L2), and each
-// workgroup touches its own U~ block.  The loads land in a scratch LDS word
-// that is never read.
-template <class T, int D>
-__device__ __forceinline__ void touch_record(const T *rec, int vb, int lane, uint32_t *sink) {
-    constexpr int NV = D / 16;
-    constexpr int line = 128;
-    constexpr int region_lines = 64 * D * (int)sizeof(T) / line;  // one 64 x D matrix
-    constexpr int per_wg = 2 * region_lines / NV;
-    constexpr int own_lines = 4 * 64 * 4 * (int)sizeof(T) / line;
-    constexpr int n_touch = per_wg + own_lines;
-    const char *base = reinterpret_cast<const char *>(rec);
-#pragma unroll
-    for (int k0 = 0; k0 < n_touch; k0 += 64) {
-        const int k = k0 + lane;
-        if (k < n_touch) {
-            size_t off;
-            if (k < per_wg) {
-                const int l = vb + NV * k;  // line among -W, then (D K)^T
-                off = l < region_lines ? (size_t)Rec<D>::WN * sizeof(T) + (size_t)l * line
-                                       : (size_t)Rec<D>::DKT * sizeof(T) + (size_t)(l - region_lines) * line;
-            } else {
-                off = (size_t)(Rec<D>::UT + vb * 4 * 64 * 4) * sizeof(T) + (size_t)(k - per_wg) * line;
-            }
-            __builtin_amdgcn_global_load_lds(base + off, sink, 4, 0, 0);
-        }
-    }
 }
 
 // One workgroup owns a block of 16 value channels of one head, and walks the
@@ -602,8 +569,6 @@ __device__ __forceinline__ void touch_record(const T *rec, int vb, int lane, uin
 //   Copy waves 2, 3: keep the LDS ring AHEAD chunks ahead with direct-to-LDS
 //   copies (half of every slot each); chunk c+1's slot is complete before the
 //   barrier of chunk c.
-//   Wave 4: touches the records kL2Ahead chunks ahead so that the copies hit
-//   L2.
 //   Every wave passes 1 + chunks barriers.
 template <class T, int D>
 __global__ __launch_bounds__(kStateThreads) void gdn_state_kernel(StateArgs a) {
@@ -630,19 +595,6 @@ __global__ __launch_bounds__(kStateThreads) void gdn_state_kernel(StateArgs a) {
     const T *rec0 = static_cast<const T *>(a.rec) + bh * a.NC * (size_t)Rec<D>::SIZE;
     const int n_ch = a.c_end - a.c_begin;
 
-    if (w == 4) {
-        // ---- L2 prefetch
-        for (int c = a.c_begin; c < min(a.c_begin + kL2Ahead, a.c_end); ++c)
-            touch_record<T, D>(rec0 + (size_t)c * Rec<D>::SIZE, vb, lane, sm.sink);
-        bare_barrier();  // barrier 0
-        for (int c = a.c_begin; c < a.c_end; ++c) {
-            if (c + kL2Ahead < a.c_end)
-                touch_record<T, D>(rec0 + (size_t)(c + kL2Ahead) * Rec<D>::SIZE, vb, lane, sm.sink);
-            bare_barrier();  // barrier of chunk c
-        }
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        return;
-    }
     if (w == 2 || w == 3) {
         // ---- copy waves: wave 2 copies units [0, H2) of each slot, wave 3 the rest and e^{g_C}
         constexpr int H2 = RG::NDMA / 2;
