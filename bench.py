@@ -256,7 +256,9 @@ def main() -> int:
                 "traffic": None if traffic is None else round(traffic),
                 "avg_launch_ms": round(kd["avg_ms"], 5)}
     call_ms = ms_per_step
-    layer_bytes = layer_bytes_per_token_head(D, es) * B * T * H
+    # bidirectional: two whole passes, plus the second pass reading the first one's output
+    lb = 2 * layer_bytes_per_token_head(D, es) + D * es if w.bidirectional else layer_bytes_per_token_head(D, es)
+    layer_bytes = lb * B * T * H
     layer = {"algorithmic_bytes": layer_bytes, "floor_ms": layer_bytes / (HBM_PEAK_GBS * 1e9) * 1e3,
              "frac_of_hbm_roofline": round(layer_bytes / (HBM_PEAK_GBS * 1e9) * 1e3 / ms_per_step, 4)}
     for nm, k in kernels.items():
