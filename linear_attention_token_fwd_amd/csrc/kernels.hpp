@@ -807,6 +807,23 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_out_kernel(OutArgs a) {
     floatx4 o[NV];
 #pragma unroll
     for (int vb = 0; vb < NV; ++vb) o[vb] = load4(rec + Rec<D>::O0 + ((vb * 4 + w) * 64 + lane) * 4);
+    // the gate (and, summing the second scan, the first scan's output) of the
+    // rows this thread normalises below, loaded with the rest (rows clamped)
+    constexpr int G = D / 8;
+    constexpr int TPP = kThreads / G;
+    constexpr int PASSES = 64 / TPP;
+    const int cg = tid % G;
+    size_t roff[PASSES];
+    float gv[PASSES][8], prev[PASSES][8];
+#pragma unroll
+    for (int pass = 0; pass < PASSES; ++pass) {
+        const int s = c * 64 + pass * TPP + tid / G;
+        const int sc_ = s < a.T ? s : a.T - 1;
+        const int t = a.reverse ? a.T - 1 - sc_ : sc_;
+        roff[pass] = (((size_t)b * a.T + t) * a.H + h) * D + 8 * cg;
+        load8(static_cast<const T *>(a.gate) + roff[pass], gv[pass]);
+        if (a.mode == 2) load8(a.acc + roff[pass], prev[pass]);
+    }
     __syncthreads();
     // O = O0 + Q' S^T for tokens 16w.., all value channels
 #pragma unroll
@@ -821,18 +838,14 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_out_kernel(OutArgs a) {
     __syncthreads();
 
     // gated RMS normalisation: G threads per token row, 8 channels each
-    constexpr int G = D / 8;
-    constexpr int TPP = kThreads / G;
-    const int cg = tid % G;
     float wv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) wv[i] = a.norm_w ? a.norm_w[h * D + 8 * cg + i] : 1.f;
 #pragma unroll
-    for (int pass = 0; pass < 64 / TPP; ++pass) {
+    for (int pass = 0; pass < PASSES; ++pass) {
         const int r = pass * TPP + tid / G;
         const int s = c * 64 + r;
         const bool live = s < a.T;
-        const int t = a.reverse ? a.T - 1 - (live ? s : a.T - 1) : (live ? s : a.T - 1);
         const float *orow = sm.Os + r * SM::LDO + 8 * cg;
         float ov[8];
 #pragma unroll
@@ -844,19 +857,16 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_out_kernel(OutArgs a) {
         for (int m = 1; m < G; m <<= 1) ss += __shfl_xor(ss, m, 64);
         const float inv = 1.0f / sqrtf(ss / D + a.eps);
         if (!live) continue;
-        const size_t off = (((size_t)b * a.T + t) * a.H + h) * D + 8 * cg;
-        float gv[8], y[8];
-        load8(static_cast<const T *>(a.gate) + off, gv);
+        const size_t off = roff[pass];
+        float y[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) y[i] = ov[i] * inv * wv[i] * silu(gv[i]);
+        for (int i = 0; i < 8; ++i) y[i] = ov[i] * inv * wv[i] * silu(gv[pass][i]);
         if (a.mode == 1) {
             store8(a.acc + off, y);
         } else {
             if (a.mode == 2) {
-                float prev[8];
-                load8(a.acc + off, prev);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) y[i] += prev[i];
+                for (int i = 0; i < 8; ++i) y[i] += prev[pass][i];
             }
             store8(static_cast<T *>(a.out) + off, y);
         }
