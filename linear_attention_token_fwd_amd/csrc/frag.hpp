@@ -66,7 +66,11 @@ template <class OT> __device__ __forceinline__ OT to_ot(float x) { return (OT)x;
 __device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f(float x) { return x; }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// SiLU with the hardware reciprocal (about 1 ulp) in place of an IEEE divide:
+// z / (1 + e^-z) is z * rcp(1 + e^-z); for large -z, e^-z = inf gives -0.
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+// 1 / sqrt(x) with the hardware reciprocal square root (about 1 ulp)
+__device__ __forceinline__ float rsqrt_fast(float x) { return __builtin_amdgcn_rsqf(x); }
 
 __device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
 

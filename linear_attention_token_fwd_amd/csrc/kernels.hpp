@@ -208,6 +208,60 @@ template <class T, int D> struct PrepSmem {
     __device__ T *P() { return reinterpret_cast<T *>(Am); }
 };
 
+// Short conv + SiLU (+ L2 normalisation for q and k) of one thread's RUN
+// tokens x 8 channels from its raw rows; MASK: positions outside [0, T) are
+// zero history and tokens past T produce zeros.
+template <class T, int D, bool MASK>
+__device__ __forceinline__ void conv_silu_norm(const PrepArgs &a, const Raw8<T> (&raw)[3][64 / (kThreads / (D / 8)) + 3],
+                                               const bool (&rv)[64 / (kThreads / (D / 8)) + 3],
+                                               const float *const (&wsrc)[3], T *const (&dst)[3], int h, int s0,
+                                               int cg, int run) {
+    constexpr int G = D / 8;
+    constexpr int RUN = 64 / (kThreads / G);
+    constexpr int ROWS = RUN + 3;
+    constexpr int LDX = PrepSmem<T, D>::LDX;
+#pragma unroll
+    for (int x = 0; x < 3; ++x) {
+        float wt[8][4];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float4 wv = reinterpret_cast<const float4 *>(wsrc[x])[(size_t)h * D + 8 * cg + i];
+            wt[i][0] = wv.x; wt[i][1] = wv.y; wt[i][2] = wv.z; wt[i][3] = wv.w;
+        }
+        // the rows widened once, positions outside [0, T) as zeros (the conv's zero history)
+        float xr[ROWS][8];
+#pragma unroll
+        for (int rr = 0; rr < ROWS; ++rr)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) xr[rr][i] = (!MASK || rv[rr]) ? raw[x][rr].get(i) : 0.f;
+#pragma unroll
+        for (int r = 0; r < RUN; ++r) {
+            const bool valid = !MASK || s0 + r < a.T;
+            float acc[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float s = wt[i][0] * xr[r][i];
+#pragma unroll
+                for (int j = 1; j < 4; ++j) s = fmaf(wt[i][j], xr[r + j][i], s);
+                acc[i] = valid ? silu(s) : 0.f;
+            }
+            if (x < 2) {
+                float ss = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ss += acc[i] * acc[i];
+#pragma unroll
+                for (int m = 1; m < G; m <<= 1) ss += __shfl_xor(ss, m, 64);
+                const float inv = valid ? rsqrt_fast(ss + a.eps_l2) : 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] *= inv;
+            }
+            T *row = dst[x] + (run * RUN + r) * LDX + 8 * cg;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) row[i] = (T)acc[i];
+        }
+    }
+}
+
 // Short conv + SiLU (+ L2 normalisation for q and k) of the chunk's 64 scan
 // positions into LDS.  Thread layout: G = D/8 threads per token row (8
 // channels each); each thread owns RUN consecutive tokens and loads its
@@ -218,7 +272,6 @@ __device__ __forceinline__ void prologue(const PrepArgs &a, PrepSmem<T, D> &sm, 
     constexpr int G = D / 8;
     constexpr int RUN = 64 / (kThreads / G);
     constexpr int ROWS = RUN + 3;
-    constexpr int LDX = PrepSmem<T, D>::LDX;
     const int tid = threadIdx.x, cg = tid % G, run = tid / G;
     const int s0 = c * 64 + run * RUN;
     const T *src[3] = {static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v)};
@@ -236,40 +289,11 @@ __device__ __forceinline__ void prologue(const PrepArgs &a, PrepSmem<T, D> &sm, 
 #pragma unroll
         for (int x = 0; x < 3; ++x) raw[x][rr].load(src[x] + off);
     }
-#pragma unroll
-    for (int x = 0; x < 3; ++x) {
-        float wt[8][4];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float4 wv = reinterpret_cast<const float4 *>(wsrc[x])[(size_t)h * D + 8 * cg + i];
-            wt[i][0] = wv.x; wt[i][1] = wv.y; wt[i][2] = wv.z; wt[i][3] = wv.w;
-        }
-#pragma unroll
-        for (int r = 0; r < RUN; ++r) {
-            const bool valid = s0 + r < a.T;
-            float acc[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                float s = 0.f;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) s += rv[r + j] ? wt[i][j] * raw[x][r + j].get(i) : 0.f;
-                acc[i] = valid ? silu(s) : 0.f;
-            }
-            if (x < 2) {
-                float ss = 0.f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) ss += acc[i] * acc[i];
-#pragma unroll
-                for (int m = 1; m < G; m <<= 1) ss += __shfl_xor(ss, m, 64);
-                const float inv = valid ? 1.0f / sqrtf(ss + a.eps_l2) : 0.f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i] *= inv;
-            }
-            T *row = dst[x] + (run * RUN + r) * LDX + 8 * cg;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) row[i] = (T)acc[i];
-        }
-    }
+    // chunks away from both ends of the sequence need no masking
+    if (c > 0 && (c + 1) * 64 <= a.T)
+        conv_silu_norm<T, D, false>(a, raw, rv, wsrc, dst, h, s0, cg, run);
+    else
+        conv_silu_norm<T, D, true>(a, raw, rv, wsrc, dst, h, s0, cg, run);
 }
 
 template <class T, int D>
@@ -855,7 +879,7 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_out_kernel(OutArgs a) {
         for (int i = 0; i < 8; ++i) ss += ov[i] * ov[i];
 #pragma unroll
         for (int m = 1; m < G; m <<= 1) ss += __shfl_xor(ss, m, 64);
-        const float inv = 1.0f / sqrtf(ss / D + a.eps);
+        const float inv = rsqrt_fast(ss * (1.0f / D) + a.eps);
         if (!live) continue;
         const size_t off = roff[pass];
         float y[8];
