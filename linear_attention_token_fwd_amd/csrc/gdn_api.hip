@@ -212,17 +212,23 @@ gdn_status run_plan(const Plan &plan, hipStream_t caller, hipEvent_t *timing) {
     return GDN_OK;
 }
 
-// Chunk ranges of a scan: ~64 chunks each, at most 16.
+// Chunk ranges of a scan: ~64 chunks each, at most 16 ranges unless a range
+// would exceed the state kernel's limit.
 int n_ranges(int NC) {
     int R = (NC + 63) / 64;
-    return R < 1 ? 1 : (R > 16 ? 16 : R);
+    R = R < 1 ? 1 : (R > 16 ? 16 : R);
+    const int need = (NC + gdn::kStateMaxRange - 1) / gdn::kStateMaxRange;
+    return R < need ? need : R;
 }
 int range_begin(int NC, int R, int i) { return (int)((long long)NC * i / R); }
 
-// Dynamic LDS of the state kernel: its operand ring, and at least 96 KB so
-// that no prep workgroup (up to 75 KB of LDS) shares its CU.
+// Dynamic LDS of the state kernel: none.  Its ~20 KB of static LDS lets a
+// prep or output workgroup share its CU, so a range's state launch starts
+// without waiting for CUs to drain (measured faster overall than keeping the
+// chain alone on its CUs).
+constexpr size_t kStateReserveLds = 0;
 template <class T, int D> constexpr size_t state_lds() {
-    return gdn::StateRing<T, D>::BYTES > 96 * 1024 ? gdn::StateRing<T, D>::BYTES : 96 * 1024;
+    return kStateReserveLds;
 }
 
 struct ScanBufs {
@@ -301,7 +307,7 @@ void plan_scan(Plan &plan, const gdn_fwd_params *p, int reverse, const ScanBufs 
         const float *S_in = i == 0 ? p->S0 : sb.smid[(i - 1) & 1];
         float *S_out = i == R - 1 ? S_T : sb.smid[i & 1];
         plan.wait(state_stream, prep_done[i]);
-        plan.launch(state_stream, "gdn_state_kernel", state, dim3((used + 7) / 8 * 8), dim3(gdn::kStateThreads),
+        plan.launch(state_stream, "gdn_state_kernel", state, dim3((used + 7) / 8 * 8), dim3(gdn::StateCfg<T, D>::THREADS),
                     state_lds<T, D>(), state_args<T, D>(p, sb, c0, c1, S_in, S_out));
         state_done[i] = plan.record(state_stream);
     }

@@ -542,35 +542,6 @@ __device__ __forceinline__ void lds_barrier() {
     bare_barrier();
 }
 
-// Ring of chunk operands in LDS (dynamic shared memory): each slot holds the
-// record's -W and (D K)^T (head-wide) and the workgroup's own U~ block,
-// copied verbatim so fragments keep the record's layout.  Every read of chunk
-// c's slot lies between the barriers of chunks c-1 and c, so after the
-// barrier of chunk c-1 the copy of chunk c+AHEAD may go into chunk c-1's
-// slot: the ring has AHEAD + 1 slots, four (copies run three chunks ahead)
-// where they fit in LDS, else three.
-template <class T, int D> struct StateRing {
-    static constexpr int WN_E = 64 * D;          // elements
-    static constexpr int DK_E = 64 * D;
-    static constexpr int UT_E = 4 * 64 * 4;      // one value block of U~
-    static constexpr int SLOT_E = WN_E + DK_E + UT_E;
-    static constexpr int SLOT_BYTES = SLOT_E * (int)sizeof(T);
-    static constexpr int N16 = SLOT_BYTES / 16;  // 16-byte units per slot
-    static constexpr int NDMA = N16 / 64;        // copy instructions per chunk (64 lanes x 16 B)
-    static constexpr int SLOTS = 4 * SLOT_BYTES <= 140 * 1024 ? 4 : 3;
-    static constexpr int AHEAD = SLOTS - 1;
-    static constexpr int BYTES = SLOTS * SLOT_BYTES;
-    static_assert(N16 % 64 == 0, "slot must be a whole number of wave copies");
-};
-
-template <class T, int D> struct StateSmem {
-    floatx4 Up[2][2][4][64];  // [chunk parity][wave][token tile][lane] partial U, fp32
-    T zut[StateRing<T, D>::UT_E];  // zeros: wave 1's stand-in for U~ (wave 0 starts its partial from U~)
-    float gcs[StateRing<T, D>::SLOTS];  // e^{g_C} of the chunks in the ring slots
-};
-
-constexpr int kStateThreads = 4 * 64;  // 2 compute waves, 2 copy waves
-
 // Workgroup placement: launched as a 1-D grid whose size is a multiple of 8.
 // Consecutive workgroup ids go to different XCDs (round robin), so id L is
 // mapped to position p = (L % 8) * per + L / 8 of the head-major list of
@@ -582,213 +553,189 @@ __device__ __forceinline__ bool xcd_position(int L, int nwg_used, int nwg_launch
     return p < nwg_used;
 }
 
-// One workgroup owns a block of 16 value channels of one head, and walks the
-// chunks [c_begin, c_end) with one barrier per chunk.
-//   Compute waves 0, 1: wave w keeps the key-channel half w of S^T (fp32, in
-//   registers).  Per chunk it forms the partial U_w = -W[:, half w] S^T[half w]
-//   for all 64 tokens, exchanges it with the other wave through LDS (double
-//   buffered by chunk parity), adds U~, and updates its own half,
-//   S^T <- e^{g_C} S^T + (D K)^T[half w] U.  It also stores its half of the
-//   chunk-entry state for the output kernel.  No S^T exchange is needed.
-//   Copy waves 2, 3: keep the LDS ring AHEAD chunks ahead with direct-to-LDS
-//   copies (half of every slot each); chunk c+1's slot is complete before the
-//   barrier of chunk c.
-//   Every wave passes 1 + chunks barriers.
+// Shape of the state kernel.  NW compute waves split the key channels
+// (KQ = D / NW each); the per-chunk U is reduced across them through LDS.
+template <class T, int D> struct StateCfg {
+    static constexpr int KPL = Mfma<T>::KPL;
+    static constexpr int KBD = D / (4 * KPL);                    // fragments over K = D
+    static constexpr int KBC = 16 / KPL;                         // fragments over K = 64 tokens
+    static constexpr int NW = (sizeof(T) == 2 && D == 64) ? 2 : 4;
+    static constexpr int KQ = D / NW;                            // key channels per wave
+    static constexpr int KBQ = KQ / (4 * KPL);                   // fragments over a wave's key channels
+    static constexpr int MQ = KQ / 16;                           // 16-row tiles of S^T per wave
+    static constexpr int TPW = 4 / NW;                           // token tiles each wave reduces
+    static constexpr int NB = 4;                                 // chunks of operands held in registers
+    static constexpr int THREADS = 64 * NW;
+    static_assert(KBQ >= 1 && KQ % (4 * KPL) == 0 && MQ >= 1, "state kernel shape");
+};
+constexpr int kStateMaxRange = 512;  // chunks per launch (e^{g_C} of the range is staged in LDS)
+
+template <class T, int D> struct StateSmem {
+    typedef StateCfg<T, D> C;
+    floatx4 part[C::NW][4][64];  // partial U of every wave, per token tile, fp32
+    T ub[64 * 16];                 // U as B fragments over the 64 tokens, per lane
+    float gcs[kStateMaxRange];     // e^{g_C} of the range's chunks
+};
+
+// Operands of one chunk held by one compute wave: -W over its key channels
+// for the 4 token tiles, its rows of (D K)^T, and U~ of the tiles it reduces.
+template <class T, int D> struct StateOps {
+    typedef StateCfg<T, D> C;
+    typedef typename Mfma<T>::frag frag;
+    frag wf[4][C::KBQ];
+    frag dkf[C::MQ][C::KBC];
+    typename Vec4<T>::type ut[C::TPW];
+};
+
+// One workgroup owns a block of 16 value channels of one head and walks the
+// chunks [c_begin, c_end).  Compute wave w keeps S^T rows w KQ .. (w+1) KQ - 1
+// (fp32, in registers) and, per chunk:
+//   A: stores its rows of the chunk-entry state for the output kernel, and
+//      forms its partial -W[:, rows] S^T[rows] for all 4 token tiles (U~
+//      entering the partial of the tiles it reduces), publishing the other
+//      waves' tiles in LDS;                                      barrier;
+//   B: sums the partials of its token tiles into U, stored as bf16/fp32
+//      B fragments in LDS;                                       barrier;
+//   C: S^T[rows] <- e^{g_C} S^T[rows] + (D K)^T[rows] U.
+// Its operand fragments come straight from the chunk records in HBM into
+// registers, NB chunks ahead (four register sets used in turn); LDS holds
+// only the exchange.  Every wave passes 1 + 2 * chunks barriers.
 template <class T, int D>
-__global__ __launch_bounds__(kStateThreads) void gdn_state_kernel(StateArgs a) {
+__global__ __launch_bounds__((StateCfg<T, D>::THREADS)) void gdn_state_kernel(StateArgs a) {
     typedef Mfma<T> M;
     typedef typename M::frag frag;
-    typedef StateRing<T, D> RG;
-    constexpr int KPL = M::KPL;
-    constexpr int KBD = D / (4 * KPL);  // fragments over K = D (key channels)
-    constexpr int KBH = KBD / 2;        // ... over one half
-    constexpr int KBC = 16 / KPL;       // fragments over K = 64 (tokens)
-    constexpr int MH = D / 32;          // 16-row tiles of S^T per half
+    typedef StateCfg<T, D> C;
+    typedef StateOps<T, D> Ops;
+    constexpr int KPL = C::KPL, KBD = C::KBD, KBC = C::KBC, KBQ = C::KBQ, MQ = C::MQ, TPW = C::TPW;
     constexpr int NV = D / 16;
-    typedef StateSmem<T, D> SM;
-    __shared__ SM sm;
-    extern __shared__ __align__(16) unsigned char ring_raw[];
-    T *ring = reinterpret_cast<T *>(ring_raw);
+    __shared__ StateSmem<T, D> sm;
 
     int p;
     if (!xcd_position(blockIdx.x, a.B * a.H * NV, gridDim.x, p)) return;
     const int vb = p % NV;
     const size_t bh = p / NV;
-    const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, n = lane % 16, g = lane / 16;
+    const int tid = threadIdx.x, lane = tid % 64, n = lane % 16, g = lane / 16;
+    const int w = __builtin_amdgcn_readfirstlane(tid / 64);  // (visibly) wave-uniform
     const int vcol = 16 * vb + n;
     const T *rec0 = static_cast<const T *>(a.rec) + bh * a.NC * (size_t)Rec<D>::SIZE;
-    const int n_ch = a.c_end - a.c_begin;
+    const int row0 = w * C::KQ;  // first key channel of this wave
 
-    if (w == 2 || w == 3) {
-        // ---- copy waves: wave 2 copies units [0, H2) of each slot, wave 3 the rest and e^{g_C}
-        constexpr int H2 = RG::NDMA / 2;
-        constexpr int N2 = H2, N3 = RG::NDMA - H2 + 1;  // copy instructions per chunk
-        auto copy_range = [&](const char *rec, char *slot, auto i0c, auto i1c) {
-            constexpr int I0 = decltype(i0c)::value, I1 = decltype(i1c)::value;
-#pragma unroll
-            for (int i = I0; i < I1; ++i) {
-                const int u = i * 64 + lane;  // 16-byte unit of the slot
-                size_t src;
-                if (i * 64 < RG::WN_E * (int)sizeof(T) / 16)
-                    src = (size_t)Rec<D>::WN * sizeof(T) + (size_t)u * 16;
-                else if (i * 64 < (RG::WN_E + RG::DK_E) * (int)sizeof(T) / 16)
-                    src = (size_t)Rec<D>::DKT * sizeof(T) + (size_t)(u - RG::WN_E * (int)sizeof(T) / 16) * 16;
-                else
-                    src = (size_t)(Rec<D>::UT + vb * RG::UT_E) * sizeof(T) +
-                          (size_t)(u - (RG::WN_E + RG::DK_E) * (int)sizeof(T) / 16) * 16;
-                __builtin_amdgcn_global_load_lds(rec + src, slot + i * 1024, 16, 0, 0);
-            }
-        };
-        auto copy_chunk = [&](int c) {
-            const char *rec = reinterpret_cast<const char *>(rec0 + (size_t)c * Rec<D>::SIZE);
-            const int sl = (c - a.c_begin) % RG::SLOTS;
-            char *slot = reinterpret_cast<char *>(ring + sl * RG::SLOT_E);
-            if (w == 2) {
-                copy_range(rec, slot, std::integral_constant<int, 0>(), std::integral_constant<int, H2>());
-            } else {
-                copy_range(rec, slot, std::integral_constant<int, H2>(), std::integral_constant<int, RG::NDMA>());
-                if (lane == 0) __builtin_amdgcn_global_load_lds(a.gC + bh * a.NC + c, &sm.gcs[sl], 4, 0, 0);
-            }
-        };
-        // leave the copies of the newest AHEAD - 1 chunks in flight
-        auto wait_older_chunks = [&]() {
-            if (w == 2)
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm((RG::AHEAD - 1) * N2));
-            else
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm((RG::AHEAD - 1) * N3));
-        };
-        for (int j = 0; j < RG::AHEAD && j < n_ch; ++j) copy_chunk(a.c_begin + j);
-        if (n_ch >= RG::AHEAD)
-            wait_older_chunks();  // chunk c_begin landed
-        else
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        bare_barrier();  // barrier 0
-        for (int c = a.c_begin; c < a.c_end; ++c) {
-            // the slot of chunk c+AHEAD-SLOTS = c-1 is free: its last reads preceded the previous barrier
-            if (c + RG::AHEAD < a.c_end) {
-                copy_chunk(c + RG::AHEAD);
-                wait_older_chunks();  // chunk c+1 landed
-            } else {
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-            }
-            bare_barrier();  // barrier of chunk c: chunk c+1's slot is complete
-        }
-        return;
-    }
+    // e^{g_C} of the range into LDS
+    for (int i = tid; i < a.c_end - a.c_begin; i += C::THREADS) sm.gcs[i] = a.gC[bh * a.NC + a.c_begin + i];
 
-    // ---- compute waves.  S^T half w: rows (key channels) (D/2) w + 16 mt + 4g + ii, column vcol.
-    // Operands that do not depend on the exchange are read from LDS ahead of
-    // use: -W and U~ of chunk c+1 right after the barrier of chunk c (its slot
-    // is complete then), (D K)^T and e^{g_C} of chunk c at the top of chunk c.
-    floatx4 S[MH];
-#pragma unroll
-    for (int mt = 0; mt < MH; ++mt)
-        S[mt] = a.S_in ? *reinterpret_cast<const floatx4 *>(a.S_in + (bh * D + vcol) * D + (D / 2) * w + 16 * mt + 4 * g)
-                       : zero4();
-    T *sc_base = static_cast<T *>(a.sc) + (bh * a.NC * NV + vb) * (size_t)ScLayout<T, D>::PER_VB;
-    frag wf[4][KBH];                   // -W fragments (token tile tt, this half's key channels)
-    typename Vec4<T>::type ut_raw[4];  // start of the partial U: U~ on wave 0, zeros on wave 1
-    auto read_next = [&](const T *slot) {
+    Ops ops[C::NB];
+    auto load_ops = [&](Ops &o, int c) {
+        const T *rec = rec0 + (size_t)c * Rec<D>::SIZE;
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-            for (int kb = 0; kb < KBH; ++kb)
-                wf[tt][kb] = *reinterpret_cast<const frag *>(slot + ((tt * KBD + w * KBH + kb) * 64 + lane) * KPL);
-        const T *utp = w == 0 ? slot + RG::WN_E + RG::DK_E : sm.zut;
+            for (int kb = 0; kb < KBQ; ++kb)
+                o.wf[tt][kb] = *reinterpret_cast<const frag *>(rec + Rec<D>::WN + ((tt * KBD + w * KBQ + kb) * 64 + lane) * KPL);
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-            ut_raw[tt] = *reinterpret_cast<const typename Vec4<T>::type *>(utp + (tt * 64 + lane) * 4);
-    };
-    floatx4 up[4];
-    // bf16: U~ enters the partial through the matrix unit, as I16 U~ (exact in
-    // fp32), with an identity A operand on wave 0 and zeros on wave 1 (whose
-    // U~ stand-in is zeros as well); fp32: U~ is the accumulator's start.
-    typename K16<T>::frag ident;
-    if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ident[i] = (T)((w == 0 && n == 4 * g + i) ? 1.f : 0.f);
-    }
-    auto start_partial = [&]() {
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            if constexpr (sizeof(T) == 2)
-                up[tt] = K16<T>::mma(ident, ut_raw[tt], zero4());
-            else
-                up[tt] = Vec4<T>::widen(ut_raw[tt]);
-        }
-    };
-    for (int i = lane + 64 * w; i < RG::UT_E; i += 128) sm.zut[i] = (T)0.f;
-    lds_barrier();  // barrier 0: chunk c_begin is in its slot, zut cleared
-    read_next(ring);
-    for (int c = a.c_begin; c < a.c_end; ++c) {
-        const int sl = (c - a.c_begin) % RG::SLOTS;
-        const T *slot = ring + sl * RG::SLOT_E;
-        const int par = c & 1;
-        // this chunk's (D K)^T rows of half w and e^{g_C}, used after the barrier
-        frag dkf[MH][KBC];
-#pragma unroll
-        for (int mt = 0; mt < MH; ++mt)
+        for (int mt = 0; mt < MQ; ++mt)
 #pragma unroll
             for (int kb = 0; kb < KBC; ++kb)
-                dkf[mt][kb] = *reinterpret_cast<const frag *>(slot + RG::WN_E + (((MH * w + mt) * KBC + kb) * 64 + lane) * KPL);
-        const float gc = sm.gcs[sl];
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __builtin_amdgcn_sched_barrier(0);
-        // S^T half w as B fragments over its key channels (tile-chained order)
-        frag sB[KBH];
+                o.dkf[mt][kb] = *reinterpret_cast<const frag *>(rec + Rec<D>::DKT + (((w * MQ + mt) * KBC + kb) * 64 + lane) * KPL);
 #pragma unroll
-        for (int kb = 0; kb < KBH; ++kb)
+        for (int j = 0; j < TPW; ++j)
+            o.ut[j] = *reinterpret_cast<const typename Vec4<T>::type *>(rec + Rec<D>::UT + ((vb * 4 + w * TPW + j) * 64 + lane) * 4);
+    };
+
+    floatx4 S[MQ];
+#pragma unroll
+    for (int mt = 0; mt < MQ; ++mt)
+        S[mt] = a.S_in ? *reinterpret_cast<const floatx4 *>(a.S_in + (bh * D + vcol) * D + row0 + 16 * mt + 4 * g) : zero4();
+    T *sc_base = static_cast<T *>(a.sc) + (bh * a.NC * NV + vb) * (size_t)ScLayout<T, D>::PER_VB;
+
+    // U~ of the tiles this wave reduces starts their partials; the others start
+    // at zero.  bf16: through the matrix unit as I16 U~ (exact in fp32), with
+    // an identity or zero A operand per tile; fp32: U~ times 1 or 0.
+    typename K16<T>::frag ident[4];
+    float own[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        own[tt] = tt / TPW == w ? 1.f : 0.f;
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ident[tt][i] = (T)(n == 4 * g + i ? own[tt] : 0.f);
+        }
+    }
+
+    const int last = a.c_end - 1;
+#pragma unroll
+    for (int j = 0; j < C::NB; ++j) load_ops(ops[j], min(a.c_begin + j, last));
+    lds_barrier();  // e^{g_C} staged
+
+    auto step = [&](Ops &o, int c) {
+        // ---- A: entry state out, partial U
+        frag sB[KBQ];
+#pragma unroll
+        for (int kb = 0; kb < KBQ; ++kb)
 #pragma unroll
             for (int j = 0; j < KPL; ++j) {
                 const int e = kb * KPL + j;
                 fset(sB[kb], j, S[e >> 2][e & 3]);
             }
-        // export the chunk-entry state (fragments kb = w KBH ..)
         T *scp = sc_base + (size_t)c * NV * ScLayout<T, D>::PER_VB;
 #pragma unroll
-        for (int kb = 0; kb < KBH; ++kb)
-            *reinterpret_cast<frag *>(scp + ((w * KBH + kb) * 64 + lane) * KPL) = sB[kb];
-        // partial U over this half (plus U~ on wave 0), all 4 token tiles
-        start_partial();
+        for (int kb = 0; kb < KBQ; ++kb)
+            *reinterpret_cast<frag *>(scp + ((w * KBQ + kb) * 64 + lane) * KPL) = sB[kb];
+        floatx4 up[4];
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
+            if constexpr (sizeof(T) == 2)
+                up[tt] = K16<T>::mma(ident[tt], o.ut[tt % TPW], zero4());
+            else
+                up[tt] = Vec4<T>::widen(o.ut[tt % TPW]) * own[tt];
 #pragma unroll
-            for (int kb = 0; kb < KBH; ++kb) up[tt] = M::mma(wf[tt][kb], sB[kb], up[tt]);
-            *reinterpret_cast<floatx4 *>(&sm.Up[par][w][tt][lane]) = up[tt];
+            for (int kb = 0; kb < KBQ; ++kb) up[tt] = M::mma(o.wf[tt][kb], sB[kb], up[tt]);
+            sm.part[w][tt][lane] = up[tt];
         }
-        lds_barrier();  // barrier of chunk c: partials published, chunk c+1's slot complete
-        floatx4 other[4];
+        lds_barrier();
+        // ---- B: U for this wave's token tiles (every wave's partial, its own included)
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) other[tt] = *reinterpret_cast<const floatx4 *>(&sm.Up[par][1 - w][tt][lane]);
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);  // keep the exchange reads ahead of the prefetch below
-        // (after the last chunk this reads a stale slot; the values are not used)
-        read_next(ring + ((c + 1 - a.c_begin) % RG::SLOTS) * RG::SLOT_E);
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);  // the reads stay in this iteration
-        floatx4 u[4];
+        for (int j = 0; j < TPW; ++j) {
+            const int tt = w * TPW + j;
+            floatx4 u = sm.part[0][tt][lane];
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) u[tt] = up[tt] + other[tt];
-#pragma unroll
-        for (int mt = 0; mt < MH; ++mt) S[mt] *= gc;
-        // U as B fragments over the tokens
+            for (int w2 = 1; w2 < C::NW; ++w2) u += sm.part[w2][tt][lane];
+            store4(&sm.ub[lane * 16 + 4 * tt], u);
+        }
+        lds_barrier();
+        // ---- C: S^T[rows] <- e^{g_C} S^T[rows] + (D K)^T[rows] U
         frag uB[KBC];
 #pragma unroll
-        for (int kb = 0; kb < KBC; ++kb)
+        for (int kb = 0; kb < KBC; ++kb) uB[kb] = *reinterpret_cast<const frag *>(&sm.ub[lane * 16 + kb * KPL]);
+        const float gc = sm.gcs[c - a.c_begin];
 #pragma unroll
-            for (int j = 0; j < KPL; ++j) {
-                const int e = kb * KPL + j;
-                fset(uB[kb], j, u[e >> 2][e & 3]);
-            }
-        // S^T half w <- e^{g_C} S^T + (D K)^T[half w] U
+        for (int mt = 0; mt < MQ; ++mt) {
+            S[mt] *= gc;
 #pragma unroll
-        for (int kb = 0; kb < KBC; ++kb)
-#pragma unroll
-            for (int mt = 0; mt < MH; ++mt) S[mt] = M::mma(dkf[mt][kb], uB[kb], S[mt]);
+            for (int kb = 0; kb < KBC; ++kb) S[mt] = M::mma(o.dkf[mt][kb], uB[kb], S[mt]);
+        }
+        // this register set now takes chunk c + NB (past the range: the last chunk again, unused)
+        load_ops(o, min(c + C::NB, last));
+    };
+    // whole groups of NB chunks (one back edge, so the loads in flight at the
+    // top of the loop are the same on every entry), then the rest
+    static_assert(C::NB == 4, "the loop below is written for four register sets");
+    const int n_ch = a.c_end - a.c_begin, full = n_ch / C::NB * C::NB;
+    for (int c = a.c_begin; c < a.c_begin + full; c += C::NB) {
+        step(ops[0], c);
+        step(ops[1], c + 1);
+        step(ops[2], c + 2);
+        step(ops[3], c + 3);
     }
+    const int rest = n_ch - full;
+    if (rest > 0) step(ops[0], a.c_begin + full);
+    if (rest > 1) step(ops[1], a.c_begin + full + 1);
+    if (rest > 2) step(ops[2], a.c_begin + full + 2);
     if (a.S_out) {
 #pragma unroll
-        for (int mt = 0; mt < MH; ++mt)
-            *reinterpret_cast<floatx4 *>(a.S_out + (bh * D + vcol) * D + (D / 2) * w + 16 * mt + 4 * g) = S[mt];
+        for (int mt = 0; mt < MQ; ++mt)
+            *reinterpret_cast<floatx4 *>(a.S_out + (bh * D + vcol) * D + row0 + 16 * mt + 4 * g) = S[mt];
     }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
 // ======================================================================= out
