@@ -1,0 +1,147 @@
+"""The C ABI of libgdn.so on the host (no GPU needed).
+
+* Every function include/gdn.h declares is exported by the library and bound
+  by the Python binding.
+* The host-side logic answers without touching a GPU: status strings, sizes,
+  workspace sizes, the launch plan, and every validation error.  Validation
+  only looks at pointer values and sizes, so the error cases below use fake,
+  never dereferenced device addresses; each case fails validation before the
+  first HIP call.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import linear_attention_token_fwd_amd as gdn
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "gdn.h")
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:gdn_status|size_t|int|const\s+char\s*\*)\s*(gdn_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdn.LIB_PATH):
+        pytest.fail("libgdn.so is not built: run python -m linear_attention_token_fwd_amd.build")
+    return gdn.load()
+
+
+def test_every_declared_function_is_exported_and_bound(lib):
+    decl = declared_functions()
+    assert len(decl) == 8, decl
+    assert set(decl) == set(gdn.EXPORTS)
+    for name in decl:
+        fn = getattr(lib, name)  # AttributeError if the library does not export it
+        assert fn.argtypes, name  # bound by the binding
+
+
+def test_missing_library_fails_loudly():
+    with pytest.raises(RuntimeError):
+        gdn.load("/nonexistent/libgdn.so")
+
+
+def test_status_strings(lib):
+    texts = [lib.gdn_status_string(s).decode() for s in range(6)]
+    assert all(texts) and len(set(texts)) == 6
+    assert lib.gdn_status_string(99)  # unknown codes still get text
+
+
+BF16_W1 = (1, 32760, 12, 128, gdn.GDN_BF16)
+
+
+def test_workspace_sizes(lib):
+    B, T, H, D, io = BF16_W1
+    ws = gdn.gdn_fwd_workspace_bytes(B, T, H, D, io)
+    NC = math.ceil(T / 64)
+    records = B * H * NC * 320 * D * 2   # -W, Q', (D K)^T, U~, O0 per chunk-head
+    states = B * H * NC * D * D * 2      # chunk-entry states
+    assert records + states <= ws <= records + states + 64 * 2**20
+    assert gdn.gdn_fwd_bidir_workspace_bytes(B, T, H, D, io) >= 2 * ws
+    assert gdn.gdn_fwd_workspace_bytes(B, 2 * T, H, D, io) > ws
+    for bad in ((0, T, H, D, io), (B, 0, H, D, io), (B, T, 0, D, io), (B, T, H, D, 7)):
+        assert gdn.gdn_fwd_workspace_bytes(*bad) == 0
+
+
+def test_launch_plan(lib):
+    B, T, H, D, io = BF16_W1
+    p = gdn._sizes(B, T, H, D, io)
+    n = lib.gdn_fwd_launch_count(ctypes.byref(p), 0)
+    names = [lib.gdn_fwd_launch_name(ctypes.byref(p), 0, i).decode() for i in range(n)]
+    ranges = n // 3
+    assert n == 3 * ranges and ranges >= 2
+    assert names == ["gdn_prep_kernel"] * ranges + ["gdn_state_kernel"] * ranges + ["gdn_out_kernel"] * ranges
+    assert lib.gdn_fwd_launch_name(ctypes.byref(p), 0, n) is None
+    assert lib.gdn_fwd_launch_count(ctypes.byref(p), 1) == 2 * n
+    short = gdn._sizes(1, 100, 2, 64, gdn.GDN_F32)
+    assert lib.gdn_fwd_launch_count(ctypes.byref(short), 0) == 3
+    for unsupported in ((1, 64, 2, 96, gdn.GDN_BF16), (1, 64, 2, 128, gdn.GDN_F32)):
+        assert lib.gdn_fwd_launch_count(ctypes.byref(gdn._sizes(*unsupported)), 0) == -1
+
+
+def fake_params(lib, B=1, T=200, H=2, D=64, io=gdn.GDN_BF16, bidir=False):
+    """A params struct whose buffers are distinct, aligned, non-overlapping
+    fake device addresses, with a large enough workspace."""
+    p = gdn._sizes(B, T, H, D, io)
+    base, step = 1 << 44, 1 << 36
+    names = ["q", "k", "v", "log_a", "beta", "gate", "conv_q", "conv_k", "conv_v", "norm_w", "S0", "o", "S_T",
+             "workspace"]
+    for i, nm in enumerate(names):
+        setattr(p, nm, base + i * step)
+    p.eps_l2 = p.eps_norm = 1e-6
+    p.reverse = 0
+    p.workspace_bytes = (lib.gdn_fwd_bidir_workspace_bytes if bidir else lib.gdn_fwd_workspace_bytes)(ctypes.byref(p))
+    assert p.workspace_bytes > 0
+    return p
+
+
+def status_of(lib, p):
+    return lib.gdn_fwd(ctypes.byref(p), None)
+
+
+CASES = [
+    ("q NULL", lambda p: setattr(p, "q", None), gdn.GDN_ERR_INVALID_ARG),
+    ("gate NULL", lambda p: setattr(p, "gate", None), gdn.GDN_ERR_INVALID_ARG),
+    ("output NULL", lambda p: setattr(p, "o", None), gdn.GDN_ERR_INVALID_ARG),
+    ("eps_l2 < 0", lambda p: setattr(p, "eps_l2", -1.0), gdn.GDN_ERR_INVALID_ARG),
+    ("eps_norm NaN", lambda p: setattr(p, "eps_norm", float("nan")), gdn.GDN_ERR_INVALID_ARG),
+    ("reverse = 2", lambda p: setattr(p, "reverse", 2), gdn.GDN_ERR_INVALID_ARG),
+    ("T = 0", lambda p: setattr(p, "T", 0), gdn.GDN_ERR_INVALID_ARG),
+    ("Dk != Dv", lambda p: setattr(p, "Dv", 128), gdn.GDN_ERR_UNSUPPORTED),
+    ("D = 96", lambda p: (setattr(p, "Dk", 96), setattr(p, "Dv", 96)), gdn.GDN_ERR_UNSUPPORTED),
+    ("fp32 D = 128", lambda p: (setattr(p, "io_dtype", gdn.GDN_F32), setattr(p, "Dk", 128), setattr(p, "Dv", 128)),
+     gdn.GDN_ERR_UNSUPPORTED),
+    ("q misaligned", lambda p: setattr(p, "q", p.q + 8), gdn.GDN_ERR_ALIGNMENT),
+    ("log_a misaligned", lambda p: setattr(p, "log_a", p.log_a + 2), gdn.GDN_ERR_ALIGNMENT),
+    ("workspace NULL", lambda p: setattr(p, "workspace", None), gdn.GDN_ERR_WORKSPACE),
+    ("workspace too small", lambda p: setattr(p, "workspace_bytes", p.workspace_bytes - 1), gdn.GDN_ERR_WORKSPACE),
+    ("workspace misaligned", lambda p: setattr(p, "workspace", p.workspace + 16), gdn.GDN_ERR_ALIGNMENT),
+    ("output overlaps q", lambda p: setattr(p, "o", p.q + 256), gdn.GDN_ERR_INVALID_ARG),
+    ("S_T overlaps the workspace", lambda p: setattr(p, "S_T", p.workspace + 4096), gdn.GDN_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("name,mutate,expect", CASES, ids=[c[0] for c in CASES])
+def test_validation_errors(lib, name, mutate, expect):
+    p = fake_params(lib)
+    mutate(p)
+    assert status_of(lib, p) == expect, name
+
+
+def test_bidirectional_rejects_reverse(lib):
+    p = fake_params(lib, bidir=True)
+    p.reverse = 1
+    assert lib.gdn_fwd_bidir(ctypes.byref(p), None, None) == gdn.GDN_ERR_INVALID_ARG
+
+
+def test_timed_call_needs_two_events_per_launch(lib):
+    p = fake_params(lib)
+    n = lib.gdn_fwd_launch_count(ctypes.byref(p), 0)
+    events = (ctypes.c_void_p * (2 * n - 1))()
+    st = lib.gdn_fwd_timed(ctypes.byref(p), None, 0, events, 2 * n - 1, None)
+    assert st == gdn.GDN_ERR_INVALID_ARG
