@@ -67,7 +67,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "linear_attention_token_fwd_amd", "csrc")
 
 
-KERNEL_SOURCES = ("frag.hpp", "kernels.hpp")
+KERNEL_SOURCES = ("frag.hpp", "sync.hpp", "kernels.hpp")
 
 
 def csrc_hash() -> str:

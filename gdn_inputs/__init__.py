@@ -21,6 +21,17 @@ Draw order per workload (numpy PCG64, seed 1000 + workload id):
   S0 ~ N(0, 0.02^2) [B, H, Dv, Dk] for the workload with an initial state.
 For bf16 workloads q, k, v and gate are rounded to bf16 (round to nearest
 even) and carried as float32 arrays holding the rounded values.
+
+Token mixer projections (generate_mixer, seed 2000 + id unless given), model
+width C, in this order:
+  x ~ N(0, 1) [B, T, C]                      (hidden states, bf16);
+  w_in ~ N(0, 1/C) [4*H*D + 2*H, C]          (bf16; unit-variance outputs);
+  b_in ~ N(0, 0.1^2) [4*H*D + 2*H]           (fp32);
+  A_log ~ U(ln 0.01, ln 0.1) [H];
+  w_out ~ N(0, 1/(H*D)) [C, H*D]             (bf16);
+  b_out ~ N(0, 0.1^2) [C];
+  conv_q, conv_k, conv_v ~ N(0, 0.5^2) [H*D, 4]; norm_w = 1.
+The 1.3B model's width is C = 1536 = 12 x 128 (T3-Video page, Table 1).
 """
 from __future__ import annotations
 
@@ -45,6 +56,28 @@ class Workload:
     @property
     def tokens(self) -> int:
         return self.B * self.T
+
+
+@dataclass(frozen=True)
+class MixerWorkload:
+    id: int
+    name: str
+    B: int
+    T: int
+    H: int
+    D: int
+    C: int
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.T
+
+
+MIXER_WORKLOADS = [
+    MixerWorkload(0, "small mixer: B1 T700 H3 d64 C192", 1, 700, 3, 64, 192),
+    MixerWorkload(1, "Wan2.1-1.3B token mixer, 480x832, 81 frames: B1 T32760 H12 d128 C1536",
+                  1, 32760, 12, 128, 1536),
+]
 
 
 WORKLOADS = [
@@ -119,3 +152,28 @@ def generate(w: Workload | int, seed: int | None = None, T: int | None = None,
     norm_w = np.ones((H, D), np.float32)
     return dict(q=q, k=k, v=v, gate=gate, log_a=log_a, beta=beta, conv_q=conv_q,
                 conv_k=conv_k, conv_v=conv_v, norm_w=norm_w, S0=S0)
+
+
+def generate_mixer(w: MixerWorkload | int, seed: int | None = None, T: int | None = None,
+                   B: int | None = None, bias: bool = True) -> dict:
+    """Draw a token mixer's hidden states and weights (float32 numpy arrays
+    holding bf16 values where the device tensor is bf16): x, w_in, b_in,
+    A_log, w_out, b_out, conv_q, conv_k, conv_v, norm_w.  bias=False gives
+    b_in = b_out = None (the same draws otherwise)."""
+    if isinstance(w, int):
+        w = MIXER_WORKLOADS[w]
+    B = w.B if B is None else B
+    T = w.T if T is None else T
+    H, D, C = w.H, w.D, w.C
+    HD, N = H * D, 4 * H * D + 2 * H
+    rng = np.random.default_rng(2000 + w.id if seed is None else seed)
+    x = round_bf16(rng.standard_normal((B, T, C), dtype=np.float32))
+    w_in = round_bf16(rng.standard_normal((N, C), dtype=np.float32) / np.float32(np.sqrt(C)))
+    b_in = (0.1 * rng.standard_normal(N)).astype(np.float32)
+    A_log = rng.uniform(np.log(0.01), np.log(0.1), size=H).astype(np.float32)
+    w_out = round_bf16(rng.standard_normal((C, HD), dtype=np.float32) / np.float32(np.sqrt(HD)))
+    b_out = (0.1 * rng.standard_normal(C)).astype(np.float32)
+    conv = [(0.5 * rng.standard_normal((HD, 4))).astype(np.float32) for _ in range(3)]
+    return dict(x=x, w_in=w_in, b_in=b_in if bias else None, A_log=A_log, w_out=w_out,
+                b_out=b_out if bias else None, conv_q=conv[0], conv_k=conv[1], conv_v=conv[2],
+                norm_w=np.ones((H, D), np.float32))

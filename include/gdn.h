@@ -145,6 +145,70 @@ gdn_status gdn_fwd_timed(const gdn_fwd_params *p, float *S_T_rev, int bidirectio
                          struct ihipEvent_t **events, int n_events,
                          struct ihipStream_t *stream);
 
+/*
+ * Token mixer projections.  The GDN layer's per-token inputs come from the
+ * hidden states x through linear projections, and its output goes back
+ * through one (LinMorph project page, "Why learn the initialization?": the
+ * GDN parameters are built from the pretrained query, key, value and output
+ * projections; the T3-Video page, Table 1, counts the "QKV proj." and
+ * "O proj." MACs of Wan2.1-T2V-1.3B).  Weights use the layout of a linear
+ * layer, [out_features, in_features], bf16; products take bf16 operands with
+ * fp32 accumulation on MFMA.
+ *
+ * gdn_in_proj computes, per token row m of x [B*T, C]:
+ *   z = x_m W_in^T + b_in,  W_in = [W_q; W_k; W_v; W_g; W_b; W_a]
+ *   q, k, v, gate = bf16(z[part])     (H*D columns each, [B, T, H, D])
+ *   beta[h]  = sigmoid(z_b[h])                    ([B, T, H] float32)
+ *   log_a[h] = -exp(A_log[h]) * softplus(z_a[h])  ([B, T, H] float32)
+ * i.e. the update gate b in (0, 1) and the decay a = exp(log_a) in (0, 1]
+ * that gdn_fwd takes, with softplus(z) = log(1 + e^z).
+ *
+ * Layouts (row-major, contiguous):
+ *   x      [B, T, C]             bf16, 16-byte aligned
+ *   w_in   [4*H*D + 2*H, C]      bf16, 16-byte aligned; rows in the order
+ *                                q (H*D), k (H*D), v (H*D), gate (H*D),
+ *                                b (H), a (H); within a block, row h*D + i
+ *                                is head h, channel i
+ *   b_in   [4*H*D + 2*H]         float32, 16-byte aligned, or NULL (no bias)
+ *   A_log  [H]                   float32
+ * Requirements: C % 64 == 0, (H*D) % 16 == 0, B*T*C and (4*H*D+2*H)*C below
+ * 2^31; otherwise GDN_ERR_UNSUPPORTED.  Ownership, ordering and errors as for
+ * gdn_fwd: device buffers owned by the caller, no allocation, one launch on
+ * `stream`, all checks on the host first (outputs must not overlap inputs or
+ * each other).
+ */
+typedef struct gdn_in_proj_params {
+    int B, T, H, D, C;
+    const void *x;
+    const void *w_in;
+    const float *b_in;        /* NULL: no bias */
+    const float *A_log;
+    void *q, *k, *v, *gate;   /* [B, T, H, D] bf16 outputs */
+    float *beta, *log_a;      /* [B, T, H] float32 outputs */
+} gdn_in_proj_params;
+
+gdn_status gdn_in_proj(const gdn_in_proj_params *p, struct ihipStream_t *stream);
+
+/*
+ * gdn_out_proj:  out = y W_out^T + b_out  per token row, y being the layer
+ * output [B, T, H, D] viewed as [B*T, H*D].
+ *   y      [B, T, H, D]   bf16, 16-byte aligned
+ *   w_out  [C, H*D]       bf16, 16-byte aligned
+ *   b_out  [C]            float32, 16-byte aligned, or NULL
+ *   out    [B, T, C]      bf16 output
+ * Requirements: (H*D) % 64 == 0, C % 4 == 0, B*T*H*D and C*H*D below 2^31;
+ * otherwise GDN_ERR_UNSUPPORTED.  Conventions as for gdn_in_proj.
+ */
+typedef struct gdn_out_proj_params {
+    int B, T, H, D, C;
+    const void *y;
+    const void *w_out;
+    const float *b_out;       /* NULL: no bias */
+    void *out;
+} gdn_out_proj_params;
+
+gdn_status gdn_out_proj(const gdn_out_proj_params *p, struct ihipStream_t *stream);
+
 /* Static, human-readable text for a status code. */
 const char *gdn_status_string(gdn_status s);
 

@@ -18,7 +18,8 @@ GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_ALIGNMENT, GDN_ERR_WOR
 GDN_F32, GDN_BF16 = 0, 1
 
 EXPORTS = ("gdn_fwd", "gdn_fwd_bidir", "gdn_fwd_workspace_bytes", "gdn_fwd_bidir_workspace_bytes",
-           "gdn_fwd_launch_count", "gdn_fwd_launch_name", "gdn_fwd_timed", "gdn_status_string")
+           "gdn_fwd_launch_count", "gdn_fwd_launch_name", "gdn_fwd_timed", "gdn_status_string",
+           "gdn_in_proj", "gdn_out_proj")
 
 
 class GdnFwdParams(ctypes.Structure):
@@ -32,6 +33,24 @@ class GdnFwdParams(ctypes.Structure):
         ("norm_w", ctypes.c_void_p), ("eps_l2", ctypes.c_float), ("eps_norm", ctypes.c_float),
         ("S0", ctypes.c_void_p), ("o", ctypes.c_void_p), ("S_T", ctypes.c_void_p),
         ("reverse", ctypes.c_int), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class GdnInProjParams(ctypes.Structure):
+    """Mirror of ``gdn_in_proj_params`` in include/gdn.h."""
+    _fields_ = [
+        ("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int), ("D", ctypes.c_int), ("C", ctypes.c_int),
+        ("x", ctypes.c_void_p), ("w_in", ctypes.c_void_p), ("b_in", ctypes.c_void_p), ("A_log", ctypes.c_void_p),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("gate", ctypes.c_void_p),
+        ("beta", ctypes.c_void_p), ("log_a", ctypes.c_void_p),
+    ]
+
+
+class GdnOutProjParams(ctypes.Structure):
+    """Mirror of ``gdn_out_proj_params`` in include/gdn.h."""
+    _fields_ = [
+        ("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int), ("D", ctypes.c_int), ("C", ctypes.c_int),
+        ("y", ctypes.c_void_p), ("w_out", ctypes.c_void_p), ("b_out", ctypes.c_void_p), ("out", ctypes.c_void_p),
     ]
 
 
@@ -69,6 +88,10 @@ def load(path: str | None = None):
     lib.gdn_fwd_timed.argtypes = [P, ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_void_p),
                                   ctypes.c_int, ctypes.c_void_p]
     lib.gdn_fwd_timed.restype = ctypes.c_int
+    lib.gdn_in_proj.argtypes = [ctypes.POINTER(GdnInProjParams), ctypes.c_void_p]
+    lib.gdn_in_proj.restype = ctypes.c_int
+    lib.gdn_out_proj.argtypes = [ctypes.POINTER(GdnOutProjParams), ctypes.c_void_p]
+    lib.gdn_out_proj.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     if path is None:
@@ -215,4 +238,67 @@ def to_device(inp: dict, device="cuda", dtype=None):
         if key in ("q", "k", "v", "gate") and dtype is not None:
             t = t.to(dtype)
         out[key] = t.to(device).contiguous()
+    return out
+
+
+def in_proj_params(x, w_in, b_in, A_log, H, D, q, k, v, gate, beta, log_a) -> GdnInProjParams:
+    """Fill the in-projection params struct from torch tensors (the library
+    validates everything)."""
+    B, T, C = x.shape
+    p = GdnInProjParams()
+    p.B, p.T, p.H, p.D, p.C = B, T, H, D, C
+    p.x, p.w_in, p.b_in, p.A_log = _ptr(x), _ptr(w_in), _ptr(b_in), _ptr(A_log)
+    p.q, p.k, p.v, p.gate = _ptr(q), _ptr(k), _ptr(v), _ptr(gate)
+    p.beta, p.log_a = _ptr(beta), _ptr(log_a)
+    return p
+
+
+def gdn_in_proj(x, w_in, A_log, H, D, b_in=None, stream=None):
+    """q, k, v, gate ([B, T, H, D] bf16) and beta, log_a ([B, T, H] fp32) from
+    the hidden states x [B, T, C] bf16 and the stacked weight
+    w_in [4 H D + 2 H, C] bf16.  Returns (q, k, v, gate, beta, log_a)."""
+    import torch
+    B, T, C = x.shape
+    N = 4 * H * D + 2 * H
+    _check(x, "x", torch.bfloat16, (B, T, C))
+    _check(w_in, "w_in", torch.bfloat16, (N, C))
+    _check(b_in, "b_in", torch.float32, (N,))
+    _check(A_log, "A_log", torch.float32, (H,))
+    dev = x.device
+    q, k, v, gate = (torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev) for _ in range(4))
+    beta = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    log_a = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    p = in_proj_params(x, w_in, b_in, A_log, H, D, q, k, v, gate, beta, log_a)
+    s = (stream if stream is not None else torch.cuda.current_stream(dev)).cuda_stream
+    st = load().gdn_in_proj(ctypes.byref(p), ctypes.c_void_p(s))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_in_proj")
+    return q, k, v, gate, beta, log_a
+
+
+def out_proj_params(y, w_out, b_out, out) -> GdnOutProjParams:
+    B, T, H, D = y.shape
+    p = GdnOutProjParams()
+    p.B, p.T, p.H, p.D, p.C = B, T, H, D, w_out.shape[0]
+    p.y, p.w_out, p.b_out, p.out = _ptr(y), _ptr(w_out), _ptr(b_out), _ptr(out)
+    return p
+
+
+def gdn_out_proj(y, w_out, b_out=None, out=None, stream=None):
+    """out [B, T, C] bf16 = y [B, T, H, D] (as [B T, H D]) times w_out^T
+    ([C, H D] bf16) plus b_out."""
+    import torch
+    B, T, H, D = y.shape
+    C = w_out.shape[0]
+    _check(y, "y", torch.bfloat16, (B, T, H, D))
+    _check(w_out, "w_out", torch.bfloat16, (C, H * D))
+    _check(b_out, "b_out", torch.float32, (C,))
+    _check(out, "out", torch.bfloat16, (B, T, C))
+    if out is None:
+        out = torch.empty((B, T, C), dtype=torch.bfloat16, device=y.device)
+    p = out_proj_params(y, w_out, b_out, out)
+    s = (stream if stream is not None else torch.cuda.current_stream(y.device)).cuda_stream
+    st = load().gdn_out_proj(ctypes.byref(p), ctypes.c_void_p(s))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_out_proj")
     return out

@@ -34,7 +34,7 @@ def lib():
 
 def test_every_declared_function_is_exported_and_bound(lib):
     decl = declared_functions()
-    assert len(decl) == 8, decl
+    assert len(decl) == 10, decl
     assert set(decl) == set(gdn.EXPORTS)
     for name in decl:
         fn = getattr(lib, name)  # AttributeError if the library does not export it
@@ -145,3 +145,71 @@ def test_timed_call_needs_two_events_per_launch(lib):
     events = (ctypes.c_void_p * (2 * n - 1))()
     st = lib.gdn_fwd_timed(ctypes.byref(p), None, 0, events, 2 * n - 1, None)
     assert st == gdn.GDN_ERR_INVALID_ARG
+
+
+def fake_in_proj(B=1, T=300, H=3, D=64, C=192):
+    """In-projection params on distinct, aligned, fake device addresses."""
+    p = gdn.GdnInProjParams()
+    p.B, p.T, p.H, p.D, p.C = B, T, H, D, C
+    base, step = 1 << 44, 1 << 36
+    for i, nm in enumerate(["x", "w_in", "b_in", "A_log", "q", "k", "v", "gate", "beta", "log_a"]):
+        setattr(p, nm, base + i * step)
+    return p
+
+
+def fake_out_proj(B=1, T=300, H=3, D=64, C=192):
+    p = gdn.GdnOutProjParams()
+    p.B, p.T, p.H, p.D, p.C = B, T, H, D, C
+    base, step = 1 << 44, 1 << 36
+    for i, nm in enumerate(["y", "w_out", "b_out", "out"]):
+        setattr(p, nm, base + i * step)
+    return p
+
+
+IN_PROJ_CASES = [
+    ("x NULL", lambda p: setattr(p, "x", None), gdn.GDN_ERR_INVALID_ARG),
+    ("A_log NULL", lambda p: setattr(p, "A_log", None), gdn.GDN_ERR_INVALID_ARG),
+    ("log_a NULL", lambda p: setattr(p, "log_a", None), gdn.GDN_ERR_INVALID_ARG),
+    ("T = 0", lambda p: setattr(p, "T", 0), gdn.GDN_ERR_INVALID_ARG),
+    ("C % 64 != 0", lambda p: setattr(p, "C", 160), gdn.GDN_ERR_UNSUPPORTED),
+    ("H D % 16 != 0", lambda p: setattr(p, "D", 60), gdn.GDN_ERR_UNSUPPORTED),
+    ("x too large", lambda p: (setattr(p, "T", 1 << 22), setattr(p, "C", 1024)), gdn.GDN_ERR_UNSUPPORTED),
+    ("w_in misaligned", lambda p: setattr(p, "w_in", p.w_in + 8), gdn.GDN_ERR_ALIGNMENT),
+    ("b_in misaligned", lambda p: setattr(p, "b_in", p.b_in + 4), gdn.GDN_ERR_ALIGNMENT),
+    ("beta misaligned", lambda p: setattr(p, "beta", p.beta + 2), gdn.GDN_ERR_ALIGNMENT),
+    ("q over x", lambda p: setattr(p, "q", p.x + 256), gdn.GDN_ERR_INVALID_ARG),
+    ("gate over k", lambda p: setattr(p, "gate", p.k + 1024), gdn.GDN_ERR_INVALID_ARG),
+    ("log_a over the bias", lambda p: setattr(p, "log_a", p.b_in), gdn.GDN_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("name,mutate,expect", IN_PROJ_CASES, ids=[c[0] for c in IN_PROJ_CASES])
+def test_in_proj_validation(lib, name, mutate, expect):
+    p = fake_in_proj()
+    mutate(p)
+    assert lib.gdn_in_proj(ctypes.byref(p), None) == expect, name
+
+
+OUT_PROJ_CASES = [
+    ("y NULL", lambda p: setattr(p, "y", None), gdn.GDN_ERR_INVALID_ARG),
+    ("out NULL", lambda p: setattr(p, "out", None), gdn.GDN_ERR_INVALID_ARG),
+    ("C = 0", lambda p: setattr(p, "C", 0), gdn.GDN_ERR_INVALID_ARG),
+    ("H D % 64 != 0", lambda p: setattr(p, "D", 48), gdn.GDN_ERR_UNSUPPORTED),
+    ("C % 4 != 0", lambda p: setattr(p, "C", 190), gdn.GDN_ERR_UNSUPPORTED),
+    ("w_out misaligned", lambda p: setattr(p, "w_out", p.w_out + 2), gdn.GDN_ERR_ALIGNMENT),
+    ("out over y", lambda p: setattr(p, "out", p.y + 16), gdn.GDN_ERR_INVALID_ARG),
+    ("out over w_out", lambda p: setattr(p, "out", p.w_out), gdn.GDN_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("name,mutate,expect", OUT_PROJ_CASES, ids=[c[0] for c in OUT_PROJ_CASES])
+def test_out_proj_validation(lib, name, mutate, expect):
+    p = fake_out_proj()
+    mutate(p)
+    assert lib.gdn_out_proj(ctypes.byref(p), None) == expect, name
+
+
+def test_projection_params_null():
+    lib = gdn.load()
+    assert lib.gdn_in_proj(None, None) == gdn.GDN_ERR_INVALID_ARG
+    assert lib.gdn_out_proj(None, None) == gdn.GDN_ERR_INVALID_ARG

@@ -1,0 +1,173 @@
+"""Parity of the token mixer projections (gdn_in_proj, gdn_out_proj, through
+the C ABI) with the fp64 projection oracle.
+
+Bars.  The products run on bf16 operands with fp32 accumulation, so:
+  * bf16 outputs (q, k, v, gate, the output projection) must sit within one
+    bf16 rounding of the exact value: |got - ref| <= 2^-8 |ref| + 1e-4, and
+    rel-L2 <= 4e-3 over the tensor;
+  * fp32 outputs (beta, log a) must match to |got - ref| <= 2e-5 + 1e-5 |ref|
+    (fp32 accumulation over C products), rel-L2 <= 1e-5.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs
+import linear_attention_token_fwd_amd as gdn
+from oracle import proj as oproj
+from tests.gpu_common import rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+MW = gdn_inputs.MIXER_WORKLOADS
+
+
+def _dev(a, dtype=torch.float32):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(dtype).contiguous()
+
+
+def check_bf16(name, got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    e = rel_l2(got, ref)
+    worst = float(np.max(np.abs(got - ref) - (2.0 ** -8 * np.abs(ref) + 1e-4)))
+    say(f"  {name}: rel-L2 {e:.3e}, worst excess over one bf16 rounding {worst:.2e}")
+    assert e <= 4e-3, f"{name}: rel-L2 {e:.3e}"
+    assert worst <= 0, f"{name}: an element is off by more than one bf16 rounding"
+
+
+def check_f32(name, got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    e = rel_l2(got, ref)
+    worst = float(np.max(np.abs(got - ref) - (2e-5 + 1e-5 * np.abs(ref))))
+    say(f"  {name}: rel-L2 {e:.3e}, worst excess {worst:.2e}")
+    assert e <= 1e-5, f"{name}: rel-L2 {e:.3e}"
+    assert worst <= 0, f"{name}: element error above the bound"
+
+
+def run_in_proj(inp, H, D):
+    """gdn_in_proj on NaN-poisoned outputs (every element must be written)."""
+    x = _dev(inp["x"], torch.bfloat16)
+    w_in = _dev(inp["w_in"], torch.bfloat16)
+    B, T, C = inp["x"].shape
+    q, k, v, g = (torch.full((B, T, H, D), float("nan"), dtype=torch.bfloat16, device="cuda") for _ in range(4))
+    beta, log_a = (torch.full((B, T, H), float("nan"), dtype=torch.float32, device="cuda") for _ in range(2))
+    A_log, b_in = _dev(inp["A_log"]), _dev(inp["b_in"])
+    p = gdn.in_proj_params(x, w_in, b_in, A_log, H, D, q, k, v, g, beta, log_a)
+    st = gdn.load().gdn_in_proj(ctypes.byref(p), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == gdn.GDN_OK, gdn.gdn_status_string(st)
+    torch.cuda.synchronize()
+    return [t.double().cpu().numpy() for t in (q, k, v, g, beta, log_a)]
+
+
+def compare_in_proj(inp, H, D, rows=None):
+    got = run_in_proj(inp, H, D)
+    x = inp["x"]
+    if rows is not None:  # the oracle on sampled token rows only
+        x = x.reshape(-1, x.shape[-1])[rows][None]
+        got = [g.reshape(-1, *g.shape[2:])[rows][None] for g in got]
+    ref = oproj.in_proj(x, inp["w_in"], inp["b_in"], inp["A_log"], H, D)
+    for name, g, r in zip(("q", "k", "v", "gate"), got[:4], ref[:4]):
+        check_bf16(name, g, r)
+    check_f32("beta", got[4], ref[4])
+    check_f32("log_a", got[5], ref[5])
+
+
+@pytest.mark.parametrize("bias", [True, False])
+def test_in_proj_small(bias):
+    """H = 3 heads of 64 (odd gate columns), C = 192, T = 700: ragged row
+    tiles and a 6-column last column tile."""
+    w = MW[0]
+    say(f"case: in_proj {w.name} bias={bias}")
+    compare_in_proj(gdn_inputs.generate_mixer(w, bias=bias), w.H, w.D)
+
+
+@pytest.mark.parametrize("B,T", [(2, 300), (1, 1), (1, 257)])
+def test_in_proj_model_width(B, T):
+    """The 1.3B model's width (C = 1536, H = 12, d = 128) at short lengths."""
+    w = MW[1]
+    say(f"case: in_proj C=1536 B={B} T={T}")
+    compare_in_proj(gdn_inputs.generate_mixer(w, T=T, B=B, seed=50 + T), w.H, w.D)
+
+
+def test_in_proj_full_size_sampled():
+    """T = 32760 at C = 1536, in the launch the benchmark times; the oracle
+    checks 1500 sampled token rows, the last rows included."""
+    w = MW[1]
+    inp = gdn_inputs.generate_mixer(w)
+    M = w.B * w.T
+    rows = np.unique(np.concatenate([np.random.default_rng(9).choice(M, 1480, replace=False),
+                                     np.arange(M - 20, M)]))
+    say(f"case: in_proj full size {w.name}, {len(rows)} sampled rows")
+    compare_in_proj(inp, w.H, w.D, rows=rows)
+
+
+def run_out_proj(y, w_out, b_out):
+    B, T, H, D = y.shape
+    C = w_out.shape[0]
+    out = torch.full((B, T, C), float("nan"), dtype=torch.bfloat16, device="cuda")
+    gdn.gdn_out_proj(_dev(y, torch.bfloat16), _dev(w_out, torch.bfloat16), _dev(b_out), out=out)
+    torch.cuda.synchronize()
+    return out.double().cpu().numpy()
+
+
+@pytest.mark.parametrize("wid,T,bias", [(0, 700, True), (0, 700, False), (1, 300, True), (1, 1, True)])
+def test_out_proj(wid, T, bias):
+    w = MW[wid]
+    inp = gdn_inputs.generate_mixer(w, T=T, bias=bias, seed=70 + T)
+    y = gdn_inputs.round_bf16(np.random.default_rng(T).standard_normal((w.B, T, w.H, w.D), dtype=np.float32))
+    say(f"case: out_proj {w.name} T={T} bias={bias}")
+    check_bf16("out", run_out_proj(y, inp["w_out"], inp["b_out"]), oproj.out_proj(y, inp["w_out"], inp["b_out"]))
+
+
+def test_out_proj_full_size_sampled():
+    w = MW[1]
+    inp = gdn_inputs.generate_mixer(w)
+    y = gdn_inputs.round_bf16(np.random.default_rng(1).standard_normal((w.B, w.T, w.H, w.D), dtype=np.float32))
+    say(f"case: out_proj full size {w.name}")
+    got = run_out_proj(y, inp["w_out"], inp["b_out"]).reshape(w.T, -1)
+    rows = np.unique(np.concatenate([np.random.default_rng(4).choice(w.T, 1480, replace=False),
+                                     np.arange(w.T - 20, w.T)]))
+    ref = oproj.out_proj(y[:, rows], inp["w_out"], inp["b_out"])[0]
+    check_bf16("out", got[rows], ref)
+
+
+def test_projections_deterministic():
+    w = MW[0]
+    inp = gdn_inputs.generate_mixer(w)
+    a = run_in_proj(inp, w.H, w.D)
+    b = run_in_proj(inp, w.H, w.D)
+    assert all(np.array_equal(x, y, equal_nan=False) for x, y in zip(a, b))
+
+
+def test_in_proj_errors_leave_outputs_untouched():
+    w = MW[0]
+    inp = gdn_inputs.generate_mixer(w)
+    x = _dev(inp["x"], torch.bfloat16)
+    w_in = _dev(inp["w_in"], torch.bfloat16)
+    A_log = _dev(inp["A_log"])
+    B, T, C = inp["x"].shape
+    H, D = w.H, w.D
+    q, k, v, g = (torch.full((B, T, H, D), 7.0, dtype=torch.bfloat16, device="cuda") for _ in range(4))
+    beta, log_a = (torch.full((B, T, H), 7.0, dtype=torch.float32, device="cuda") for _ in range(2))
+    lib = gdn.load()
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def status(mutate):
+        p = gdn.in_proj_params(x, w_in, None, A_log, H, D, q, k, v, g, beta, log_a)
+        mutate(p)
+        return lib.gdn_in_proj(ctypes.byref(p), s)
+
+    assert status(lambda p: setattr(p, "C", 160)) == gdn.GDN_ERR_UNSUPPORTED       # C % 64 != 0
+    assert status(lambda p: setattr(p, "x", p.x + 2)) == gdn.GDN_ERR_ALIGNMENT
+    assert status(lambda p: setattr(p, "q", None)) == gdn.GDN_ERR_INVALID_ARG
+    assert status(lambda p: setattr(p, "k", p.q)) == gdn.GDN_ERR_INVALID_ARG       # outputs overlap
+    assert status(lambda p: setattr(p, "beta", p.w_in)) == gdn.GDN_ERR_INVALID_ARG  # output over an input
+    torch.cuda.synchronize()
+    for t in (q, k, v, g, beta, log_a):
+        assert bool(torch.all(t == 7.0))
