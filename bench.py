@@ -137,6 +137,9 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=1, help="workload id (default 1: T=32760 H=12 d=128)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: all available)")
+    ap.add_argument("--mixer", action="store_true",
+                    help="time the whole token mixer (in-projection with the gate parameterisation, the layer, "
+                         "out-projection) at T=32760, C=1536, H=12, d=128 instead of the layer alone")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB (read 1 GiB, write 1 GiB) three times, to "
                          "calibrate the FETCH_SIZE / WRITE_SIZE counters")
@@ -164,6 +167,8 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "dispatches": 3}), flush=True)
         return 0
+    if args.mixer:
+        return run_mixer(args)
     w = gdn_inputs.WORKLOADS[args.workload]
     log(f"workload {w.id}: {w.name}")
     t0 = time.time()
@@ -310,6 +315,144 @@ def main() -> int:
                     for k, v in kernels.items()},
         "cpu_baseline": cpu,
         "parity": parity,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+GEMM_KERNELS = {"in_proj": "gdn_gemm_kernel<in-projection>", "out_proj": "gdn_gemm_kernel<plain>"}
+
+
+def run_mixer(args) -> int:
+    """One step = one gdn_mixer_fwd call: in-projection (bf16 MFMA GEMM with
+    the gate parameterisation in its epilogue), the layer, out-projection."""
+    import numpy as np
+    import torch
+
+    import gdn_inputs
+    import linear_attention_token_fwd_amd as gdn
+
+    w = gdn_inputs.MIXER_WORKLOADS[1]
+    log(f"mixer workload: {w.name}")
+    inp = gdn_inputs.generate_mixer(w)
+    B, T, H, D, C = w.B, w.T, w.H, w.D, w.C
+    N = 4 * H * D + 2 * H
+
+    def dev(a, dt=torch.float32):
+        return None if a is None else torch.from_numpy(a).to("cuda").to(dt).contiguous()
+    x, w_in, w_out = dev(inp["x"], torch.bfloat16), dev(inp["w_in"], torch.bfloat16), dev(inp["w_out"], torch.bfloat16)
+    b_in, b_out, A_log = dev(inp["b_in"]), dev(inp["b_out"]), dev(inp["A_log"])
+    conv = [dev(inp[k]) for k in ("conv_q", "conv_k", "conv_v")]
+    norm_w = dev(inp["norm_w"])
+    out = torch.empty((B, T, C), dtype=torch.bfloat16, device="cuda")
+    S_T = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
+    workspace = torch.empty(gdn.gdn_mixer_workspace_bytes(B, T, H, D, C), dtype=torch.uint8, device="cuda")
+    lib = gdn.load()
+    p = gdn.mixer_params(x, w_in, b_in, A_log, *conv, norm_w, None, w_out, b_out, out, S_T, workspace, H, D)
+    stream = torch.cuda.Stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+
+    def step():
+        st = lib.gdn_mixer_fwd(ctypes.byref(p), sptr)
+        if st != gdn.GDN_OK:
+            raise gdn.GdnError(st, "gdn_mixer_fwd")
+
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t_start) * 1e3 / args.steps
+    tokens_per_s = B * T / (ms_per_step * 1e-3)
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step, {tokens_per_s:.4e} tokens/s")
+
+    # ---- per-kernel durations (HIP events on each launch's stream)
+    ev = HipEvents()
+    lp = gdn._sizes(B, T, H, D, gdn.GDN_BF16)
+    nl = lib.gdn_fwd_launch_count(ctypes.byref(lp), 0)
+    names = ["in_proj", "out_proj"] + [lib.gdn_fwd_launch_name(ctypes.byref(lp), 0, i).decode() for i in range(nl)]
+    reps = min(args.steps, 20)
+    nev = 4 + 2 * nl
+    evs = [ev.create(nev) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for i in range(reps):
+        st = lib.gdn_mixer_fwd_timed(ctypes.byref(p), evs[i], nev, sptr)
+        if st != gdn.GDN_OK:
+            raise gdn.GdnError(st, "gdn_mixer_fwd_timed")
+    torch.cuda.synchronize()
+    per_launch, per_call = {}, {}
+    for i in range(reps):
+        tot = {}
+        for j, nm in enumerate(names):
+            ev.sync(evs[i][2 * j + 1])
+            dms = ev.elapsed_ms(evs[i][2 * j], evs[i][2 * j + 1])
+            per_launch.setdefault(nm, []).append(dms)
+            tot[nm] = tot.get(nm, 0.0) + dms
+        for nm, v in tot.items():
+            per_call.setdefault(nm, []).append(v)
+    flops = {"in_proj": 2.0 * B * T * C * N, "out_proj": 2.0 * B * T * H * D * C}
+    kb = kernel_bytes_per_token_head(D, 2)
+    kernels = {}
+    for nm in per_launch:
+        n = names.count(nm)
+        k = {"launches_per_call": n, "avg_ms": float(np.mean(per_launch[nm])),
+             "ms_per_call": float(np.mean(per_call[nm]))}
+        if nm in flops:
+            k["kernel"] = GEMM_KERNELS[nm]
+            k["flops_per_launch"] = flops[nm]
+            k["TFLOPs"] = flops[nm] / (k["avg_ms"] * 1e-3) / 1e12
+        else:
+            k["bytes_per_launch"] = kb[nm] * B * T * H / n
+            k["GBps"] = kb[nm] * B * T * H / (k["ms_per_call"] * 1e-3) / 1e9
+        kernels[nm] = k
+        log(f"  {nm}: {k['avg_ms']:.4f} ms/launch x{n} = {k['ms_per_call']:.4f} ms/call")
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_call"])
+    kd = kernels[dom]
+    if dom in flops:
+        achieved = kd["flops_per_launch"] / (kd["avg_ms"] * 1e-3) / 1e12
+        roofline = {"kernel": kd["kernel"], "bound": "mfma", "achieved": round(achieved, 1),
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "traffic": None, "avg_launch_ms": round(kd["avg_ms"], 5)}
+    else:
+        achieved = kd["bytes_per_launch"] / (kd["avg_ms"] * 1e-3) / 1e9
+        roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "avg_launch_ms": round(kd["avg_ms"], 5)}
+
+    cpu, parity = None, None
+    if not args.no_cpu_baseline:
+        from oracle import proj as oproj
+        got = out.double().cpu().numpy()
+        got_s = S_T.double().cpu().numpy()
+        log("running the oracle on the host ...")
+        t1 = time.perf_counter()
+        ref, ref_s, _ = oproj.mixer(inp["x"], inp["w_in"], inp["b_in"], inp["A_log"], inp["conv_q"],
+                                    inp["conv_k"], inp["conv_v"], inp["norm_w"], inp["w_out"], inp["b_out"],
+                                    H, D, threads=args.cpu_threads)
+        cpu_s = time.perf_counter() - t1
+        cores = min(H, len(os.sched_getaffinity(0))) if args.cpu_threads == 0 else args.cpu_threads
+        cpu = {"value": round(B * T / cpu_s, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+               "sample": f"the whole workload ({B}x{T} tokens, fp64 projections with numpy, the layer one "
+                         f"thread per head), {cpu_s:.2f} s wall",
+               "host_cores_available": len(os.sched_getaffinity(0))}
+        parity = {"out_rel_l2": float(np.linalg.norm(got - ref) / np.linalg.norm(ref)),
+                  "S_T_rel_l2": float(np.linalg.norm(got_s - ref_s) / np.linalg.norm(ref_s))}
+        log(f"oracle {cpu_s:.2f} s; parity {parity}")
+
+    res = {
+        "metric": "GDN token mixer fwd tokens/s (in-projection, layer, out-projection) at T=32760,C=1536,"
+                  "H=12,d=128 bf16",
+        "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "T": T, "H": H, "d": D, "C": C, "chunk": 64},
+        "roofline": roofline,
+        "kernels": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kernels.items()},
+        "cpu_baseline": cpu, "parity": parity,
     }
     print(json.dumps(res), flush=True)
     return 0

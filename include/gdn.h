@@ -209,6 +209,48 @@ typedef struct gdn_out_proj_params {
 
 gdn_status gdn_out_proj(const gdn_out_proj_params *p, struct ihipStream_t *stream);
 
+/*
+ * The whole token mixer: gdn_in_proj, then the layer (gdn_fwd, forward scan,
+ * bf16), then gdn_out_proj, all on `stream`:
+ *   out = out_proj( GDN layer( in_proj(x) ) )
+ * The intermediates (q, k, v, gate, b, log a and the layer output y) live in
+ * the caller's workspace, of at least gdn_mixer_workspace_bytes() bytes,
+ * 256-byte aligned (that function reads B, T, H, D, C only and returns 0 for
+ * invalid sizes).  D must be 64 or 128 and every requirement of the three
+ * stages holds; all checks of all stages run before the first launch.
+ *   x [B, T, C], w_in, b_in, A_log as for gdn_in_proj; conv_*, norm_w, eps,
+ *   S0, S_T as for gdn_fwd; w_out, b_out as for gdn_out_proj; out [B, T, C]
+ *   bf16.  No caller buffer may overlap the workspace; out may not overlap
+ *   any input.
+ * gdn_mixer_fwd_timed does the same and records events[0] / events[1] around
+ * the in-projection launch, events[2] / events[3] around the output
+ * projection, and events[4 + 2i] / events[5 + 2i] around launch i of the
+ * layer (gdn_fwd_launch_count of the layer's sizes), on the stream each runs
+ * on; n_events >= 4 + 2 * that count, else GDN_ERR_INVALID_ARG.
+ */
+typedef struct gdn_mixer_params {
+    int B, T, H, D, C;
+    const void *x;
+    const void *w_in;
+    const float *b_in;        /* NULL: no bias */
+    const float *A_log;
+    const float *conv_q, *conv_k, *conv_v;
+    const float *norm_w;      /* NULL: ones */
+    float eps_l2, eps_norm;
+    const float *S0;          /* NULL: zero initial state */
+    float *S_T;               /* final state, or NULL */
+    const void *w_out;
+    const float *b_out;       /* NULL: no bias */
+    void *out;
+    void *workspace;
+    size_t workspace_bytes;
+} gdn_mixer_params;
+
+size_t gdn_mixer_workspace_bytes(const gdn_mixer_params *p);
+gdn_status gdn_mixer_fwd(const gdn_mixer_params *p, struct ihipStream_t *stream);
+gdn_status gdn_mixer_fwd_timed(const gdn_mixer_params *p, struct ihipEvent_t **events, int n_events,
+                               struct ihipStream_t *stream);
+
 /* Static, human-readable text for a status code. */
 const char *gdn_status_string(gdn_status s);
 

@@ -19,7 +19,7 @@ GDN_F32, GDN_BF16 = 0, 1
 
 EXPORTS = ("gdn_fwd", "gdn_fwd_bidir", "gdn_fwd_workspace_bytes", "gdn_fwd_bidir_workspace_bytes",
            "gdn_fwd_launch_count", "gdn_fwd_launch_name", "gdn_fwd_timed", "gdn_status_string",
-           "gdn_in_proj", "gdn_out_proj")
+           "gdn_in_proj", "gdn_out_proj", "gdn_mixer_workspace_bytes", "gdn_mixer_fwd", "gdn_mixer_fwd_timed")
 
 
 class GdnFwdParams(ctypes.Structure):
@@ -51,6 +51,18 @@ class GdnOutProjParams(ctypes.Structure):
     _fields_ = [
         ("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int), ("D", ctypes.c_int), ("C", ctypes.c_int),
         ("y", ctypes.c_void_p), ("w_out", ctypes.c_void_p), ("b_out", ctypes.c_void_p), ("out", ctypes.c_void_p),
+    ]
+
+
+class GdnMixerParams(ctypes.Structure):
+    """Mirror of ``gdn_mixer_params`` in include/gdn.h."""
+    _fields_ = [
+        ("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int), ("D", ctypes.c_int), ("C", ctypes.c_int),
+        ("x", ctypes.c_void_p), ("w_in", ctypes.c_void_p), ("b_in", ctypes.c_void_p), ("A_log", ctypes.c_void_p),
+        ("conv_q", ctypes.c_void_p), ("conv_k", ctypes.c_void_p), ("conv_v", ctypes.c_void_p),
+        ("norm_w", ctypes.c_void_p), ("eps_l2", ctypes.c_float), ("eps_norm", ctypes.c_float),
+        ("S0", ctypes.c_void_p), ("S_T", ctypes.c_void_p), ("w_out", ctypes.c_void_p), ("b_out", ctypes.c_void_p),
+        ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -92,6 +104,13 @@ def load(path: str | None = None):
     lib.gdn_in_proj.restype = ctypes.c_int
     lib.gdn_out_proj.argtypes = [ctypes.POINTER(GdnOutProjParams), ctypes.c_void_p]
     lib.gdn_out_proj.restype = ctypes.c_int
+    PM = ctypes.POINTER(GdnMixerParams)
+    lib.gdn_mixer_workspace_bytes.argtypes = [PM]
+    lib.gdn_mixer_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdn_mixer_fwd.argtypes = [PM, ctypes.c_void_p]
+    lib.gdn_mixer_fwd.restype = ctypes.c_int
+    lib.gdn_mixer_fwd_timed.argtypes = [PM, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_void_p]
+    lib.gdn_mixer_fwd_timed.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     if path is None:
@@ -302,3 +321,57 @@ def gdn_out_proj(y, w_out, b_out=None, out=None, stream=None):
     if st != GDN_OK:
         raise GdnError(st, "gdn_out_proj")
     return out
+
+
+def mixer_params(x, w_in, b_in, A_log, conv_q, conv_k, conv_v, norm_w, S0, w_out, b_out, out, S_T,
+                 workspace, H, D, eps_l2=1e-6, eps_norm=1e-6) -> GdnMixerParams:
+    """Fill the mixer params struct from torch tensors (the library validates)."""
+    B, T, C = x.shape
+    p = GdnMixerParams()
+    p.B, p.T, p.H, p.D, p.C = B, T, H, D, C
+    p.x, p.w_in, p.b_in, p.A_log = _ptr(x), _ptr(w_in), _ptr(b_in), _ptr(A_log)
+    p.conv_q, p.conv_k, p.conv_v, p.norm_w = _ptr(conv_q), _ptr(conv_k), _ptr(conv_v), _ptr(norm_w)
+    p.eps_l2, p.eps_norm = eps_l2, eps_norm
+    p.S0, p.S_T, p.w_out, p.b_out, p.out = _ptr(S0), _ptr(S_T), _ptr(w_out), _ptr(b_out), _ptr(out)
+    p.workspace = _ptr(workspace)
+    p.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return p
+
+
+def gdn_mixer_workspace_bytes(B: int, T: int, H: int, D: int, C: int) -> int:
+    p = GdnMixerParams()
+    p.B, p.T, p.H, p.D, p.C = B, T, H, D, C
+    return load().gdn_mixer_workspace_bytes(ctypes.byref(p))
+
+
+def gdn_mixer_fwd(x, w_in, A_log, conv_q, conv_k, conv_v, w_out, H, D, b_in=None, b_out=None, norm_w=None,
+                  S0=None, eps_l2=1e-6, eps_norm=1e-6, out=None, S_T=None, want_state=True, workspace=None,
+                  stream=None):
+    """The whole token mixer on device tensors: out [B, T, C] bf16 =
+    out_proj(GDN layer(in_proj(x))).  Returns (out, S_T)."""
+    import torch
+    B, T, C = x.shape
+    N = 4 * H * D + 2 * H
+    f32 = torch.float32
+    for t, name, dt, shp in ((x, "x", torch.bfloat16, (B, T, C)), (w_in, "w_in", torch.bfloat16, (N, C)),
+                             (b_in, "b_in", f32, (N,)), (A_log, "A_log", f32, (H,)),
+                             (conv_q, "conv_q", f32, (H * D, 4)), (conv_k, "conv_k", f32, (H * D, 4)),
+                             (conv_v, "conv_v", f32, (H * D, 4)), (norm_w, "norm_w", f32, (H, D)),
+                             (S0, "S0", f32, (B, H, D, D)), (w_out, "w_out", torch.bfloat16, (C, H * D)),
+                             (b_out, "b_out", f32, (C,)), (out, "out", torch.bfloat16, (B, T, C)),
+                             (S_T, "S_T", f32, (B, H, D, D))):
+        _check(t, name, dt, shp)
+    if out is None:
+        out = torch.empty((B, T, C), dtype=torch.bfloat16, device=x.device)
+    if S_T is None and want_state:
+        S_T = torch.empty((B, H, D, D), dtype=f32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(gdn_mixer_workspace_bytes(B, T, H, D, C), 1), dtype=torch.uint8,
+                                device=x.device)
+    p = mixer_params(x, w_in, b_in, A_log, conv_q, conv_k, conv_v, norm_w, S0, w_out, b_out, out, S_T,
+                     workspace, H, D, eps_l2, eps_norm)
+    s = (stream if stream is not None else torch.cuda.current_stream(x.device)).cuda_stream
+    st = load().gdn_mixer_fwd(ctypes.byref(p), ctypes.c_void_p(s))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_mixer_fwd")
+    return out, S_T

@@ -10,6 +10,7 @@
 #include <vector>
 
 #include "../../include/gdn.h"
+#include "internal.hpp"
 #include "kernels.hpp"
 
 namespace {
@@ -387,6 +388,12 @@ gdn_status call(const gdn_fwd_params *p, float *S_T_rev, bool bidir, hipEvent_t 
 }
 
 }  // namespace
+
+gdn_status gdn_internal::fwd_check(const gdn_fwd_params *p) { return validate(p, nullptr, 1); }
+
+gdn_status gdn_internal::fwd_call(const gdn_fwd_params *p, hipEvent_t *timing, int n_timing, hipStream_t s) {
+    return call(p, nullptr, false, timing, n_timing, s);
+}
 
 extern "C" {
 

@@ -1,5 +1,6 @@
-// gdn_proj.hip -- host side of the token mixer projections declared in
-// include/gdn.h (gdn_in_proj, gdn_out_proj): validation and the launch.
+// gdn_proj.hip -- host side of the token mixer entry points declared in
+// include/gdn.h: the projections (gdn_in_proj, gdn_out_proj) and the whole
+// mixer (gdn_mixer_fwd): validation, workspace carve-up and the launches.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -7,6 +8,7 @@
 
 #include "../../include/gdn.h"
 #include "gemm.hpp"
+#include "internal.hpp"
 
 namespace {
 
@@ -63,7 +65,7 @@ gdn_status launch_gemm(gdn::GemmArgs &a, hipStream_t s) {
     return GDN_OK;
 }
 
-gdn_status in_proj(const gdn_in_proj_params *p, hipStream_t s) {
+gdn_status in_proj_check(const gdn_in_proj_params *p) {
     if (!p || p->B < 1 || p->T < 1 || p->H < 1 || p->D < 1 || p->C < 1) return GDN_ERR_INVALID_ARG;
     if (!p->x || !p->w_in || !p->A_log || !p->q || !p->k || !p->v || !p->gate || !p->beta || !p->log_a)
         return GDN_ERR_INVALID_ARG;
@@ -83,9 +85,12 @@ gdn_status in_proj(const gdn_in_proj_params *p, hipStream_t s) {
     const Span outs[] = {span(p->q, m * hd * 2),    span(p->k, m * hd * 2),    span(p->v, m * hd * 2),
                          span(p->gate, m * hd * 2), span(p->beta, m * h * 4), span(p->log_a, m * h * 4)};
     if (!disjoint(ins, outs)) return GDN_ERR_INVALID_ARG;
+    return GDN_OK;
+}
 
+gdn_status in_proj_launch(const gdn_in_proj_params *p, hipStream_t s) {
     gdn::GemmArgs a = {};
-    a.M = (int)M; a.N = (int)N; a.K = p->C;
+    a.M = p->B * p->T; a.N = 4 * p->H * p->D + 2 * p->H; a.K = p->C;
     a.x = static_cast<const bf16 *>(p->x);
     a.w = static_cast<const bf16 *>(p->w_in);
     a.bias = p->b_in;
@@ -93,12 +98,12 @@ gdn_status in_proj(const gdn_in_proj_params *p, hipStream_t s) {
     a.dst[1] = static_cast<bf16 *>(p->k);
     a.dst[2] = static_cast<bf16 *>(p->v);
     a.dst[3] = static_cast<bf16 *>(p->gate);
-    a.HD = (int)HD; a.H = p->H;
+    a.HD = p->H * p->D; a.H = p->H;
     a.beta = p->beta; a.log_a = p->log_a; a.A_log = p->A_log;
     return launch_gemm<gdn::kEpiInProj>(a, s);
 }
 
-gdn_status out_proj(const gdn_out_proj_params *p, hipStream_t s) {
+gdn_status out_proj_check(const gdn_out_proj_params *p) {
     if (!p || p->B < 1 || p->T < 1 || p->H < 1 || p->D < 1 || p->C < 1) return GDN_ERR_INVALID_ARG;
     if (!p->y || !p->w_out || !p->out) return GDN_ERR_INVALID_ARG;
     const double M = (double)p->B * p->T, HD = (double)p->H * p->D;
@@ -112,14 +117,115 @@ gdn_status out_proj(const gdn_out_proj_params *p, hipStream_t s) {
     const Span ins[] = {span(p->y, m * hd * 2), span(p->w_out, c * hd * 2), span(p->b_out, p->b_out ? c * 4 : 0)};
     const Span outs[] = {span(p->out, m * c * 2)};
     if (!disjoint(ins, outs)) return GDN_ERR_INVALID_ARG;
+    return GDN_OK;
+}
 
+gdn_status out_proj_launch(const gdn_out_proj_params *p, hipStream_t s) {
     gdn::GemmArgs a = {};
-    a.M = (int)M; a.N = p->C; a.K = (int)HD;
+    a.M = p->B * p->T; a.N = p->C; a.K = p->H * p->D;
     a.x = static_cast<const bf16 *>(p->y);
     a.w = static_cast<const bf16 *>(p->w_out);
     a.bias = p->b_out;
     a.out = static_cast<bf16 *>(p->out);
     return launch_gemm<gdn::kEpiPlain>(a, s);
+}
+
+// ------------------------------------------------------------------ mixer
+constexpr size_t kWsAlign = 256;
+size_t round_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+struct MixerParts {
+    gdn_in_proj_params in;
+    gdn_fwd_params layer;
+    gdn_out_proj_params out;
+    size_t total;  // workspace bytes
+};
+
+// The three stages' params with the intermediates carved from the workspace
+// (q, k, v, gate, y as [B, T, H, D] bf16, b and log a as [B, T, H] fp32, then
+// the layer's own workspace).  sizes_only: leave every pointer NULL.
+bool mixer_parts(const gdn_mixer_params *p, MixerParts &mp, bool sizes_only) {
+    if (!p || p->B < 1 || p->T < 1 || p->H < 1 || p->D < 1 || p->C < 1) return false;
+    const size_t m = (size_t)p->B * p->T, hd = (size_t)p->H * p->D, h = p->H;
+    if ((double)m * hd > 4.0e12) return false;
+    mp = MixerParts{};
+    gdn_fwd_params &L = mp.layer;
+    L.B = p->B; L.T = p->T; L.H = p->H; L.Dk = p->D; L.Dv = p->D; L.io_dtype = GDN_BF16;
+    const size_t layer_ws = gdn_fwd_workspace_bytes(&L);
+    if (layer_ws == 0) return false;
+    size_t off[8], o = 0;
+    for (int i = 0; i < 5; ++i) { off[i] = o; o += round_up(m * hd * 2); }   // q k v gate y
+    for (int i = 5; i < 7; ++i) { off[i] = o; o += round_up(m * h * 4); }    // b, log a
+    off[7] = o;
+    mp.total = o + layer_ws;
+    char *ws = sizes_only ? nullptr : static_cast<char *>(p->workspace);
+    auto at = [&](int i) -> void * { return ws ? ws + off[i] : nullptr; };
+
+    gdn_in_proj_params &I = mp.in;
+    I.B = p->B; I.T = p->T; I.H = p->H; I.D = p->D; I.C = p->C;
+    I.x = p->x; I.w_in = p->w_in; I.b_in = p->b_in; I.A_log = p->A_log;
+    I.q = at(0); I.k = at(1); I.v = at(2); I.gate = at(3);
+    I.beta = static_cast<float *>(at(5)); I.log_a = static_cast<float *>(at(6));
+
+    L.q = at(0); L.k = at(1); L.v = at(2); L.gate = at(3);
+    L.beta = static_cast<const float *>(at(5)); L.log_a = static_cast<const float *>(at(6));
+    L.conv_q = p->conv_q; L.conv_k = p->conv_k; L.conv_v = p->conv_v;
+    L.norm_w = p->norm_w; L.eps_l2 = p->eps_l2; L.eps_norm = p->eps_norm;
+    L.S0 = p->S0; L.S_T = p->S_T; L.o = at(4); L.reverse = 0;
+    L.workspace = at(7); L.workspace_bytes = ws ? p->workspace_bytes - off[7] : 0;
+
+    gdn_out_proj_params &O = mp.out;
+    O.B = p->B; O.T = p->T; O.H = p->H; O.D = p->D; O.C = p->C;
+    O.y = at(4); O.w_out = p->w_out; O.b_out = p->b_out; O.out = p->out;
+    return true;
+}
+
+gdn_status mixer_call(const gdn_mixer_params *p, hipEvent_t *timing, int n_timing, hipStream_t s) {
+    MixerParts mp;
+    if (!mixer_parts(p, mp, true)) return GDN_ERR_INVALID_ARG;
+    if (!p->workspace || p->workspace_bytes < mp.total) return GDN_ERR_WORKSPACE;
+    if (!aligned(p->workspace, kWsAlign)) return GDN_ERR_ALIGNMENT;
+    mixer_parts(p, mp, false);
+    // the caller's buffers must not overlap the workspace
+    const size_t m = (size_t)p->B * p->T, hd = (size_t)p->H * p->D, n = 4 * hd + 2 * p->H, c = p->C;
+    const Span ws[] = {span(p->workspace, mp.total)};
+    const size_t hh = p->H, dd = p->D;
+    const Span user[] = {span(p->x, m * c * 2),          span(p->w_in, n * c * 2),
+                         span(p->w_out, c * hd * 2),     span(p->out, m * c * 2),
+                         span(p->b_in, p->b_in ? n * 4 : 0), span(p->b_out, p->b_out ? c * 4 : 0),
+                         span(p->A_log, hh * 4),         span(p->conv_q, hd * 16),
+                         span(p->conv_k, hd * 16),       span(p->conv_v, hd * 16),
+                         span(p->norm_w, p->norm_w ? hd * 4 : 0),
+                         span(p->S0, p->S0 ? (size_t)p->B * hh * dd * dd * 4 : 0),
+                         span(p->S_T, p->S_T ? (size_t)p->B * hh * dd * dd * 4 : 0)};
+    if (!disjoint(user, ws)) return GDN_ERR_INVALID_ARG;
+    // the mixer's outputs must not overlap any of its inputs or each other
+    const Span ins[] = {user[0], user[1], user[2], user[4], user[5], user[6], user[7], user[8], user[9], user[10],
+                        user[11]};
+    const Span outs[] = {user[3], user[12]};
+    if (!disjoint(ins, outs)) return GDN_ERR_INVALID_ARG;
+    // every check of the three stages before the first launch
+    gdn_status st = in_proj_check(&mp.in);
+    if (st == GDN_OK) st = gdn_internal::fwd_check(&mp.layer);
+    if (st == GDN_OK) st = out_proj_check(&mp.out);
+    if (st != GDN_OK) return st;
+    int n_layer = 0;
+    if (timing) {
+        n_layer = gdn_fwd_launch_count(&mp.layer, 0);
+        if (n_layer < 0 || n_timing < 4 + 2 * n_layer) return GDN_ERR_INVALID_ARG;
+    }
+    auto rec = [&](int i) { return !timing || hipEventRecord(timing[i], s) == hipSuccess; };
+    if (!rec(0)) return GDN_ERR_HIP;
+    st = in_proj_launch(&mp.in, s);
+    if (st != GDN_OK) return st;
+    if (!rec(1)) return GDN_ERR_HIP;
+    st = gdn_internal::fwd_call(&mp.layer, timing ? timing + 4 : nullptr, timing ? n_timing - 4 : 0, s);
+    if (st != GDN_OK) return st;
+    if (!rec(2)) return GDN_ERR_HIP;
+    st = out_proj_launch(&mp.out, s);
+    if (st != GDN_OK) return st;
+    if (!rec(3)) return GDN_ERR_HIP;
+    return GDN_OK;
 }
 
 }  // namespace
@@ -128,7 +234,8 @@ extern "C" {
 
 gdn_status gdn_in_proj(const gdn_in_proj_params *p, struct ihipStream_t *stream) {
     try {
-        return in_proj(p, stream);
+        gdn_status st = in_proj_check(p);
+        return st != GDN_OK ? st : in_proj_launch(p, stream);
     } catch (...) {
         return GDN_ERR_HIP;
     }
@@ -136,7 +243,35 @@ gdn_status gdn_in_proj(const gdn_in_proj_params *p, struct ihipStream_t *stream)
 
 gdn_status gdn_out_proj(const gdn_out_proj_params *p, struct ihipStream_t *stream) {
     try {
-        return out_proj(p, stream);
+        gdn_status st = out_proj_check(p);
+        return st != GDN_OK ? st : out_proj_launch(p, stream);
+    } catch (...) {
+        return GDN_ERR_HIP;
+    }
+}
+
+size_t gdn_mixer_workspace_bytes(const gdn_mixer_params *p) {
+    try {
+        MixerParts mp;
+        return mixer_parts(p, mp, true) ? mp.total : 0;
+    } catch (...) {
+        return 0;
+    }
+}
+
+gdn_status gdn_mixer_fwd(const gdn_mixer_params *p, struct ihipStream_t *stream) {
+    try {
+        return mixer_call(p, nullptr, 0, stream);
+    } catch (...) {
+        return GDN_ERR_HIP;
+    }
+}
+
+gdn_status gdn_mixer_fwd_timed(const gdn_mixer_params *p, struct ihipEvent_t **events, int n_events,
+                               struct ihipStream_t *stream) {
+    if (!events) return GDN_ERR_INVALID_ARG;
+    try {
+        return mixer_call(p, reinterpret_cast<hipEvent_t *>(events), n_events, stream);
     } catch (...) {
         return GDN_ERR_HIP;
     }

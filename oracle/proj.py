@@ -74,3 +74,17 @@ def out_proj(y, w_out, b_out=None):
     y = np.asarray(y, np.float64)
     B, T, H, D = y.shape
     return linear(y.reshape(B * T, H * D), w_out, b_out).reshape(B, T, -1)
+
+
+def mixer(x, w_in, b_in, A_log, conv_q, conv_k, conv_v, norm_w, w_out, b_out, H, D, S0=None,
+          eps_l2=1e-6, eps_norm=1e-6, threads=0):
+    """The whole token mixer: in_proj, the GDN layer (the C oracle, forward
+    scan), out_proj.  The layer oracle takes its inputs as float32 (it is
+    built for the exact values a device receives), so the projection outputs
+    are rounded to float32 at that boundary, a relative change of at most
+    2^-24.  Returns (out [B, T, C], S_T [B, H, D, D], y [B, T, H, D]), fp64."""
+    from oracle import gdn_fwd
+    q, k, v, g, beta, log_a = in_proj(x, w_in, b_in, A_log, H, D)
+    y, S_T, _ = gdn_fwd(q, k, v, log_a, beta, g, conv_q, conv_k, conv_v, norm_w, S0, eps_l2, eps_norm,
+                        threads=threads)
+    return out_proj(y, w_out, b_out), S_T, y

@@ -34,7 +34,7 @@ def lib():
 
 def test_every_declared_function_is_exported_and_bound(lib):
     decl = declared_functions()
-    assert len(decl) == 10, decl
+    assert len(decl) == 13, decl
     assert set(decl) == set(gdn.EXPORTS)
     for name in decl:
         fn = getattr(lib, name)  # AttributeError if the library does not export it
@@ -213,3 +213,57 @@ def test_projection_params_null():
     lib = gdn.load()
     assert lib.gdn_in_proj(None, None) == gdn.GDN_ERR_INVALID_ARG
     assert lib.gdn_out_proj(None, None) == gdn.GDN_ERR_INVALID_ARG
+
+
+def fake_mixer(lib, B=1, T=300, H=3, D=64, C=192):
+    p = gdn.GdnMixerParams()
+    p.B, p.T, p.H, p.D, p.C = B, T, H, D, C
+    base, step = 1 << 44, 1 << 36
+    names = ["x", "w_in", "b_in", "A_log", "conv_q", "conv_k", "conv_v", "norm_w", "S0", "S_T", "w_out", "b_out",
+             "out", "workspace"]
+    for i, nm in enumerate(names):
+        setattr(p, nm, base + i * step)
+    p.eps_l2 = p.eps_norm = 1e-6
+    p.workspace_bytes = lib.gdn_mixer_workspace_bytes(ctypes.byref(p))
+    return p
+
+
+def test_mixer_workspace_bytes(lib):
+    B, T, H, D, C = 1, 32760, 12, 128, 1536
+    need = gdn.gdn_mixer_workspace_bytes(B, T, H, D, C)
+    inter = 5 * B * T * H * D * 2 + 2 * B * T * H * 4  # q, k, v, gate, y and b, log a
+    layer = gdn.gdn_fwd_workspace_bytes(B, T, H, D, gdn.GDN_BF16)
+    assert inter + layer <= need <= inter + layer + 8 * 256
+    assert gdn.gdn_mixer_workspace_bytes(0, T, H, D, C) == 0
+
+
+MIXER_CASES = [
+    ("x NULL", lambda p: setattr(p, "x", None), gdn.GDN_ERR_INVALID_ARG),
+    ("conv_k NULL", lambda p: setattr(p, "conv_k", None), gdn.GDN_ERR_INVALID_ARG),
+    ("w_out NULL", lambda p: setattr(p, "w_out", None), gdn.GDN_ERR_INVALID_ARG),
+    ("D = 96", lambda p: setattr(p, "D", 96), gdn.GDN_ERR_WORKSPACE),
+    ("C % 64 != 0", lambda p: setattr(p, "C", 160), gdn.GDN_ERR_UNSUPPORTED),
+    ("eps negative", lambda p: setattr(p, "eps_norm", -1.0), gdn.GDN_ERR_INVALID_ARG),
+    ("workspace NULL", lambda p: setattr(p, "workspace", None), gdn.GDN_ERR_WORKSPACE),
+    ("workspace small", lambda p: setattr(p, "workspace_bytes", p.workspace_bytes - 1), gdn.GDN_ERR_WORKSPACE),
+    ("workspace misaligned", lambda p: setattr(p, "workspace", p.workspace + 64), gdn.GDN_ERR_ALIGNMENT),
+    ("S0 inside the workspace", lambda p: setattr(p, "S0", p.workspace + 1024), gdn.GDN_ERR_INVALID_ARG),
+    ("out over x", lambda p: setattr(p, "out", p.x + 512), gdn.GDN_ERR_INVALID_ARG),
+    ("S_T over w_out", lambda p: setattr(p, "S_T", p.w_out), gdn.GDN_ERR_INVALID_ARG),
+    ("S_T over out", lambda p: setattr(p, "S_T", p.out + 4096), gdn.GDN_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("name,mutate,expect", MIXER_CASES, ids=[c[0] for c in MIXER_CASES])
+def test_mixer_validation(lib, name, mutate, expect):
+    p = fake_mixer(lib)
+    mutate(p)
+    assert lib.gdn_mixer_fwd(ctypes.byref(p), None) == expect, name
+
+
+def test_mixer_timed_needs_events(lib):
+    p = fake_mixer(lib)
+    assert lib.gdn_mixer_fwd_timed(ctypes.byref(p), None, 0, None) == gdn.GDN_ERR_INVALID_ARG
+    n = lib.gdn_fwd_launch_count(ctypes.byref(gdn._sizes(1, 300, 3, 64, gdn.GDN_BF16)), 0)
+    events = (ctypes.c_void_p * (3 + 2 * n))()
+    assert lib.gdn_mixer_fwd_timed(ctypes.byref(p), events, 3 + 2 * n, None) == gdn.GDN_ERR_INVALID_ARG

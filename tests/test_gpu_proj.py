@@ -171,3 +171,46 @@ def test_in_proj_errors_leave_outputs_untouched():
     torch.cuda.synchronize()
     for t in (q, k, v, g, beta, log_a):
         assert bool(torch.all(t == 7.0))
+
+
+def run_mixer(inp, H, D, S0=None):
+    B, T, C = inp["x"].shape
+    out = torch.full((B, T, C), float("nan"), dtype=torch.bfloat16, device="cuda")
+    S_T = torch.full((B, H, D, D), float("nan"), dtype=torch.float32, device="cuda")
+    gdn.gdn_mixer_fwd(_dev(inp["x"], torch.bfloat16), _dev(inp["w_in"], torch.bfloat16), _dev(inp["A_log"]),
+                      _dev(inp["conv_q"]), _dev(inp["conv_k"]), _dev(inp["conv_v"]),
+                      _dev(inp["w_out"], torch.bfloat16), H, D, b_in=_dev(inp["b_in"]), b_out=_dev(inp["b_out"]),
+                      norm_w=_dev(inp["norm_w"]), S0=_dev(S0), out=out, S_T=S_T)
+    torch.cuda.synchronize()
+    return out.double().cpu().numpy(), S_T.double().cpu().numpy()
+
+
+def compare_mixer(inp, H, D, S0=None):
+    got, s = run_mixer(inp, H, D, S0)
+    ref, rs, _ = oproj.mixer(inp["x"], inp["w_in"], inp["b_in"], inp["A_log"], inp["conv_q"], inp["conv_k"],
+                             inp["conv_v"], inp["norm_w"], inp["w_out"], inp["b_out"], H, D, S0=S0)
+    assert np.all(np.isfinite(got)) and np.all(np.isfinite(s))
+    e, es = rel_l2(got, ref), rel_l2(s, rs)
+    rows = np.linalg.norm(got - ref, axis=-1) / np.maximum(np.linalg.norm(ref, axis=-1), 1e-30)
+    say(f"  mixer out rel-L2 {e:.3e}, S_T rel-L2 {es:.3e}, worst token row {rows.max():.3e} (bar 1e-2)")
+    assert e <= 1e-2 and es <= 1e-2 and rows.max() <= 5e-2
+
+
+@pytest.mark.parametrize("T", [700, 1, 65])
+def test_mixer_small(T):
+    """The whole mixer (in_proj, layer, out_proj) at H = 3, d = 64, C = 192,
+    with a random initial state and norm weight."""
+    w = MW[0]
+    inp = gdn_inputs.generate_mixer(w, T=T, seed=90 + T)
+    inp["norm_w"] = (1 + 0.3 * np.random.default_rng(T).standard_normal((w.H, w.D))).astype(np.float32)
+    S0 = (0.05 * np.random.default_rng(T + 1).standard_normal((1, w.H, w.D, w.D))).astype(np.float32)
+    say(f"case: mixer {w.name} T={T}")
+    compare_mixer(inp, w.H, w.D, S0)
+
+
+def test_mixer_full_size():
+    """The 1.3B model's token mixer at T = 32760 (the configuration the
+    benchmark's mixer line times), every token against the oracle."""
+    w = MW[1]
+    say(f"case: mixer full size {w.name}")
+    compare_mixer(gdn_inputs.generate_mixer(w), w.H, w.D)

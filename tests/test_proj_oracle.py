@@ -199,3 +199,31 @@ def test_projection_mutant_is_caught(name):
         except Exception:  # an assertion or a crash both count as caught
             failed.append(pin.__name__)
     assert failed, f"mutant '{name}' passed every pin"
+
+
+def test_mixer_oracle_composition():
+    """The mixer oracle hands the projections' outputs to the layer oracle and
+    the layer's output to the output projection: with an identity output
+    weight (C = H D) and no output bias its output is the layer's y; with
+    b = sigmoid(-800) = 0 (no writes) the final state is S0 decayed by
+    exp(sum log a) (the closed form of the delta rule without updates)."""
+    import gdn_inputs
+    import oracle
+    H, D = 2, 8
+    w = gdn_inputs.MixerWorkload(99, "tiny", 1, 23, H, D, H * D)
+    inp = gdn_inputs.generate_mixer(w, seed=3)
+    C = H * D
+    N = 4 * C + 2 * H
+    inp["b_in"][4 * C:4 * C + H] = -800.0
+    inp["w_in"][4 * C:4 * C + H] = 0.0
+    S0 = np.random.default_rng(1).normal(size=(1, H, D, D))
+    out, S_T, y = proj_module.mixer(inp["x"], inp["w_in"], inp["b_in"], inp["A_log"], inp["conv_q"],
+                                    inp["conv_k"], inp["conv_v"], inp["norm_w"], np.eye(C), None, H, D, S0=S0)
+    assert out.shape == (1, 23, C) and N == inp["w_in"].shape[0]
+    np.testing.assert_array_equal(out, y.reshape(1, 23, C))
+    q, k, v, g, beta, log_a = proj_module.in_proj(inp["x"], inp["w_in"], inp["b_in"], inp["A_log"], H, D)
+    y2, _, _ = oracle.gdn_fwd(q, k, v, log_a, beta, g, inp["conv_q"], inp["conv_k"], inp["conv_v"],
+                              inp["norm_w"], S0)
+    np.testing.assert_array_equal(y, y2)
+    decay = np.exp(np.sum(log_a.astype(np.float32).astype(np.float64)[0], axis=0))  # [H]
+    np.testing.assert_allclose(S_T[0], decay[:, None, None] * S0.astype(np.float32)[0], rtol=1e-6)
