@@ -196,7 +196,7 @@ gdn_status gdn_in_proj(const gdn_in_proj_params *p, struct ihipStream_t *stream)
  *   w_out  [C, H*D]       bf16, 16-byte aligned
  *   b_out  [C]            float32, 16-byte aligned, or NULL
  *   out    [B, T, C]      bf16 output
- * Requirements: (H*D) % 64 == 0, C % 4 == 0, B*T*H*D and C*H*D below 2^31;
+ * Requirements: (H*D) % 64 == 0, C % 8 == 0, B*T*H*D and C*H*D below 2^31;
  * otherwise GDN_ERR_UNSUPPORTED.  Conventions as for gdn_in_proj.
  */
 typedef struct gdn_out_proj_params {

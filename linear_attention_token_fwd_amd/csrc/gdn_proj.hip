@@ -107,7 +107,7 @@ gdn_status out_proj_check(const gdn_out_proj_params *p) {
     if (!p || p->B < 1 || p->T < 1 || p->H < 1 || p->D < 1 || p->C < 1) return GDN_ERR_INVALID_ARG;
     if (!p->y || !p->w_out || !p->out) return GDN_ERR_INVALID_ARG;
     const double M = (double)p->B * p->T, HD = (double)p->H * p->D;
-    if ((long long)HD % 64 != 0 || p->C % 4 != 0 || M * HD > kMaxElems || (double)p->C * HD > kMaxElems ||
+    if ((long long)HD % 64 != 0 || p->C % 8 != 0 || M * HD > kMaxElems || (double)p->C * HD > kMaxElems ||
         M * p->C > 4.0e12)
         return GDN_ERR_UNSUPPORTED;
     const void *al16[] = {p->y, p->w_out, p->b_out, p->out};

@@ -15,8 +15,8 @@
 // W, 128 bytes each, 64 KB) are copied global -> LDS by direct-to-LDS loads
 // (16 B per lane, 8 rows x 128 B per load, so each row is one whole cache
 // line) into a ring of 2 stages: the copy of step s + 1 runs while step s is
-// multiplied.  In LDS the 16-byte chunks of a row are XOR-swizzled so that the
-// 16 rows of an MFMA fragment read fall on distinct banks.  Wave (wm, wn) owns
+// multiplied.  In LDS the 16-byte chunks of a row are XOR-swizzled by the row
+// so that the fragment reads are free of bank conflicts.  Wave (wm, wn) owns
 // the 128 x 128 sub-tile (8 x 8 MFMA tiles of 16 x 16) and reads each W
 // fragment from LDS while the MFMAs of the previous one run.
 //
@@ -38,7 +38,9 @@ constexpr int UNIT = 1024;     // bytes of one copy unit: 8 rows x 128 B
 constexpr int XU = BM / 8;     // X units per step
 constexpr int WU = BN / 8;     // W units per step
 constexpr int STAGE_BYTES = (XU + WU) * UNIT;     // 64 KB
-constexpr int LDS_BYTES = STAGES * STAGE_BYTES;   // 128 KB
+constexpr int EPI_LD = 272;     // bytes per staged output row (128 bf16 + 16 B pad)
+constexpr int EPI_WAVE = 128 * EPI_LD;            // one wave's 128 x 128 output block
+constexpr int LDS_BYTES = STAGES * STAGE_BYTES > 4 * EPI_WAVE ? STAGES * STAGE_BYTES : 4 * EPI_WAVE;  // 136 KB
 constexpr int THREADS = 256;
 constexpr int DMA_PER_WAVE = (XU + WU) / (THREADS / 64);  // 16
 constexpr int GROUP_M = 4;     // row tiles per group of the tile order
@@ -110,9 +112,10 @@ __global__ __launch_bounds__(gemm::THREADS, 1) void gdn_gemm_kernel(GemmArgs a) 
     // W), the 128 bytes k = 64 s .. 64 s + 63 of that row, as 64 units of 8
     // rows x 128 B; one direct-to-LDS load (16 B per lane) fills one unit, so
     // every row is read as one whole 128-byte line.  Lane L of a unit loads
-    // 16-byte chunk c = (L % 8) ^ sw of row L / 8, sw = (L / 8) ^ (unit % 2):
-    // chunk c of row r' of unit u sits in slot 8 r' + (c ^ r' ^ (u % 2)).
-    // The swizzle spreads the 16 rows of a fragment read over all LDS banks.
+    // 16-byte chunk c = (L % 8) ^ (L / 8) of row L / 8: chunk c of row r' sits
+    // in slot 8 r' + (c ^ r').  A 128-bit LDS read is served 8 lanes at a
+    // time, and the swizzle puts the 8 rows such a group reads (the same
+    // chunk of rows r' = 0..7) on 8 distinct 16-byte bank groups.
     // Waves 0, 1 copy the X units, waves 2, 3 the W units.  Rows past the end
     // read the last row (never stored).  Element offsets fit in 32 bits (the
     // host checks M K and N K).
@@ -124,7 +127,7 @@ __global__ __launch_bounds__(gemm::THREADS, 1) void gdn_gemm_kernel(GemmArgs a) 
         for (int b = 0; b < DMA_PER_WAVE; ++b) {
             const int u = w * DMA_PER_WAVE + b;  // unit of the step
             const int row = u < XU ? min(m0 + 8 * u + rr, a.M - 1) : min(n0 + 8 * (u - XU) + rr, a.N - 1);
-            off[b] = (unsigned)row * (unsigned)a.K + 8 * (chunk ^ (u & 1));
+            off[b] = (unsigned)row * (unsigned)a.K + 8 * chunk;
         }
     }
     auto issue = [&](int s) {
@@ -139,7 +142,7 @@ __global__ __launch_bounds__(gemm::THREADS, 1) void gdn_gemm_kernel(GemmArgs a) 
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
         const int rr = r & 7, hi = r >> 3;
-        fo[kb] = hi * UNIT + (8 * rr + ((4 * kb + g) ^ rr ^ hi)) * 16;
+        fo[kb] = hi * UNIT + (8 * rr + ((4 * kb + g) ^ rr)) * 16;
     }
 
     floatx4 acc[8][8];
@@ -155,59 +158,61 @@ __global__ __launch_bounds__(gemm::THREADS, 1) void gdn_gemm_kernel(GemmArgs a) 
     // step s, reading each W fragment while the MFMAs of the previous one run.
     const int S = a.K / BK;
     issue(0);
-    frag xf[8], wf[2];
+    // A step is 16 groups (kb, i) of 8 MFMAs sharing W fragment (kb, i) and
+    // the 8 X fragments of kb.  W fragments are read two groups ahead, the X
+    // fragments of kb = 1 during the second half of kb = 0.
+    frag xf[2][8], wf[3];
     for (int s = 0; s < S; ++s) {
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         lds_barrier();
         if (s + 1 < S) issue(s + 1);
         const unsigned char *buf = smem + (s % STAGES) * STAGE_BYTES;
+        auto wfrag = [&](int q) {  // W fragment of group q = 8 kb + i
+            return *reinterpret_cast<const frag *>(buf + 2 * (XU / 2 + 8 * wn + (q & 7)) * UNIT + fo[q >> 3]);
+        };
+        auto xfrag = [&](int kb, int j) {
+            return *reinterpret_cast<const frag *>(buf + 2 * (8 * wm + j) * UNIT + fo[kb]);
+        };
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int j = 0; j < 8; ++j) xf[0][j] = xfrag(0, j);
+        wf[0] = wfrag(0);
+        wf[1] = wfrag(1);
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                xf[j] = *reinterpret_cast<const frag *>(buf + 2 * (8 * wm + j) * UNIT + fo[kb]);
-            wf[0] = *reinterpret_cast<const frag *>(buf + 2 * (XU / 2 + 8 * wn) * UNIT + fo[kb]);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                if (i + 1 < 8)
-                    wf[(i + 1) & 1] = *reinterpret_cast<const frag *>(buf + 2 * (XU / 2 + 8 * wn + i + 1) * UNIT + fo[kb]);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) acc[i][j] = Mf::mma(wf[i & 1], xf[j], acc[i][j]);
-                __builtin_amdgcn_sched_barrier(0);
+        for (int q = 0; q < 16; ++q) {
+            if (q + 2 < 16) wf[(q + 2) % 3] = wfrag(q + 2);
+            if (q >= 4 && q < 8) {
+                xf[1][2 * (q - 4)] = xfrag(1, 2 * (q - 4));
+                xf[1][2 * (q - 4) + 1] = xfrag(1, 2 * (q - 4) + 1);
             }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[q & 7][j] = Mf::mma(wf[q % 3], xf[q >> 3][j], acc[q & 7][j]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
-    // acc[i][j]: lane (r, g) holds out[m0 + 128 wm + 16 j + r][n0 + 128 wn + 16 i + 4g .. +3].
-    // A 16-column tile never straddles two of q, k, v, gate (H D % 16 == 0),
-    // so the destination of tile i is the same for the whole wave.
-    const int row0 = m0 + 128 * wm + r;
+    // Epilogue.  acc[i][j]: lane (r, g) holds out[m0 + 128 wm + 16 j + r][n0 +
+    // 128 wn + 16 i + 4g .. +3].  The in-projection's gate columns (past
+    // 4 H D) go out from registers, element by element; every other value,
+    // bias added, is staged as bf16 in LDS (each wave its own 128 x 128 block,
+    // rows padded to 272 B) and stored from there as 16-byte pieces of whole
+    // 256-byte row segments.
+    const int row0 = m0 + 128 * wm, col0 = n0 + 128 * wn;
+    const int ncols = EPI == kEpiPlain ? a.N : min(a.N, 4 * a.HD);  // columns staged and stored from LDS
+    if (EPI == kEpiInProj) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int tcol = n0 + 128 * wn + 16 * i;  // wave-uniform
-        if (tcol >= a.N) break;
-        const int col = tcol + 4 * g;
-        bf16 *dst;
-        size_t ld;
-        if (EPI == kEpiPlain) {
-            dst = a.out + col;
-            ld = a.N;
-        } else if (tcol < 4 * a.HD) {
-            const int part = __builtin_amdgcn_readfirstlane(tcol / a.HD);
-            bf16 *base = part == 0 ? a.dst[0] : part == 1 ? a.dst[1] : part == 2 ? a.dst[2] : a.dst[3];
-            dst = base + (col - part * a.HD);
-            ld = a.HD;
-        } else {
-            // the gate columns: b = sigmoid(z), log a = -exp(A_h) softplus(z)
+        for (int i = 0; i < 8; ++i) {
+            const int tcol = col0 + 16 * i;  // wave-uniform
+            if (tcol + 16 <= 4 * a.HD || tcol >= a.N) continue;
+            const int col = tcol + 4 * g;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int row = row0 + 16 * j;
+                const int row = row0 + 16 * j + r;
                 if (row >= a.M) break;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int jj = col + e - 4 * a.HD;
-                    if (jj >= 2 * a.H) break;
+                    if (jj < 0 || jj >= 2 * a.H) continue;
                     const float z = acc[i][j][e] + (a.bias ? a.bias[col + e] : 0.f);
                     if (jj < a.H)
                         a.beta[(size_t)row * a.H + jj] = sigmoid_f(z);
@@ -215,14 +220,48 @@ __global__ __launch_bounds__(gemm::THREADS, 1) void gdn_gemm_kernel(GemmArgs a) 
                         a.log_a[(size_t)row * a.H + (jj - a.H)] = -expf(a.A_log[jj - a.H]) * softplus_f(z);
                 }
             }
-            continue;
         }
-        if (col >= a.N) continue;
-        floatx4 bv = add_bias4(a.bias, col, zero4());
+    }
+    lds_barrier();  // every wave is done with the operand stages
+    unsigned char *stage = smem + w * EPI_WAVE;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int col = col0 + 16 * i + 4 * g;
+        const floatx4 bv = col + 4 <= ncols ? add_bias4(a.bias, col, zero4()) : zero4();
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int row = row0 + 16 * j;
-            if (row < a.M) store_bf16x4(dst + (size_t)row * ld, acc[i][j] + bv);
+            const floatx4 v = acc[i][j] + bv;
+            bf16x4 o = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+            *reinterpret_cast<bf16x4 *>(stage + (16 * j + r) * EPI_LD + (16 * i + 4 * g) * 2) = o;
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(kLgkm0);  // this wave's block is in LDS (only this wave reads it)
+    // 16 lanes per row, 8 columns (16 B) each, 4 rows per pass
+    const int lr = lane / 16, lc = 8 * (lane % 16);
+    const int col = col0 + lc;
+    if (col < ncols) {
+        bf16 *dst;
+        size_t ld;
+        if (EPI == kEpiPlain) {
+            dst = a.out + col;
+            ld = a.N;
+        } else {
+            const int part = col / a.HD;
+            bf16 *base = part == 0 ? a.dst[0] : part == 1 ? a.dst[1] : part == 2 ? a.dst[2] : a.dst[3];
+            dst = base + (col - part * a.HD);
+            ld = a.HD;
+        }
+        const bool full = col + 8 <= ncols;  // else 4 columns (ncols % 4 == 0)
+#pragma unroll 4
+        for (int pass = 0; pass < 32; ++pass) {
+            const int rr = 4 * pass + lr;
+            const int row = row0 + rr;
+            if (row >= a.M) break;
+            const unsigned char *src = stage + rr * EPI_LD + lc * 2;
+            if (full)
+                *reinterpret_cast<bf16x8 *>(dst + (size_t)row * ld) = *reinterpret_cast<const bf16x8 *>(src);
+            else
+                *reinterpret_cast<bf16x4 *>(dst + (size_t)row * ld) = *reinterpret_cast<const bf16x4 *>(src);
         }
     }
 }

@@ -195,7 +195,7 @@ OUT_PROJ_CASES = [
     ("out NULL", lambda p: setattr(p, "out", None), gdn.GDN_ERR_INVALID_ARG),
     ("C = 0", lambda p: setattr(p, "C", 0), gdn.GDN_ERR_INVALID_ARG),
     ("H D % 64 != 0", lambda p: setattr(p, "D", 48), gdn.GDN_ERR_UNSUPPORTED),
-    ("C % 4 != 0", lambda p: setattr(p, "C", 190), gdn.GDN_ERR_UNSUPPORTED),
+    ("C % 8 != 0", lambda p: setattr(p, "C", 196), gdn.GDN_ERR_UNSUPPORTED),
     ("w_out misaligned", lambda p: setattr(p, "w_out", p.w_out + 2), gdn.GDN_ERR_ALIGNMENT),
     ("out over y", lambda p: setattr(p, "out", p.y + 16), gdn.GDN_ERR_INVALID_ARG),
     ("out over w_out", lambda p: setattr(p, "out", p.w_out), gdn.GDN_ERR_INVALID_ARG),
