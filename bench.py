@@ -67,25 +67,26 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "linear_attention_token_fwd_amd", "csrc")
 
 
-KERNEL_SOURCES = ("frag.hpp", "sync.hpp", "kernels.hpp")
+KERNEL_SOURCES = ("frag.hpp", "sync.hpp", "kernels.hpp")        # the layer's kernels
+MIXER_SOURCES = KERNEL_SOURCES + ("gemm.hpp",)                   # + the projection GEMM
 
 
-def csrc_hash() -> str:
+def csrc_hash(sources=KERNEL_SOURCES) -> str:
     """sha256 over the kernel sources (device code only), to tell whether a
     stored profile still describes the kernels being run."""
     import hashlib
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in sources:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
-def profiled_traffic(kernel: str, workload_tag: str):
+def profiled_traffic(kernel: str, stem: str, sources=KERNEL_SOURCES):
     """HBM bytes per dispatch of `kernel` from the committed rocprofv3 summary
-    (FETCH_SIZE + WRITE_SIZE counters, copy-calibrated), or None if there is
-    none or it was taken on different kernel sources."""
-    path = os.path.join(HERE, "profiles", f"gdn_kernels_{workload_tag}.txt")
+    profiles/<stem>.txt (FETCH_SIZE + WRITE_SIZE counters, copy-calibrated),
+    or None if there is none or it was taken on different kernel sources."""
+    path = os.path.join(HERE, "profiles", f"{stem}.txt")
     if not os.path.exists(path):
         return None
     src, val = None, None
@@ -95,7 +96,7 @@ def profiled_traffic(kernel: str, workload_tag: str):
                 src = line.split(":", 1)[1].strip()
             if line.startswith(f"traffic_bytes[{kernel}]:"):
                 val = float(line.split(":", 1)[1])
-    return val if src == csrc_hash() else None
+    return val if src == csrc_hash(sources) else None
 
 
 class HipEvents:
@@ -254,7 +255,7 @@ def main() -> int:
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_call"])
     kd = kernels[dom]
     tag = f"T{T}_H{H}_d{D}_{w.dtype}" + ("_bidir" if w.bidirectional else "")
-    traffic = profiled_traffic(dom, tag)
+    traffic = profiled_traffic(dom, f"gdn_kernels_{tag}")
     achieved = kd["bytes_per_launch"] / (kd["avg_ms"] * 1e-3) / 1e9  # algorithmic bytes per launch / avg launch
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -413,14 +414,16 @@ def run_mixer(args) -> int:
     kd = kernels[dom]
     if dom in flops:
         achieved = kd["flops_per_launch"] / (kd["avg_ms"] * 1e-3) / 1e12
+        traffic = profiled_traffic(kd["kernel"], f"gdn_mixer_T{T}_C{C}_H{H}_d{D}_bf16", MIXER_SOURCES)
         roofline = {"kernel": kd["kernel"], "bound": "mfma", "achieved": round(achieved, 1),
                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                    "traffic": None, "avg_launch_ms": round(kd["avg_ms"], 5)}
+                    "traffic": None if traffic is None else round(traffic), "avg_launch_ms": round(kd["avg_ms"], 5)}
     else:
         achieved = kd["bytes_per_launch"] / (kd["avg_ms"] * 1e-3) / 1e9
+        traffic = profiled_traffic(dom, f"gdn_mixer_T{T}_C{C}_H{H}_d{D}_bf16", MIXER_SOURCES)
         roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                    "avg_launch_ms": round(kd["avg_ms"], 5)}
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": None if traffic is None else round(traffic), "avg_launch_ms": round(kd["avg_ms"], 5)}
 
     cpu, parity = None, None
     if not args.no_cpu_baseline:
