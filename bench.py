@@ -136,6 +136,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=1, help="workload id (default 1: T=32760 H=12 d=128)")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="batch rows B (default: the workload's own, 1); e.g. 2 for a classifier-free-guidance pair")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: all available)")
     ap.add_argument("--mixer", action="store_true",
@@ -173,7 +175,7 @@ def main() -> int:
     w = gdn_inputs.WORKLOADS[args.workload]
     log(f"workload {w.id}: {w.name}")
     t0 = time.time()
-    inp = gdn_inputs.generate(w)
+    inp = gdn_inputs.generate(w, B=args.batch or None)
     log(f"inputs generated in {time.time() - t0:.1f} s")
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     d = gdn.to_device(inp, dtype=dt)
@@ -254,7 +256,7 @@ def main() -> int:
                        "GBps": bytes_per_call / (call_ms * 1e-3) / 1e9}
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_call"])
     kd = kernels[dom]
-    tag = f"T{T}_H{H}_d{D}_{w.dtype}" + ("_bidir" if w.bidirectional else "")
+    tag = f"T{T}_H{H}_d{D}_{w.dtype}" + ("_bidir" if w.bidirectional else "") + (f"_B{B}" if B > 1 else "")
     traffic = profiled_traffic(dom, f"gdn_kernels_{tag}")
     achieved = kd["bytes_per_launch"] / (kd["avg_ms"] * 1e-3) / 1e9  # algorithmic bytes per launch / avg launch
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
@@ -308,7 +310,8 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "B": B, "T": T, "H": H, "d": D, "chunk": 64,
+        "config": {"workload": w.name + (f", run as a batch of B={B}" if B != w.B else ""), "B": B, "T": T, "H": H,
+                   "d": D, "chunk": 64,
                    "bidirectional": w.bidirectional},
         "roofline": roofline,
         "layer": layer,

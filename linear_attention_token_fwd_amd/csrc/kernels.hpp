@@ -583,6 +583,10 @@ __global__ __launch_bounds__((StateCfg<T, D>::THREADS)) void gdn_state_kernel(St
     // blocks of one head share an XCD's L2 for the head's chunk records
     int p;
     if (!xcd_position(blockIdx.x, a.B * a.H * NV, gridDim.x, p)) return;
+    // The chain is the critical path of the whole call and shares its CUs
+    // with prep and output workgroups: its waves win the instruction issue
+    // arbitration on their SIMDs (measured: 0.795 -> 0.776 ms per call).
+    __builtin_amdgcn_s_setprio(3);
     const int vb = p % NV;
     const size_t bh = p / NV;
     const int tid = threadIdx.x, lane = tid % 64, n = lane % 16, g = lane / 16;

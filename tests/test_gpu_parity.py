@@ -30,6 +30,12 @@ def test_full_workload(wid):
     compare_workload(W[wid])
 
 
+def test_cfg_pair_batch():
+    """A classifier-free-guidance pair as one call: B = 2 at the full
+    480x832 length (T = 32760, H = 12, d = 128), every head of both rows."""
+    compare_workload(W[1], B=2, seed=4242)
+
+
 @pytest.mark.parametrize("wid", [0, 1])
 @pytest.mark.parametrize("T", [1, 2, 3, 4, 63, 64, 65, 129])
 def test_edge_lengths(wid, T):
