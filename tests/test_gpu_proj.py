@@ -214,3 +214,12 @@ def test_mixer_full_size():
     w = MW[1]
     say(f"case: mixer full size {w.name}")
     compare_mixer(gdn_inputs.generate_mixer(w), w.H, w.D)
+
+
+def test_mixer_batch_d128_no_bias():
+    """The mixer with two batch rows, heads of 128 and no biases (H = 2,
+    C = 256, T = 130: a ragged last chunk and a ragged row tile)."""
+    w = gdn_inputs.MixerWorkload(98, "B2 T130 H2 d128 C256", 2, 130, 2, 128, 256)
+    inp = gdn_inputs.generate_mixer(w, bias=False, seed=31)
+    say(f"case: mixer {w.name}, no bias")
+    compare_mixer(inp, w.H, w.D)
