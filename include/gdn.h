@@ -124,6 +124,25 @@ gdn_status gdn_fwd_bidir(const gdn_fwd_params *p, float *S_T_rev,
                          struct ihipStream_t *stream);
 
 /*
+ * Variable-length batch: p->B sequences of different lengths packed along
+ * the token axis, each its own scan with its own initial and final state
+ * (classifier-free-guidance pairs of equal length can also use gdn_fwd with
+ * B = 2).  cu_seqlens is a HOST array of p->B + 1 ints: cu_seqlens[0] = 0,
+ * sequence b is token rows cu_seqlens[b] .. cu_seqlens[b+1] - 1, every length
+ * >= 1 (else GDN_ERR_INVALID_ARG).  The table is read during the call and
+ * copied into the workspace on `stream`; the caller may release it when the
+ * call returns.  p->T is ignored (the library uses the longest length).
+ * Layouts: q, k, v, gate, o [total, H, D] and log_a, beta [total, H] with
+ * total = cu_seqlens[p->B]; S0, S_T [p->B, H, Dv, Dk].  Everything else
+ * (dtypes, supported sizes, reverse, errors, execution) is as for gdn_fwd;
+ * the workspace is gdn_fwd_varlen_workspace_bytes(p, cu_seqlens) bytes (0 for
+ * an invalid table).  Each sequence's result equals gdn_fwd on that sequence
+ * alone.
+ */
+size_t gdn_fwd_varlen_workspace_bytes(const gdn_fwd_params *p, const int *cu_seqlens);
+gdn_status gdn_fwd_varlen(const gdn_fwd_params *p, const int *cu_seqlens, struct ihipStream_t *stream);
+
+/*
  * Measurement aids.  A call is a fixed sequence of kernel launches (a range
  * of chunks per launch, spread over the streams above);
  * gdn_fwd_launch_count() says how many (bidirectional != 0 for

@@ -19,7 +19,8 @@ GDN_F32, GDN_BF16 = 0, 1
 
 EXPORTS = ("gdn_fwd", "gdn_fwd_bidir", "gdn_fwd_workspace_bytes", "gdn_fwd_bidir_workspace_bytes",
            "gdn_fwd_launch_count", "gdn_fwd_launch_name", "gdn_fwd_timed", "gdn_status_string",
-           "gdn_in_proj", "gdn_out_proj", "gdn_mixer_workspace_bytes", "gdn_mixer_fwd", "gdn_mixer_fwd_timed")
+           "gdn_in_proj", "gdn_out_proj", "gdn_mixer_workspace_bytes", "gdn_mixer_fwd", "gdn_mixer_fwd_timed",
+           "gdn_fwd_varlen", "gdn_fwd_varlen_workspace_bytes")
 
 
 class GdnFwdParams(ctypes.Structure):
@@ -100,6 +101,11 @@ def load(path: str | None = None):
     lib.gdn_fwd_timed.argtypes = [P, ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_void_p),
                                   ctypes.c_int, ctypes.c_void_p]
     lib.gdn_fwd_timed.restype = ctypes.c_int
+    IP = ctypes.POINTER(ctypes.c_int)
+    lib.gdn_fwd_varlen.argtypes = [P, IP, ctypes.c_void_p]
+    lib.gdn_fwd_varlen.restype = ctypes.c_int
+    lib.gdn_fwd_varlen_workspace_bytes.argtypes = [P, IP]
+    lib.gdn_fwd_varlen_workspace_bytes.restype = ctypes.c_size_t
     lib.gdn_in_proj.argtypes = [ctypes.POINTER(GdnInProjParams), ctypes.c_void_p]
     lib.gdn_in_proj.restype = ctypes.c_int
     lib.gdn_out_proj.argtypes = [ctypes.POINTER(GdnOutProjParams), ctypes.c_void_p]
@@ -374,4 +380,47 @@ def gdn_mixer_fwd(x, w_in, A_log, conv_q, conv_k, conv_v, w_out, H, D, b_in=None
     st = load().gdn_mixer_fwd(ctypes.byref(p), ctypes.c_void_p(s))
     if st != GDN_OK:
         raise GdnError(st, "gdn_mixer_fwd")
+    return out, S_T
+
+
+def seq_table(cu_seqlens):
+    """A ctypes int array of the sequence offsets (host memory)."""
+    vals = [int(x) for x in cu_seqlens]
+    return (ctypes.c_int * len(vals))(*vals)
+
+
+def gdn_fwd_varlen_workspace_bytes(cu_seqlens, H: int, D: int, io_dtype: int = GDN_BF16) -> int:
+    cu = seq_table(cu_seqlens)
+    return load().gdn_fwd_varlen_workspace_bytes(ctypes.byref(_sizes(len(cu) - 1, 0, H, D, io_dtype)), cu)
+
+
+def gdn_fwd_varlen(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, cu_seqlens, norm_w=None, S0=None,
+                   eps_l2=1e-6, eps_norm=1e-6, reverse=False, out=None, S_T=None, want_state=True,
+                   workspace=None, stream=None):
+    """A variable-length batch: q, k, v, gate [1, total, H, D], log_a, beta
+    [1, total, H], sequences at token rows cu_seqlens[b] .. cu_seqlens[b+1]-1
+    (a host sequence of ints), S0 / S_T [N, H, D, D].  Returns (out, S_T)."""
+    import torch
+    lib = load()
+    cu = seq_table(cu_seqlens)
+    N = len(cu) - 1
+    out = _prepare(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, None, out, None)
+    _, total, H, D = q.shape
+    if q.shape[0] != 1:
+        raise ValueError("q must be [1, total, H, D] (sequences packed along the token axis)")
+    _check(S0, "S0", torch.float32, (N, H, D, D))
+    _check(S_T, "S_T", torch.float32, (N, H, D, D))
+    if S_T is None and want_state:
+        S_T = torch.empty((N, H, D, D), dtype=torch.float32, device=q.device)
+    io = GDN_BF16 if q.dtype == torch.bfloat16 else GDN_F32
+    if workspace is None:
+        need = lib.gdn_fwd_varlen_workspace_bytes(ctypes.byref(_sizes(N, 0, H, D, io)), cu)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    p = make_params(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, out, S_T, workspace,
+                    eps_l2, eps_norm, reverse)
+    p.B = N
+    s = (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
+    st = lib.gdn_fwd_varlen(ctypes.byref(p), cu, ctypes.c_void_p(s))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_fwd_varlen")
     return out, S_T

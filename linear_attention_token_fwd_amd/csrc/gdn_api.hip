@@ -24,15 +24,17 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
     // per scan: chunk records, e^{g_C}, chunk-entry states, two state hand-off buffers;
     // then, for two scans, one fp32 accumulator for the sum of their outputs
-    size_t rec, gC, sc, smid, per_scan, acc, total;  // byte offsets within a scan's block, sizes
+    // then, for variable-length batches, the device copy of the sequence table
+    size_t rec, gC, sc, smid, per_scan, acc, seq, total;  // byte offsets within a scan's block, sizes
 };
 
 int n_chunks(int T) { return (T + gdn::kChunk - 1) / gdn::kChunk; }
 
 size_t elem_size(gdn_dtype d) { return d == GDN_BF16 ? 2 : 4; }
 
-// scans = number of scans whose buffers are alive at once (1 or 2)
-Layout layout(const gdn_fwd_params *p, int scans) {
+// scans = number of scans whose buffers are alive at once (1 or 2); varlen:
+// room for a sequence table of B + 1 ints
+Layout layout(const gdn_fwd_params *p, int scans, bool varlen = false) {
     const size_t B = p->B, T = p->T, H = p->H, D = p->Dk, NC = n_chunks(p->T), es = elem_size(p->io_dtype);
     Layout L;
     size_t off = 0;
@@ -46,7 +48,8 @@ Layout layout(const gdn_fwd_params *p, int scans) {
     off += 2 * round_up(B * H * D * D * sizeof(float));
     L.per_scan = off;
     L.acc = scans * off;
-    L.total = L.acc + (scans == 2 ? round_up(B * T * H * D * sizeof(float)) : 0);
+    L.seq = L.acc + (scans == 2 ? round_up(B * T * H * D * sizeof(float)) : 0);
+    L.total = L.seq + (varlen ? round_up((B + 1) * sizeof(int)) : 0);
     return L;
 }
 
@@ -74,7 +77,9 @@ Range rng(const void *ptr, size_t bytes) { return Range{(uintptr_t)ptr, (uintptr
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
 bool aligned(const void *ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
 
-gdn_status validate(const gdn_fwd_params *p, const float *S_T_rev, int scans) {
+// tokens: rows of the per-token tensors (B T, or the packed total of a
+// variable-length batch, which also needs the sequence table's room)
+gdn_status validate(const gdn_fwd_params *p, const float *S_T_rev, int scans, size_t tokens, bool varlen) {
     if (!sizes_ok(p)) return GDN_ERR_INVALID_ARG;
     if (!p->q || !p->k || !p->v || !p->log_a || !p->beta || !p->gate || !p->conv_q || !p->conv_k ||
         !p->conv_v || !p->o)
@@ -84,8 +89,8 @@ gdn_status validate(const gdn_fwd_params *p, const float *S_T_rev, int scans) {
     if (p->reverse != 0 && p->reverse != 1) return GDN_ERR_INVALID_ARG;
     if (!supported(p)) return GDN_ERR_UNSUPPORTED;
     const size_t es = elem_size(p->io_dtype);
-    const size_t B = p->B, T = p->T, H = p->H, D = p->Dk;
-    const size_t tok = B * T * H;
+    const size_t B = p->B, H = p->H, D = p->Dk;
+    const size_t tok = tokens * H;
     const void *vec16[] = {p->q, p->k, p->v, p->gate, p->o, p->conv_q, p->conv_k, p->conv_v,
                            p->S0, p->S_T, S_T_rev};
     for (const void *ptr : vec16)
@@ -93,7 +98,7 @@ gdn_status validate(const gdn_fwd_params *p, const float *S_T_rev, int scans) {
     const void *vec4[] = {p->log_a, p->beta, p->norm_w};
     for (const void *ptr : vec4)
         if (ptr && !aligned(ptr, 4)) return GDN_ERR_ALIGNMENT;
-    const Layout L = layout(p, scans);
+    const Layout L = layout(p, scans, varlen);
     if (!p->workspace || p->workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
     if (!aligned(p->workspace, kAlign)) return GDN_ERR_ALIGNMENT;
     // outputs must not overlap any input, the workspace or each other
@@ -250,9 +255,10 @@ ScanBufs scan_bufs(const gdn_fwd_params *p, const Layout &L, int scan) {
 }
 
 template <class T, int D>
-gdn::PrepArgs prep_args(const gdn_fwd_params *p, int reverse, const ScanBufs &sb, int c_begin) {
+gdn::PrepArgs prep_args(const gdn_fwd_params *p, int reverse, const ScanBufs &sb, int c_begin, const int *cu) {
     gdn::PrepArgs pa;
     pa.B = p->B; pa.T = p->T; pa.H = p->H; pa.NC = n_chunks(p->T); pa.reverse = reverse;
+    pa.cu = cu;
     pa.c_begin = c_begin;
     pa.q = p->q; pa.k = p->k; pa.v = p->v;
     pa.log_a = p->log_a; pa.beta = p->beta;
@@ -265,19 +271,22 @@ gdn::PrepArgs prep_args(const gdn_fwd_params *p, int reverse, const ScanBufs &sb
 
 template <class T, int D>
 gdn::StateArgs state_args(const gdn_fwd_params *p, const ScanBufs &sb, int c0, int c1, const float *S_in,
-                          float *S_out) {
+                          float *S_out, float *S_T, const int *cu) {
     gdn::StateArgs sa;
     sa.B = p->B; sa.T = p->T; sa.H = p->H; sa.NC = n_chunks(p->T);
+    sa.cu = cu;
     sa.c_begin = c0; sa.c_end = c1;
     sa.rec = sb.rec; sa.gC = sb.gC;
-    sa.S_in = S_in; sa.S_out = S_out; sa.sc = sb.sc;
+    sa.S_in = S_in; sa.S_out = S_out; sa.S_T = S_T; sa.sc = sb.sc;
     return sa;
 }
 
 template <class T, int D>
-gdn::OutArgs out_args(const gdn_fwd_params *p, int reverse, const ScanBufs &sb, int c0, int mode, float *acc) {
+gdn::OutArgs out_args(const gdn_fwd_params *p, int reverse, const ScanBufs &sb, int c0, int mode, float *acc,
+                      const int *cu) {
     gdn::OutArgs oa;
     oa.B = p->B; oa.T = p->T; oa.H = p->H; oa.NC = n_chunks(p->T); oa.reverse = reverse;
+    oa.cu = cu;
     oa.c_begin = c0; oa.mode = mode;
     oa.rec = sb.rec; oa.sc = sb.sc;
     oa.gate = p->gate; oa.norm_w = p->norm_w; oa.eps = p->eps_norm;
@@ -287,10 +296,11 @@ gdn::OutArgs out_args(const gdn_fwd_params *p, int reverse, const ScanBufs &sb, 
 
 // One scan's range-pipelined launches: preps on `prep_stream`, the state
 // chain on `state_stream` (range i waits for prep i), and the output of each
-// range on `out_stream` (waits for state i).  out_mode: see OutArgs.
+// range on `out_stream` (waits for state i).  out_mode: see OutArgs.  cu: the
+// device copy of the sequence table of a variable-length batch, or null.
 template <class T, int D>
 void plan_scan(Plan &plan, const gdn_fwd_params *p, int reverse, const ScanBufs &sb, float *S_T, int prep_stream,
-               int state_stream, int out_stream, int out_mode, float *acc) {
+               int state_stream, int out_stream, int out_mode, float *acc, const int *cu) {
     const int NC = n_chunks(p->T), R = n_ranges(NC);
     const void *prep = reinterpret_cast<const void *>(&gdn::gdn_prep_kernel<T, D>);
     const void *state = reinterpret_cast<const void *>(&gdn::gdn_state_kernel<T, D>);
@@ -299,51 +309,52 @@ void plan_scan(Plan &plan, const gdn_fwd_params *p, int reverse, const ScanBufs 
     for (int i = 0; i < R; ++i) {
         const int c0 = range_begin(NC, R, i), c1 = range_begin(NC, R, i + 1);
         plan.launch(prep_stream, "gdn_prep_kernel", prep, dim3(c1 - c0, p->H, p->B), dim3(gdn::kThreads),
-                    sizeof(gdn::PrepSmem<T, D>), prep_args<T, D>(p, reverse, sb, c0));
+                    sizeof(gdn::PrepSmem<T, D>), prep_args<T, D>(p, reverse, sb, c0, cu));
         prep_done[i] = plan.record(prep_stream);
     }
     const int used = p->B * p->H * (D / 16);
     for (int i = 0; i < R; ++i) {
         const int c0 = range_begin(NC, R, i), c1 = range_begin(NC, R, i + 1);
+        // a sequence that ends in range i writes S_T; the others hand over through smid
         const float *S_in = i == 0 ? p->S0 : sb.smid[(i - 1) & 1];
-        float *S_out = i == R - 1 ? S_T : sb.smid[i & 1];
+        float *S_out = i == R - 1 ? nullptr : sb.smid[i & 1];
         plan.wait(state_stream, prep_done[i]);
         plan.launch(state_stream, "gdn_state_kernel", state, dim3((used + 7) / 8 * 8), dim3(gdn::StateCfg<T, D>::THREADS),
-                    state_lds<T, D>(), state_args<T, D>(p, sb, c0, c1, S_in, S_out));
+                    state_lds<T, D>(), state_args<T, D>(p, sb, c0, c1, S_in, S_out, S_T, cu));
         state_done[i] = plan.record(state_stream);
     }
     for (int i = 0; i < R; ++i) {
         const int c0 = range_begin(NC, R, i), c1 = range_begin(NC, R, i + 1);
         plan.wait(out_stream, state_done[i]);
         plan.launch(out_stream, "gdn_out_kernel", out, dim3(c1 - c0, p->H, p->B), dim3(gdn::kThreads),
-                    sizeof(gdn::OutSmem<T, D>), out_args<T, D>(p, reverse, sb, c0, out_mode, acc));
+                    sizeof(gdn::OutSmem<T, D>), out_args<T, D>(p, reverse, sb, c0, out_mode, acc, cu));
     }
 }
 
 template <class T, int D>
-gdn_status plan_fwd(Plan &plan, const gdn_fwd_params *p, float *S_T_rev, bool bidir) {
-    const Layout L = layout(p, bidir ? 2 : 1);
+gdn_status plan_fwd(Plan &plan, const gdn_fwd_params *p, float *S_T_rev, bool bidir, const int *cu) {
+    const Layout L = layout(p, bidir ? 2 : 1, cu != nullptr);
     const int start = plan.record(0);
     for (int s = 1; s < kStreams; ++s) plan.wait(s, start);
     if (!bidir) {
-        plan_scan<T, D>(plan, p, p->reverse, scan_bufs(p, L, 0), p->S_T, 1, 0, 2, 0, nullptr);
+        plan_scan<T, D>(plan, p, p->reverse, scan_bufs(p, L, 0), p->S_T, 1, 0, 2, 0, nullptr, cu);
     } else {
         // the two directions are independent: forward chain on stream 0,
         // reversed chain on stream 3, all preps on stream 1; the outputs run
         // on stream 2, the reversed scan's after all of the forward scan's
         // (they add into its fp32 sum)
         float *acc = reinterpret_cast<float *>(static_cast<char *>(p->workspace) + L.acc);
-        plan_scan<T, D>(plan, p, 0, scan_bufs(p, L, 0), p->S_T, 1, 0, 2, 1, acc);
-        plan_scan<T, D>(plan, p, 1, scan_bufs(p, L, 1), S_T_rev, 1, 3, 2, 2, acc);
+        plan_scan<T, D>(plan, p, 0, scan_bufs(p, L, 0), p->S_T, 1, 0, 2, 1, acc, cu);
+        plan_scan<T, D>(plan, p, 1, scan_bufs(p, L, 1), S_T_rev, 1, 3, 2, 2, acc, cu);
     }
     for (int s = 1; s < kStreams; ++s) plan.wait(0, plan.record(s));
     return GDN_OK;
 }
 
-gdn_status make_plan(Plan &plan, const gdn_fwd_params *p, float *S_T_rev, bool bidir) {
-    if (p->io_dtype == GDN_BF16 && p->Dk == 128) return plan_fwd<bf16, 128>(plan, p, S_T_rev, bidir);
-    if (p->io_dtype == GDN_BF16 && p->Dk == 64) return plan_fwd<bf16, 64>(plan, p, S_T_rev, bidir);
-    if (p->io_dtype == GDN_F32 && p->Dk == 64) return plan_fwd<float, 64>(plan, p, S_T_rev, bidir);
+gdn_status make_plan(Plan &plan, const gdn_fwd_params *p, float *S_T_rev, bool bidir, const int *cu = nullptr) {
+    if (p->io_dtype == GDN_BF16 && p->Dk == 128) return plan_fwd<bf16, 128>(plan, p, S_T_rev, bidir, cu);
+    if (p->io_dtype == GDN_BF16 && p->Dk == 64) return plan_fwd<bf16, 64>(plan, p, S_T_rev, bidir, cu);
+    if (p->io_dtype == GDN_F32 && p->Dk == 64) return plan_fwd<float, 64>(plan, p, S_T_rev, bidir, cu);
     return GDN_ERR_UNSUPPORTED;
 }
 
@@ -375,7 +386,8 @@ gdn_status set_attributes() {
 
 gdn_status call(const gdn_fwd_params *p, float *S_T_rev, bool bidir, hipEvent_t *timing, int n_timing,
                 hipStream_t s) {
-    gdn_status st = validate(p, S_T_rev, bidir ? 2 : 1);
+    if (!sizes_ok(p)) return GDN_ERR_INVALID_ARG;
+    gdn_status st = validate(p, S_T_rev, bidir ? 2 : 1, (size_t)p->B * p->T, false);
     if (st != GDN_OK) return st;
     if (bidir && p->reverse != 0) return GDN_ERR_INVALID_ARG;
     Plan plan;
@@ -387,9 +399,57 @@ gdn_status call(const gdn_fwd_params *p, float *S_T_rev, bool bidir, hipEvent_t 
     return run_plan(plan, s, timing);
 }
 
+// Variable-length batch: p->B sequences packed along the token axis,
+// sequence b at rows cu[b] .. cu[b+1] - 1 (host table).  Returns the longest
+// length in *T_max, or an error for a malformed table.
+gdn_status check_seq_table(const gdn_fwd_params *p, const int *cu, int *T_max) {
+    if (!p || !cu || p->B < 1) return GDN_ERR_INVALID_ARG;
+    if (cu[0] != 0) return GDN_ERR_INVALID_ARG;
+    int longest = 0;
+    for (int b = 0; b < p->B; ++b) {
+        const long long len = (long long)cu[b + 1] - cu[b];
+        if (len < 1) return GDN_ERR_INVALID_ARG;  // lengths >= 1, offsets increasing
+        if (len > longest) longest = (int)len;
+    }
+    *T_max = longest;
+    return GDN_OK;
+}
+
+// The params of a variable-length call with T set to the longest length.
+gdn_status varlen_params(const gdn_fwd_params *p, const int *cu, gdn_fwd_params &q) {
+    int T_max = 0;
+    gdn_status st = check_seq_table(p, cu, &T_max);
+    if (st != GDN_OK) return st;
+    q = *p;
+    q.T = T_max;
+    return sizes_ok(&q) ? GDN_OK : GDN_ERR_INVALID_ARG;
+}
+
+gdn_status varlen_call(const gdn_fwd_params *p, const int *cu, hipStream_t s) {
+    gdn_fwd_params q;
+    gdn_status st = varlen_params(p, cu, q);
+    if (st != GDN_OK) return st;
+    st = validate(&q, nullptr, 1, (size_t)cu[q.B], true);
+    if (st != GDN_OK) return st;
+    const Layout L = layout(&q, 1, true);
+    int *cu_dev = reinterpret_cast<int *>(static_cast<char *>(q.workspace) + L.seq);
+    Plan plan;
+    st = make_plan(plan, &q, nullptr, false, cu_dev);
+    if (st != GDN_OK) return st;
+    st = set_attributes();
+    if (st != GDN_OK) return st;
+    // the table goes to the workspace first, on the caller's stream
+    if (hipMemcpyAsync(cu_dev, cu, sizeof(int) * (q.B + 1), hipMemcpyHostToDevice, s) != hipSuccess)
+        return GDN_ERR_HIP;
+    return run_plan(plan, s, nullptr);
+}
+
 }  // namespace
 
-gdn_status gdn_internal::fwd_check(const gdn_fwd_params *p) { return validate(p, nullptr, 1); }
+gdn_status gdn_internal::fwd_check(const gdn_fwd_params *p) {
+    if (!sizes_ok(p)) return GDN_ERR_INVALID_ARG;
+    return validate(p, nullptr, 1, (size_t)p->B * p->T, false);
+}
 
 gdn_status gdn_internal::fwd_call(const gdn_fwd_params *p, hipEvent_t *timing, int n_timing, hipStream_t s) {
     return call(p, nullptr, false, timing, n_timing, s);
@@ -418,6 +478,24 @@ gdn_status gdn_fwd(const gdn_fwd_params *p, struct ihipStream_t *stream) {
 gdn_status gdn_fwd_bidir(const gdn_fwd_params *p, float *S_T_rev, struct ihipStream_t *stream) {
     try {
         return call(p, S_T_rev, true, nullptr, 0, stream);
+    } catch (...) {
+        return GDN_ERR_HIP;
+    }
+}
+
+size_t gdn_fwd_varlen_workspace_bytes(const gdn_fwd_params *p, const int *cu_seqlens) {
+    try {
+        gdn_fwd_params q;
+        if (varlen_params(p, cu_seqlens, q) != GDN_OK) return 0;
+        return layout(&q, 1, true).total;
+    } catch (...) {
+        return 0;
+    }
+}
+
+gdn_status gdn_fwd_varlen(const gdn_fwd_params *p, const int *cu_seqlens, struct ihipStream_t *stream) {
+    try {
+        return varlen_call(p, cu_seqlens, stream);
     } catch (...) {
         return GDN_ERR_HIP;
     }

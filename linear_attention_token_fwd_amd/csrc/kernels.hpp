@@ -52,8 +52,26 @@ template <int D> struct Rec {
     static constexpr int SIZE = 320 * D;
 };
 
+// Sequences.  Without a table (cu == null) batch row b is a sequence of T
+// tokens starting at token row b T.  With one (variable-length batches) the
+// tokens of all sequences are packed, sequence b is rows cu[b] .. cu[b+1] - 1,
+// T is the longest length and NC = ceil(T / 64) chunks are reserved per
+// sequence in the workspace; chunks past a sequence's end do nothing.
+struct SeqSpan {
+    long long off;  // first token row
+    int len;        // tokens
+};
+__device__ __forceinline__ SeqSpan seq_span(const int *cu, int b, int T) {
+    if (cu) {
+        const int o = cu[b];
+        return SeqSpan{o, cu[b + 1] - o};
+    }
+    return SeqSpan{(long long)b * T, T};
+}
+
 struct PrepArgs {
     int B, T, H, NC, reverse;
+    const int *cu;  // sequence table [B + 1] or null
     int c_begin;  // first chunk of this launch (chunk = c_begin + blockIdx.x)
     const void *q, *k, *v;
     const float *log_a, *beta, *conv_q, *conv_k, *conv_v;
@@ -64,11 +82,13 @@ struct PrepArgs {
 
 struct StateArgs {
     int B, T, H, NC;
+    const int *cu;       // sequence table [B + 1] or null
     int c_begin, c_end;  // chunks [c_begin, c_end) of the scan
     const void *rec;
     const float *gC;
     const float *S_in;   // [B][H][D][D] state entering chunk c_begin, or null (zeros)
-    float *S_out;        // [B][H][D][D] state after chunk c_end - 1, or null
+    float *S_out;        // [B][H][D][D] state after chunk c_end - 1 (handed to the next range)
+    float *S_T;          // [B][H][D][D] final state of sequences that end in this range, or null
     void *sc;            // [B][H][NC][D/16 value blocks] chunk-entry S^T as B fragments
 };
 
@@ -83,6 +103,7 @@ template <class T, int D> struct ScLayout {
 
 struct OutArgs {
     int B, T, H, NC, reverse;
+    const int *cu;      // sequence table [B + 1] or null
     int c_begin;        // chunk = c_begin + blockIdx.x
     int mode;           // 0: write y; 1: write this scan's y to acc (fp32); 2: y = acc + this scan's y
     const void *rec;    // chunk records (QP, O0)
@@ -210,13 +231,13 @@ template <class T, int D> struct PrepSmem {
 };
 
 // Short conv + SiLU (+ L2 normalisation for q and k) of one thread's RUN
-// tokens x 8 channels from its raw rows; MASK: positions outside [0, T) are
-// zero history and tokens past T produce zeros.
+// tokens x 8 channels from its raw rows; MASK: positions outside [0, len) are
+// zero history and tokens past the sequence's end produce zeros.
 template <class T, int D, bool MASK>
 __device__ __forceinline__ void conv_silu_norm(const PrepArgs &a, const Raw8<T> (&raw)[3][64 / (kThreads / (D / 8)) + 3],
                                                const bool (&rv)[64 / (kThreads / (D / 8)) + 3],
                                                const float *const (&wsrc)[3], T *const (&dst)[3], int h, int s0,
-                                               int cg, int run) {
+                                               int cg, int run, int len) {
     constexpr int G = D / 8;
     constexpr int RUN = 64 / (kThreads / G);
     constexpr int ROWS = RUN + 3;
@@ -237,7 +258,7 @@ __device__ __forceinline__ void conv_silu_norm(const PrepArgs &a, const Raw8<T> 
             for (int i = 0; i < 8; ++i) xr[rr][i] = (!MASK || rv[rr]) ? raw[x][rr].get(i) : 0.f;
 #pragma unroll
         for (int r = 0; r < RUN; ++r) {
-            const bool valid = !MASK || s0 + r < a.T;
+            const bool valid = !MASK || s0 + r < len;
             float acc[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -269,7 +290,7 @@ __device__ __forceinline__ void conv_silu_norm(const PrepArgs &a, const Raw8<T> 
 // RUN + 3 input rows (3 rows of causal history) once, all loads issued before
 // any is used.
 template <class T, int D>
-__device__ __forceinline__ void prologue(const PrepArgs &a, PrepSmem<T, D> &sm, int c, int h, int b) {
+__device__ __forceinline__ void prologue(const PrepArgs &a, PrepSmem<T, D> &sm, int c, int h, SeqSpan sq) {
     constexpr int G = D / 8;
     constexpr int RUN = 64 / (kThreads / G);
     constexpr int ROWS = RUN + 3;
@@ -283,18 +304,18 @@ __device__ __forceinline__ void prologue(const PrepArgs &a, PrepSmem<T, D> &sm, 
 #pragma unroll
     for (int rr = 0; rr < ROWS; ++rr) {
         const int sp = s0 - 3 + rr;
-        rv[rr] = sp >= 0 && sp < a.T;
-        int si = a.reverse ? a.T - 1 - sp : sp;
-        si = si < 0 ? 0 : (si >= a.T ? a.T - 1 : si);
-        const size_t off = (((size_t)b * a.T + si) * a.H + h) * D + 8 * cg;
+        rv[rr] = sp >= 0 && sp < sq.len;
+        int si = a.reverse ? sq.len - 1 - sp : sp;
+        si = si < 0 ? 0 : (si >= sq.len ? sq.len - 1 : si);
+        const size_t off = (((size_t)sq.off + si) * a.H + h) * D + 8 * cg;
 #pragma unroll
         for (int x = 0; x < 3; ++x) raw[x][rr].load(src[x] + off);
     }
     // chunks away from both ends of the sequence need no masking
-    if (c > 0 && (c + 1) * 64 <= a.T)
-        conv_silu_norm<T, D, false>(a, raw, rv, wsrc, dst, h, s0, cg, run);
+    if (c > 0 && (c + 1) * 64 <= sq.len)
+        conv_silu_norm<T, D, false>(a, raw, rv, wsrc, dst, h, s0, cg, run, sq.len);
     else
-        conv_silu_norm<T, D, true>(a, raw, rv, wsrc, dst, h, s0, cg, run);
+        conv_silu_norm<T, D, true>(a, raw, rv, wsrc, dst, h, s0, cg, run, sq.len);
 }
 
 template <class T, int D>
@@ -313,15 +334,17 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_prep_kernel(PrepArgs a) {
     SM &sm = *reinterpret_cast<SM *>(smem_raw);
 
     const int c = a.c_begin + blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const SeqSpan sq = seq_span(a.cu, b, a.T);
+    if (c * 64 >= sq.len) return;  // past this sequence's end (variable lengths)
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, n = lane % 16, g = lane / 16;
 
     // ---- gates: b and the cumulative log decay g inside the chunk
     if (tid < 64) {
         const int s = c * 64 + tid;
-        const bool valid = s < a.T;
-        const int src = a.reverse ? a.T - 1 - s : s;
-        float la = valid ? a.log_a[((size_t)b * a.T + src) * a.H + h] : 0.f;
-        float be = valid ? a.beta[((size_t)b * a.T + src) * a.H + h] : 0.f;
+        const bool valid = s < sq.len;
+        const int src = a.reverse ? sq.len - 1 - s : s;
+        float la = valid ? a.log_a[((size_t)sq.off + src) * a.H + h] : 0.f;
+        float be = valid ? a.beta[((size_t)sq.off + src) * a.H + h] : 0.f;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             float y = __shfl_up(la, off, 64);
@@ -332,7 +355,7 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_prep_kernel(PrepArgs a) {
         sm.eg[tid] = expf(la);
         sm.dk[tid] = expf(__shfl(la, 63, 64) - la);
     }
-    prologue<T, D>(a, sm, c, h, b);
+    prologue<T, D>(a, sm, c, h, sq);
     __syncthreads();
 
     // ---- A = strictly lower (b_i e^{g_i - g_j} k_i . k_j), rows 16w.. of this wave
@@ -594,9 +617,13 @@ __global__ __launch_bounds__((StateCfg<T, D>::THREADS)) void gdn_state_kernel(St
     const int vcol = 16 * vb + n;
     const T *rec0 = static_cast<const T *>(a.rec) + bh * a.NC * (size_t)Rec<D>::SIZE;
     const int row0 = w * C::KQ;  // first key channel of this wave
+    // this sequence's chunks in the range (variable lengths: possibly none)
+    const int nc_seq = (seq_span(a.cu, (int)(bh / a.H), a.T).len + 63) / 64;
+    const int c_end = min(a.c_end, nc_seq);
+    if (a.c_begin >= c_end) return;
 
     // e^{g_C} of the range into LDS
-    for (int i = tid; i < a.c_end - a.c_begin; i += C::THREADS) sm.gcs[i] = a.gC[bh * a.NC + a.c_begin + i];
+    for (int i = tid; i < c_end - a.c_begin; i += C::THREADS) sm.gcs[i] = a.gC[bh * a.NC + a.c_begin + i];
 
     Ops ops[C::NB];
     auto load_ops = [&](Ops &o, int c) {
@@ -636,7 +663,7 @@ __global__ __launch_bounds__((StateCfg<T, D>::THREADS)) void gdn_state_kernel(St
         }
     }
 
-    const int last = a.c_end - 1;
+    const int last = c_end - 1;
 #pragma unroll
     for (int j = 0; j < C::NB; ++j) load_ops(ops[j], min(a.c_begin + j, last));
     lds_barrier();  // e^{g_C} staged
@@ -694,7 +721,7 @@ __global__ __launch_bounds__((StateCfg<T, D>::THREADS)) void gdn_state_kernel(St
     // whole groups of NB chunks (one back edge, so the loads in flight at the
     // top of the loop are the same on every entry), then the rest
     static_assert(C::NB == 4, "the loop below is written for four register sets");
-    const int n_ch = a.c_end - a.c_begin, full = n_ch / C::NB * C::NB;
+    const int n_ch = c_end - a.c_begin, full = n_ch / C::NB * C::NB;
     for (int c = a.c_begin; c < a.c_begin + full; c += C::NB) {
         step(ops[0], c);
         step(ops[1], c + 1);
@@ -705,10 +732,12 @@ __global__ __launch_bounds__((StateCfg<T, D>::THREADS)) void gdn_state_kernel(St
     if (rest > 0) step(ops[0], a.c_begin + full);
     if (rest > 1) step(ops[1], a.c_begin + full + 1);
     if (rest > 2) step(ops[2], a.c_begin + full + 2);
-    if (a.S_out) {
+    // the sequence's final state if it ends in this range, else the hand-off
+    float *S_dst = c_end == nc_seq ? a.S_T : a.S_out;
+    if (S_dst) {
 #pragma unroll
         for (int mt = 0; mt < MQ; ++mt)
-            *reinterpret_cast<floatx4 *>(a.S_out + (bh * D + vcol) * D + row0 + 16 * mt + 4 * g) = S[mt];
+            *reinterpret_cast<floatx4 *>(S_dst + (bh * D + vcol) * D + row0 + 16 * mt + 4 * g) = S[mt];
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
@@ -733,6 +762,8 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_out_kernel(OutArgs a) {
     SM &sm = *reinterpret_cast<SM *>(smem_raw);
 
     const int c = a.c_begin + blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const SeqSpan sq = seq_span(a.cu, b, a.T);
+    if (c * 64 >= sq.len) return;  // past this sequence's end (variable lengths)
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, n = lane % 16, g = lane / 16;
     const size_t bh = (size_t)b * a.H + h;
 
@@ -764,9 +795,9 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_out_kernel(OutArgs a) {
 #pragma unroll
     for (int pass = 0; pass < PASSES; ++pass) {
         const int s = c * 64 + pass * TPP + tid / G;
-        const int sc_ = s < a.T ? s : a.T - 1;
-        const int t = a.reverse ? a.T - 1 - sc_ : sc_;
-        roff[pass] = (((size_t)b * a.T + t) * a.H + h) * D + 8 * cg;
+        const int sc_ = s < sq.len ? s : sq.len - 1;
+        const int t = a.reverse ? sq.len - 1 - sc_ : sc_;
+        roff[pass] = (((size_t)sq.off + t) * a.H + h) * D + 8 * cg;
         load8(static_cast<const T *>(a.gate) + roff[pass], gv[pass]);
         if (a.mode == 2) load8(a.acc + roff[pass], prev[pass]);
     }
@@ -791,7 +822,7 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_out_kernel(OutArgs a) {
     for (int pass = 0; pass < PASSES; ++pass) {
         const int r = pass * TPP + tid / G;
         const int s = c * 64 + r;
-        const bool live = s < a.T;
+        const bool live = s < sq.len;
         const float *orow = sm.Os + r * SM::LDO + 8 * cg;
         float ov[8];
 #pragma unroll

@@ -34,7 +34,7 @@ def lib():
 
 def test_every_declared_function_is_exported_and_bound(lib):
     decl = declared_functions()
-    assert len(decl) == 13, decl
+    assert len(decl) == 15, decl
     assert set(decl) == set(gdn.EXPORTS)
     for name in decl:
         fn = getattr(lib, name)  # AttributeError if the library does not export it
@@ -267,3 +267,34 @@ def test_mixer_timed_needs_events(lib):
     n = lib.gdn_fwd_launch_count(ctypes.byref(gdn._sizes(1, 300, 3, 64, gdn.GDN_BF16)), 0)
     events = (ctypes.c_void_p * (3 + 2 * n))()
     assert lib.gdn_mixer_fwd_timed(ctypes.byref(p), events, 3 + 2 * n, None) == gdn.GDN_ERR_INVALID_ARG
+
+
+def test_varlen_workspace_and_table_checks(lib):
+    p = fake_params(lib, B=3, T=1, H=2, D=64)
+    good = gdn.seq_table([0, 5, 70, 200])
+    need = lib.gdn_fwd_varlen_workspace_bytes(ctypes.byref(p), good)
+    # as a batch of 3 rows of the longest length (130), plus the table
+    dense = gdn.gdn_fwd_workspace_bytes(3, 130, 2, 64, gdn.GDN_BF16)
+    assert dense < need <= dense + 256
+    for bad in ([1, 5, 70, 200], [0, 5, 5, 200], [0, 70, 5, 200]):
+        assert lib.gdn_fwd_varlen_workspace_bytes(ctypes.byref(p), gdn.seq_table(bad)) == 0
+    assert lib.gdn_fwd_varlen_workspace_bytes(ctypes.byref(p), None) == 0
+
+
+def test_varlen_validation(lib):
+    p = fake_params(lib, B=3, T=1, H=2, D=64)
+    cu = gdn.seq_table([0, 5, 70, 200])
+    p.workspace_bytes = lib.gdn_fwd_varlen_workspace_bytes(ctypes.byref(p), cu)
+    assert lib.gdn_fwd_varlen(ctypes.byref(p), None, None) == gdn.GDN_ERR_INVALID_ARG
+    assert lib.gdn_fwd_varlen(ctypes.byref(p), gdn.seq_table([0, 5, 4, 200]), None) == gdn.GDN_ERR_INVALID_ARG
+    small = fake_params(lib, B=3, T=1, H=2, D=64)
+    small.workspace_bytes = p.workspace_bytes - 1
+    assert lib.gdn_fwd_varlen(ctypes.byref(small), cu, None) == gdn.GDN_ERR_WORKSPACE
+    q = fake_params(lib, B=3, T=1, H=2, D=64)
+    q.workspace_bytes = p.workspace_bytes
+    q.o = q.q + 256  # output over an input
+    assert lib.gdn_fwd_varlen(ctypes.byref(q), cu, None) == gdn.GDN_ERR_INVALID_ARG
+    q = fake_params(lib, B=3, T=1, H=2, D=64)
+    q.Dk = q.Dv = 96
+    q.workspace_bytes = 1 << 30
+    assert lib.gdn_fwd_varlen(ctypes.byref(q), cu, None) == gdn.GDN_ERR_UNSUPPORTED

@@ -120,3 +120,77 @@ def test_errors_leave_outputs_untouched():
     assert e.value.status == gdn.GDN_ERR_WORKSPACE
     torch.cuda.synchronize()
     assert bool((out == 7.0).all())
+
+
+VARLEN_LENGTHS = [1, 63, 64, 65, 200, 7, 129, 3]
+
+
+def _varlen_inputs(w, lengths, seed):
+    """Sequences of the given lengths sharing the layer's weights, packed
+    along the token axis; each with its own random initial state."""
+    base = gdn_inputs.generate(w, T=max(lengths), H=3, seed=seed)
+    seqs = []
+    for i, L in enumerate(lengths):
+        d = gdn_inputs.generate(w, T=L, H=3, seed=seed + 1 + i)
+        for key in ("conv_q", "conv_k", "conv_v", "norm_w"):
+            d[key] = base[key]
+        d["S0"] = (0.05 * np.random.default_rng(seed + 100 + i).standard_normal((1, 3, w.D, w.D))).astype(np.float32)
+        seqs.append(d)
+    packed = {key: np.concatenate([d[key] for d in seqs], axis=1)
+              for key in ("q", "k", "v", "gate", "log_a", "beta")}
+    for key in ("conv_q", "conv_k", "conv_v", "norm_w"):
+        packed[key] = base[key]
+    packed["S0"] = np.concatenate([d["S0"] for d in seqs], axis=0)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).tolist()
+    return seqs, packed, cu
+
+
+@pytest.mark.parametrize("wid,reverse", [(0, False), (1, False), (1, True)])
+def test_varlen_batch(wid, reverse):
+    """Sequences of different lengths (inside the conv window, one chunk,
+    chunk boundaries, several chunks) in one call: every sequence against the
+    oracle on that sequence alone, and bit-identical to gdn_fwd on it."""
+    import linear_attention_token_fwd_amd as gdn
+    w = W[wid]
+    seqs, packed, cu = _varlen_inputs(w, VARLEN_LENGTHS, seed=500 + wid)
+    say(f"case: varlen workload {wid} lengths {VARLEN_LENGTHS} reverse={reverse}")
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    d = gdn.to_device(packed, dtype=dt)
+    total = cu[-1]
+    out = torch.full((1, total, 3, w.D), float("nan"), dtype=dt, device="cuda")
+    S_T = torch.full((len(seqs), 3, w.D, w.D), float("nan"), dtype=torch.float32, device="cuda")
+    gdn.gdn_fwd_varlen(d["q"], d["k"], d["v"], d["log_a"], d["beta"], d["gate"], d["conv_q"], d["conv_k"],
+                       d["conv_v"], cu, norm_w=d["norm_w"], S0=d["S0"], reverse=reverse, out=out, S_T=S_T)
+    torch.cuda.synchronize()
+    y = out.double().cpu().numpy()
+    s = S_T.double().cpu().numpy()
+    for i, seq in enumerate(seqs):
+        ys = y[:, cu[i]:cu[i + 1]]
+        ry, rs, _ = oracle.inputs_for(seq, reverse=reverse)
+        check(f"y[{i}] (T={VARLEN_LENGTHS[i]})", ys, ry, w.dtype)
+        check(f"S_T[{i}]", s[i:i + 1], rs, w.dtype)
+        y1, s1 = run_gpu(seq, w.dtype, reverse=reverse)
+        assert np.array_equal(ys, y1) and np.array_equal(s[i:i + 1], s1), f"sequence {i} differs from gdn_fwd alone"
+
+
+def test_varlen_long_and_short():
+    """Two sequences of very different lengths at the model's shape (d = 128,
+    12 heads): 4096 and 37 tokens."""
+    import linear_attention_token_fwd_amd as gdn
+    w = W[1]
+    lengths = [4096, 37]
+    base = gdn_inputs.generate(w, T=4096 + 37, seed=808)
+    cu = [0, 4096, 4133]
+    d = gdn.to_device(base, dtype=torch.bfloat16)
+    say(f"case: varlen lengths {lengths}, H=12")
+    out, S_T = gdn.gdn_fwd_varlen(d["q"], d["k"], d["v"], d["log_a"], d["beta"], d["gate"], d["conv_q"],
+                                  d["conv_k"], d["conv_v"], cu, norm_w=d["norm_w"])
+    torch.cuda.synchronize()
+    y = out.double().cpu().numpy()
+    s = S_T.double().cpu().numpy()
+    for i in range(2):
+        seq = {key: (val[:, cu[i]:cu[i + 1]] if key in ("q", "k", "v", "gate", "log_a", "beta") else val)
+               for key, val in base.items()}
+        ry, rs, _ = oracle.inputs_for(seq)
+        check(f"y[{i}]", y[:, cu[i]:cu[i + 1]], ry, "bf16")
+        check(f"S_T[{i}]", s[i:i + 1], rs, "bf16")
