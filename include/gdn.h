@@ -44,7 +44,12 @@
  * kept, default priority), which wait for `stream` at the start of the call
  * and which `stream` waits for at its end.  Calls from several host threads
  * are enqueued one at a time (a lock); their work may then share the library
- * streams.  Two in-flight calls must not share a workspace.
+ * streams.  Two in-flight calls must not share a workspace.  A call can be
+ * captured into a HIP graph on `stream` (the fork onto the library streams
+ * and the join back are captured with it; the first call on a device, which
+ * creates those streams and events, should run before capturing); a replay
+ * repeats the call exactly.  gdn_fwd_varlen copies its table from host
+ * memory and is not meant for capture.
  *
  * Errors.  All checks run on the host before anything is enqueued; on any
  * error nothing is launched and no output is touched.  Launch failures
