@@ -138,6 +138,8 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=1, help="workload id (default 1: T=32760 H=12 d=128)")
     ap.add_argument("--batch", type=int, default=0,
                     help="batch rows B (default: the workload's own, 1); e.g. 2 for a classifier-free-guidance pair")
+    ap.add_argument("--no-graph-cache", action="store_true",
+                    help="turn the library's launch-graph cache off: every call launches its kernels directly")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: all available)")
     ap.add_argument("--mixer", action="store_true",
@@ -170,6 +172,8 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "dispatches": 3}), flush=True)
         return 0
+    if args.no_graph_cache:
+        gdn.gdn_set_graph_cache_limit(0)
     if args.mixer:
         return run_mixer(args)
     w = gdn_inputs.WORKLOADS[args.workload]
@@ -310,7 +314,9 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": w.name + (f", run as a batch of B={B}" if B != w.B else ""), "B": B, "T": T, "H": H,
+        "config": {"workload": w.name + (f", run as a batch of B={B}" if B != w.B else ""),
+                   "launches": "direct" if args.no_graph_cache or w.bidirectional else "cached graph",
+                   "B": B, "T": T, "H": H,
                    "d": D, "chunk": 64,
                    "bidirectional": w.bidirectional},
         "roofline": roofline,
@@ -454,7 +460,8 @@ def run_mixer(args) -> int:
         "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w.name, "B": B, "T": T, "H": H, "d": D, "C": C, "chunk": 64},
+        "config": {"workload": w.name, "layer launches": "direct" if args.no_graph_cache else "cached graph",
+                   "B": B, "T": T, "H": H, "d": D, "C": C, "chunk": 64},
         "roofline": roofline,
         "kernels": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},

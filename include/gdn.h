@@ -51,6 +51,25 @@
  * repeats the call exactly.  gdn_fwd_varlen copies its table from host
  * memory and is not meant for capture.
  *
+ * Graph cache.  Outside a capture, on a stream other than the null stream,
+ * gdn_fwd, gdn_fwd_varlen and the layer stage of gdn_mixer_fwd record their
+ * launches as a HIP graph (a capture of `stream`, in thread-local mode,
+ * inside the call) the second time a call has the same launches (the same
+ * sizes, pointers and scalars; the first such call launches directly), and
+ * replay the graph for every later such call.  The result is the same as
+ * launching directly, bit for bit; the graph removes the gaps between
+ * dependent kernels on different streams.  Callers whose buffers move from
+ * call to call simply keep launching directly.  The library keeps the most
+ * recently used graphs per process (8 by default), each holding only the
+ * recorded launches, no memory of its own.  gdn_fwd_bidir, the timed calls
+ * and calls on the null stream or on a stream being captured always launch
+ * directly.
+ *   gdn_set_graph_cache_limit(n): keep at most n graphs (0 <= n <= 64;
+ *     0 turns the cache off and frees it); GDN_ERR_INVALID_ARG otherwise.
+ *     Graphs past the new limit are destroyed at once, so call it with no
+ *     library call in flight on any stream.
+ *   gdn_graph_cache_count(): the number of graphs held.
+ *
  * Errors.  All checks run on the host before anything is enqueued; on any
  * error nothing is launched and no output is touched.  Launch failures
  * return GDN_ERR_HIP.  Faults inside kernels surface at the caller's next
@@ -274,6 +293,11 @@ size_t gdn_mixer_workspace_bytes(const gdn_mixer_params *p);
 gdn_status gdn_mixer_fwd(const gdn_mixer_params *p, struct ihipStream_t *stream);
 gdn_status gdn_mixer_fwd_timed(const gdn_mixer_params *p, struct ihipEvent_t **events, int n_events,
                                struct ihipStream_t *stream);
+
+/* The graph cache of gdn_fwd, gdn_fwd_varlen and gdn_mixer_fwd (see "Graph
+ * cache" at the top of this header). */
+gdn_status gdn_set_graph_cache_limit(int max_graphs);
+int gdn_graph_cache_count(void);
 
 /* Static, human-readable text for a status code. */
 const char *gdn_status_string(gdn_status s);

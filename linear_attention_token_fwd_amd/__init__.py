@@ -20,7 +20,8 @@ GDN_F32, GDN_BF16 = 0, 1
 EXPORTS = ("gdn_fwd", "gdn_fwd_bidir", "gdn_fwd_workspace_bytes", "gdn_fwd_bidir_workspace_bytes",
            "gdn_fwd_launch_count", "gdn_fwd_launch_name", "gdn_fwd_timed", "gdn_status_string",
            "gdn_in_proj", "gdn_out_proj", "gdn_mixer_workspace_bytes", "gdn_mixer_fwd", "gdn_mixer_fwd_timed",
-           "gdn_fwd_varlen", "gdn_fwd_varlen_workspace_bytes")
+           "gdn_fwd_varlen", "gdn_fwd_varlen_workspace_bytes", "gdn_set_graph_cache_limit",
+           "gdn_graph_cache_count")
 
 
 class GdnFwdParams(ctypes.Structure):
@@ -119,6 +120,10 @@ def load(path: str | None = None):
     lib.gdn_mixer_fwd_timed.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_set_graph_cache_limit.argtypes = [ctypes.c_int]
+    lib.gdn_set_graph_cache_limit.restype = ctypes.c_int
+    lib.gdn_graph_cache_count.argtypes = []
+    lib.gdn_graph_cache_count.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -126,6 +131,18 @@ def load(path: str | None = None):
 
 def gdn_status_string(status: int) -> str:
     return load().gdn_status_string(int(status)).decode()
+
+
+def gdn_set_graph_cache_limit(max_graphs: int) -> None:
+    """Keep at most max_graphs recorded launch graphs (0 turns graphs off)."""
+    st = load().gdn_set_graph_cache_limit(int(max_graphs))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_set_graph_cache_limit")
+
+
+def gdn_graph_cache_count() -> int:
+    """The number of launch graphs the library holds."""
+    return int(load().gdn_graph_cache_count())
 
 
 def _sizes(B, T, H, D, dtype) -> GdnFwdParams:

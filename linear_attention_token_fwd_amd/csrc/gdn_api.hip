@@ -7,6 +7,7 @@
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <utility>
 #include <vector>
 
 #include "../../include/gdn.h"
@@ -154,7 +155,7 @@ struct Plan {
     template <class Args>
     void launch(int stream, const char *name, const void *fn, dim3 grid, dim3 block, size_t smem, const Args &a) {
         static_assert(sizeof(Args) <= sizeof(Launch::args), "kernel arguments too large");
-        Launch L;
+        Launch L = {};  // zero-filled: the argument bytes past sizeof(Args) take part in plan_key()
         L.fn = fn; L.grid = grid; L.block = block; L.smem = smem; L.name = name;
         memcpy(L.args, &a, sizeof(Args));
         ops.push_back(Op{Op::LAUNCH, stream, (int)launches.size()});
@@ -192,15 +193,9 @@ gdn_status device_res(int n_events, DeviceRes *&out) {
     return GDN_OK;
 }
 
-// timing: NULL, or 2 events per launch recorded right before and right after it
-gdn_status run_plan(const Plan &plan, hipStream_t caller, hipEvent_t *timing) {
-    std::lock_guard<std::mutex> lock(g_mutex);
-    DeviceRes *r = nullptr;
-    gdn_status st = device_res(plan.n_events, r);
-    if (st != GDN_OK) return st;
-    hipStream_t streams[kStreams];
-    streams[0] = caller;
-    for (int i = 1; i < kStreams; ++i) streams[i] = r->streams[i];
+// Enqueue the plan's operations (caller holds g_mutex).  timing: NULL, or 2
+// events per launch recorded right before and right after it.
+gdn_status enqueue_ops(const Plan &plan, const hipStream_t *streams, DeviceRes *r, hipEvent_t *timing) {
     for (const Op &op : plan.ops) {
         hipStream_t s = streams[op.stream];
         if (op.kind == Op::RECORD) {
@@ -216,6 +211,119 @@ gdn_status run_plan(const Plan &plan, hipStream_t caller, hipEvent_t *timing) {
         }
     }
     return GDN_OK;
+}
+
+// Graphs.  A plan can be recorded once as a HIP graph (capturing the caller's
+// stream, which forks onto the library streams through the plan's events and
+// joins back) and replayed for identical plans: one graph launch in place of
+// dozens of launches and event operations, which removes the gaps between
+// dependent kernels on different streams (measured 5-9% faster per call on
+// the single-scan workloads; the bidirectional plan runs faster directly).
+// Plans are identical when their operations and every launch's kernel, shape
+// and argument bytes (pointers included) are.  A plan is recorded the second
+// time it is seen (the first call runs directly), so callers whose buffers
+// move from call to call never pay for recording.  The most recently used
+// g_graph_limit graphs are kept per process (0: no graphs, every plan runs
+// directly), and the keys of the last kSeenPlans plans seen once.
+constexpr int kMaxCachedGraphs = 64;
+constexpr size_t kSeenPlans = 16;
+size_t g_graph_limit = 8;  // guarded by g_mutex, like the lists below
+struct CachedGraph {
+    int device;
+    std::vector<unsigned char> key;
+    hipGraphExec_t exec;
+};
+std::vector<CachedGraph> g_graphs;  // least recently used first
+std::vector<std::pair<int, std::vector<unsigned char>>> g_seen;  // oldest first
+
+// Caller holds g_mutex.  Destroys the least recently used graphs until at
+// most `keep` remain.
+void evict_graphs(size_t keep) {
+    while (g_graphs.size() > keep) {
+        (void)hipGraphExecDestroy(g_graphs.front().exec);
+        g_graphs.erase(g_graphs.begin());
+    }
+}
+
+std::vector<unsigned char> plan_key(const Plan &plan) {
+    std::vector<unsigned char> k;
+    auto put = [&](const void *p, size_t n) {
+        const unsigned char *b = static_cast<const unsigned char *>(p);
+        k.insert(k.end(), b, b + n);
+    };
+    for (const Op &op : plan.ops) {
+        const int v[3] = {(int)op.kind, op.stream, op.event};
+        put(v, sizeof(v));
+    }
+    for (const Launch &L : plan.launches) {
+        const unsigned g[6] = {L.grid.x, L.grid.y, L.grid.z, L.block.x, L.block.y, L.block.z};
+        put(&L.fn, sizeof(L.fn));
+        put(g, sizeof(g));
+        put(&L.smem, sizeof(L.smem));
+        put(L.args, sizeof(L.args));
+    }
+    return k;
+}
+
+// Caller holds g_mutex.  Replays the cached graph of this plan, or records,
+// caches and launches one; returns false (nothing enqueued) when a graph
+// cannot be used, and the plan then runs directly.
+bool launch_as_graph(const Plan &plan, const hipStream_t *streams, DeviceRes *r, gdn_status &st) {
+    hipStream_t caller = streams[0];
+    if (g_graph_limit == 0) return false;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (caller == nullptr || hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+        return false;  // the null stream cannot be captured; the caller's own capture records the plan itself
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return false;
+    std::vector<unsigned char> key = plan_key(plan);
+    for (size_t i = 0; i < g_graphs.size(); ++i) {
+        if (g_graphs[i].device != dev || g_graphs[i].key != key) continue;
+        CachedGraph hit = std::move(g_graphs[i]);
+        g_graphs.erase(g_graphs.begin() + i);
+        g_graphs.push_back(std::move(hit));
+        st = hipGraphLaunch(g_graphs.back().exec, caller) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+        return true;
+    }
+    bool seen = false;
+    for (size_t i = 0; i < g_seen.size() && !seen; ++i) {
+        if (g_seen[i].first != dev || g_seen[i].second != key) continue;
+        g_seen.erase(g_seen.begin() + i);
+        seen = true;
+    }
+    if (!seen) {  // first sighting: remember it and run directly
+        if (g_seen.size() >= kSeenPlans) g_seen.erase(g_seen.begin());
+        g_seen.emplace_back(dev, std::move(key));
+        return false;
+    }
+    if (hipStreamBeginCapture(caller, hipStreamCaptureModeThreadLocal) != hipSuccess) return false;
+    const gdn_status recorded = enqueue_ops(plan, streams, r, nullptr);
+    hipGraph_t graph = nullptr;
+    const hipError_t ended = hipStreamEndCapture(caller, &graph);
+    hipGraphExec_t exec = nullptr;
+    const bool ok = recorded == GDN_OK && ended == hipSuccess && graph &&
+                    hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) == hipSuccess;
+    if (graph) (void)hipGraphDestroy(graph);
+    if (!ok) return false;
+    evict_graphs(g_graph_limit - 1);
+    g_graphs.push_back(CachedGraph{dev, std::move(key), exec});
+    st = hipGraphLaunch(exec, caller) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    return true;
+}
+
+// timing: NULL, or 2 events per launch recorded right before and right after
+// it (timed plans always run directly).  as_graph: replay the plan as a
+// cached graph where possible.
+gdn_status run_plan(const Plan &plan, hipStream_t caller, hipEvent_t *timing, bool as_graph = false) {
+    std::lock_guard<std::mutex> lock(g_mutex);
+    DeviceRes *r = nullptr;
+    gdn_status st = device_res(plan.n_events, r);
+    if (st != GDN_OK) return st;
+    hipStream_t streams[kStreams];
+    streams[0] = caller;
+    for (int i = 1; i < kStreams; ++i) streams[i] = r->streams[i];
+    if (as_graph && !timing && launch_as_graph(plan, streams, r, st)) return st;
+    return enqueue_ops(plan, streams, r, timing);
 }
 
 // Chunk ranges of a scan: ~64 chunks each, at most 16 ranges unless a range
@@ -257,6 +365,7 @@ ScanBufs scan_bufs(const gdn_fwd_params *p, const Layout &L, int scan) {
 template <class T, int D>
 gdn::PrepArgs prep_args(const gdn_fwd_params *p, int reverse, const ScanBufs &sb, int c_begin, const int *cu) {
     gdn::PrepArgs pa;
+    memset(&pa, 0, sizeof(pa));  // padding too: the argument bytes key the graph cache
     pa.B = p->B; pa.T = p->T; pa.H = p->H; pa.NC = n_chunks(p->T); pa.reverse = reverse;
     pa.cu = cu;
     pa.c_begin = c_begin;
@@ -273,6 +382,7 @@ template <class T, int D>
 gdn::StateArgs state_args(const gdn_fwd_params *p, const ScanBufs &sb, int c0, int c1, const float *S_in,
                           float *S_out, float *S_T, const int *cu) {
     gdn::StateArgs sa;
+    memset(&sa, 0, sizeof(sa));  // padding too: the argument bytes key the graph cache
     sa.B = p->B; sa.T = p->T; sa.H = p->H; sa.NC = n_chunks(p->T);
     sa.cu = cu;
     sa.c_begin = c0; sa.c_end = c1;
@@ -285,6 +395,7 @@ template <class T, int D>
 gdn::OutArgs out_args(const gdn_fwd_params *p, int reverse, const ScanBufs &sb, int c0, int mode, float *acc,
                       const int *cu) {
     gdn::OutArgs oa;
+    memset(&oa, 0, sizeof(oa));  // padding too: the argument bytes key the graph cache
     oa.B = p->B; oa.T = p->T; oa.H = p->H; oa.NC = n_chunks(p->T); oa.reverse = reverse;
     oa.cu = cu;
     oa.c_begin = c0; oa.mode = mode;
@@ -396,7 +507,7 @@ gdn_status call(const gdn_fwd_params *p, float *S_T_rev, bool bidir, hipEvent_t 
     if (timing && n_timing < 2 * (int)plan.launches.size()) return GDN_ERR_INVALID_ARG;
     st = set_attributes();
     if (st != GDN_OK) return st;
-    return run_plan(plan, s, timing);
+    return run_plan(plan, s, timing, !bidir);
 }
 
 // Variable-length batch: p->B sequences packed along the token axis,
@@ -441,7 +552,7 @@ gdn_status varlen_call(const gdn_fwd_params *p, const int *cu, hipStream_t s) {
     // the table goes to the workspace first, on the caller's stream
     if (hipMemcpyAsync(cu_dev, cu, sizeof(int) * (q.B + 1), hipMemcpyHostToDevice, s) != hipSuccess)
         return GDN_ERR_HIP;
-    return run_plan(plan, s, nullptr);
+    return run_plan(plan, s, nullptr, true);
 }
 
 }  // namespace
@@ -544,6 +655,20 @@ const char *gdn_status_string(gdn_status s) {
     case GDN_ERR_HIP: return "HIP runtime or launch failure";
     }
     return "unknown status";
+}
+
+gdn_status gdn_set_graph_cache_limit(int max_graphs) {
+    if (max_graphs < 0 || max_graphs > kMaxCachedGraphs) return GDN_ERR_INVALID_ARG;
+    std::lock_guard<std::mutex> lock(g_mutex);
+    g_graph_limit = (size_t)max_graphs;
+    evict_graphs(g_graph_limit);
+    if (max_graphs == 0) g_seen.clear();
+    return GDN_OK;
+}
+
+int gdn_graph_cache_count(void) {
+    std::lock_guard<std::mutex> lock(g_mutex);
+    return (int)g_graphs.size();
 }
 
 }  // extern "C"

@@ -34,11 +34,11 @@ def lib():
 
 def test_every_declared_function_is_exported_and_bound(lib):
     decl = declared_functions()
-    assert len(decl) == 15, decl
+    assert len(decl) == 17, decl
     assert set(decl) == set(gdn.EXPORTS)
     for name in decl:
         fn = getattr(lib, name)  # AttributeError if the library does not export it
-        assert fn.argtypes, name  # bound by the binding
+        assert fn.argtypes is not None, name  # bound by the binding
 
 
 def test_missing_library_fails_loudly():
@@ -50,6 +50,16 @@ def test_status_strings(lib):
     texts = [lib.gdn_status_string(s).decode() for s in range(6)]
     assert all(texts) and len(set(texts)) == 6
     assert lib.gdn_status_string(99)  # unknown codes still get text
+
+
+def test_graph_cache_limit(lib):
+    assert lib.gdn_set_graph_cache_limit(-1) == gdn.GDN_ERR_INVALID_ARG
+    assert lib.gdn_set_graph_cache_limit(65) == gdn.GDN_ERR_INVALID_ARG
+    assert lib.gdn_set_graph_cache_limit(0) == gdn.GDN_OK
+    assert lib.gdn_set_graph_cache_limit(8) == gdn.GDN_OK
+    assert lib.gdn_graph_cache_count() == 0  # nothing is recorded without a device call
+    with pytest.raises(gdn.GdnError):
+        gdn.gdn_set_graph_cache_limit(100)
 
 
 BF16_W1 = (1, 32760, 12, 128, gdn.GDN_BF16)
