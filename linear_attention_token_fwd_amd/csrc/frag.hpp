@@ -74,4 +74,22 @@ __device__ __forceinline__ float rsqrt_fast(float x) { return __builtin_amdgcn_r
 
 __device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
 
+// Sum over aligned groups of N = 8 or 16 consecutive lanes, every lane of a
+// group receiving the group's sum, by DPP lane permutations (no LDS): swap
+// neighbours, swap pairs (quad_perm), then mirror each half row (lanes 0-3
+// <-> 7-4 of every 8) and, for 16, each row (lanes 0-7 <-> 15-8).  After the
+// quad steps the four lanes of a quad hold the same value, so a mirror adds
+// the other quad's (or half row's) total.
+template <int CTRL> __device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int N> __device__ __forceinline__ float group_sum(float x) {
+    static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
+    x += dpp_f<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+    x += dpp_f<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+    x += dpp_f<0x141>(x);  // row_half_mirror
+    if constexpr (N == 16) x += dpp_f<0x140>(x);  // row_mirror
+    return x;
+}
+
 }  // namespace gdn

@@ -236,8 +236,8 @@ template <class T, int D> struct PrepSmem {
 template <class T, int D, bool MASK>
 __device__ __forceinline__ void conv_silu_norm(const PrepArgs &a, const Raw8<T> (&raw)[3][64 / (kThreads / (D / 8)) + 3],
                                                const bool (&rv)[64 / (kThreads / (D / 8)) + 3],
-                                               const float *const (&wsrc)[3], T *const (&dst)[3], int h, int s0,
-                                               int cg, int run, int len) {
+                                               const float4 *wlds, T *const (&dst)[3], int s0, int cg, int run,
+                                               int len) {
     constexpr int G = D / 8;
     constexpr int RUN = 64 / (kThreads / G);
     constexpr int ROWS = RUN + 3;
@@ -247,7 +247,7 @@ __device__ __forceinline__ void conv_silu_norm(const PrepArgs &a, const Raw8<T> 
         float wt[8][4];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            float4 wv = reinterpret_cast<const float4 *>(wsrc[x])[(size_t)h * D + 8 * cg + i];
+            const float4 wv = wlds[x * D + 8 * cg + i];
             wt[i][0] = wv.x; wt[i][1] = wv.y; wt[i][2] = wv.z; wt[i][3] = wv.w;
         }
         // the rows widened once, positions outside [0, T) as zeros (the conv's zero history)
@@ -271,8 +271,7 @@ __device__ __forceinline__ void conv_silu_norm(const PrepArgs &a, const Raw8<T> 
                 float ss = 0.f;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) ss += acc[i] * acc[i];
-#pragma unroll
-                for (int m = 1; m < G; m <<= 1) ss += __shfl_xor(ss, m, 64);
+                ss = group_sum<G>(ss);
                 const float inv = valid ? rsqrt_fast(ss + a.eps_l2) : 0.f;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) acc[i] *= inv;
@@ -287,18 +286,35 @@ __device__ __forceinline__ void conv_silu_norm(const PrepArgs &a, const Raw8<T> 
 // Short conv + SiLU (+ L2 normalisation for q and k) of the chunk's 64 scan
 // positions into LDS.  Thread layout: G = D/8 threads per token row (8
 // channels each); each thread owns RUN consecutive tokens and loads its
-// RUN + 3 input rows (3 rows of causal history) once, all loads issued before
-// any is used.
-template <class T, int D>
-__device__ __forceinline__ void prologue(const PrepArgs &a, PrepSmem<T, D> &sm, int c, int h, SeqSpan sq) {
+// RUN + 3 input rows (3 rows of causal history) once.  The head's conv
+// weights are copied straight into LDS (the A storage, unused until A is
+// formed), so every load of the prologue is in flight at once; `mid` runs
+// after the loads are issued and must end with a barrier that follows a
+// wait for them (the weights are read from LDS afterwards).
+template <class T, int D, class Mid>
+__device__ __forceinline__ void prologue(const PrepArgs &a, PrepSmem<T, D> &sm, unsigned char *smem, int c, int h,
+                                         SeqSpan sq, Mid mid) {
     constexpr int G = D / 8;
     constexpr int RUN = 64 / (kThreads / G);
     constexpr int ROWS = RUN + 3;
     const int tid = threadIdx.x, cg = tid % G, run = tid / G;
     const int s0 = c * 64 + run * RUN;
     const T *src[3] = {static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v)};
-    const float *wsrc[3] = {a.conv_q, a.conv_k, a.conv_v};
     T *dst[3] = {sm.Qs, sm.Ks, sm.Vs};
+    // weights [3][D][4] fp32: 1 KB units of 64 channels, 16 B per lane
+    float4 *wlds = reinterpret_cast<float4 *>(sm.Am);
+    {
+        constexpr int UNITS = 3 * D / 64;
+        const int w = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
+        const unsigned char *wl = smem + ((const unsigned char *)wlds - (const unsigned char *)&sm);
+#pragma unroll
+        for (int u = w; u < UNITS; u += kWaves) {
+            const int x = u / (D / 64), ch = (u % (D / 64)) * 64 + lane;
+            const float *wsrc = x == 0 ? a.conv_q : (x == 1 ? a.conv_k : a.conv_v);
+            __builtin_amdgcn_global_load_lds(wsrc + ((size_t)h * D + ch) * 4, const_cast<unsigned char *>(wl) + u * 1024,
+                                             16, 0, 0);
+        }
+    }
     Raw8<T> raw[3][ROWS];
     bool rv[ROWS];
 #pragma unroll
@@ -311,11 +327,12 @@ __device__ __forceinline__ void prologue(const PrepArgs &a, PrepSmem<T, D> &sm, 
 #pragma unroll
         for (int x = 0; x < 3; ++x) raw[x][rr].load(src[x] + off);
     }
+    mid();
     // chunks away from both ends of the sequence need no masking
     if (c > 0 && (c + 1) * 64 <= sq.len)
-        conv_silu_norm<T, D, false>(a, raw, rv, wsrc, dst, h, s0, cg, run, sq.len);
+        conv_silu_norm<T, D, false>(a, raw, rv, wlds, dst, s0, cg, run, sq.len);
     else
-        conv_silu_norm<T, D, true>(a, raw, rv, wsrc, dst, h, s0, cg, run, sq.len);
+        conv_silu_norm<T, D, true>(a, raw, rv, wlds, dst, s0, cg, run, sq.len);
 }
 
 template <class T, int D>
@@ -338,24 +355,29 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_prep_kernel(PrepArgs a) {
     if (c * 64 >= sq.len) return;  // past this sequence's end (variable lengths)
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, n = lane % 16, g = lane / 16;
 
-    // ---- gates: b and the cumulative log decay g inside the chunk
-    if (tid < 64) {
-        const int s = c * 64 + tid;
-        const bool valid = s < sq.len;
-        const int src = a.reverse ? sq.len - 1 - s : s;
-        float la = valid ? a.log_a[((size_t)sq.off + src) * a.H + h] : 0.f;
-        float be = valid ? a.beta[((size_t)sq.off + src) * a.H + h] : 0.f;
+    // ---- gates (b and the cumulative log decay g inside the chunk), loaded
+    // after the prologue's loads are issued
+    auto gates = [&] {
+        if (tid < 64) {
+            const int s = c * 64 + tid;
+            const bool valid = s < sq.len;
+            const int src = a.reverse ? sq.len - 1 - s : s;
+            float la = valid ? a.log_a[((size_t)sq.off + src) * a.H + h] : 0.f;
+            float be = valid ? a.beta[((size_t)sq.off + src) * a.H + h] : 0.f;
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            float y = __shfl_up(la, off, 64);
-            if (tid >= off) la += y;
+            for (int off = 1; off < 64; off <<= 1) {
+                float y = __shfl_up(la, off, 64);
+                if (tid >= off) la += y;
+            }
+            sm.g[tid] = la;
+            sm.b[tid] = be;
+            sm.eg[tid] = expf(la);
+            sm.dk[tid] = expf(__shfl(la, 63, 64) - la);
         }
-        sm.g[tid] = la;
-        sm.b[tid] = be;
-        sm.eg[tid] = expf(la);
-        sm.dk[tid] = expf(__shfl(la, 63, 64) - la);
-    }
-    prologue<T, D>(a, sm, c, h, sq);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's weight copies have landed
+        __syncthreads();
+    };
+    prologue<T, D>(a, sm, smem_raw, c, h, sq, gates);
     __syncthreads();
 
     // ---- A = strictly lower (b_i e^{g_i - g_j} k_i . k_j), rows 16w.. of this wave
@@ -371,12 +393,20 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_prep_kernel(PrepArgs a) {
             for (int t = 0; t < 4; ++t)
                 if (t <= w) acc[t] = M::mma(fa, row_frag(sm.Ks + (16 * t + n) * SM::LDX, kb, g), acc[t]);
         }
+        // gates into registers first (the stores below may alias them for the compiler)
+        float gi[4], bi[4], gj[4];
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            gi[ii] = sm.g[16 * w + 4 * g + ii];
+            bi[ii] = sm.b[16 * w + 4 * g + ii];
+            gj[ii] = sm.g[16 * ii + n];
+        }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int i = 16 * w + 4 * g + ii, j = 16 * t + n;
-                sm.Am[i * SM::LDA + j] = (j < i) ? sm.b[i] * __expf(sm.g[i] - sm.g[j]) * acc[t][ii] : 0.f;
+                sm.Am[i * SM::LDA + j] = (j < i) ? bi[ii] * __expf(gi[ii] - gj[t]) * acc[t][ii] : 0.f;
             }
         }
     }
@@ -406,6 +436,17 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_prep_kernel(PrepArgs a) {
     kfrag Xf[4][NCT];
     // waves 0, 1 own the columns of diag(b e^g) K (W), waves 2, 3 those of diag(b) V (U~)
     const bool wave_k = w < 2;
+    // bf16: the identity as a K = 16 B operand (lane (n, g) holds rows 4g..4g+3
+    // of column n).  A product with it copies the A operand, read as rows of
+    // a row-major tile, into C-tile order; with -I it also negates.  Exact.
+    kfrag ident{}, nident{};
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            ident[e] = (T)(4 * g + e == n ? 1.f : 0.f);
+            nident[e] = (T)(4 * g + e == n ? -1.f : 0.f);
+        }
+    }
     const T *rsrc = wave_k ? sm.Ks : sm.Vs;
     const int col0 = (D / 2) * (w & 1);  // first column of this wave inside K or V
 #pragma unroll
@@ -426,10 +467,19 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_prep_kernel(PrepArgs a) {
         }
         floatx4 acc[NCT];
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
+        for (int ct = 0; ct < NCT; ++ct) {
+            if constexpr (sizeof(T) == 2) {
+                // rows 16I.. of R's columns col0 + 16ct.. into C-tile order
+                const kfrag rf = *reinterpret_cast<const kfrag *>(rsrc + (16 * I + n) * SM::LDX + col0 + 16 * ct + 4 * g);
+                acc[ct] = K::mma(rf, ident, zero4());
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii)
-                acc[ct][ii] = scale[ii] * to_f(rsrc[(16 * I + 4 * g + ii) * SM::LDX + col0 + 16 * ct + n]);
+                for (int ii = 0; ii < 4; ++ii) acc[ct][ii] *= scale[ii];
+            } else {
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii)
+                    acc[ct][ii] = scale[ii] * to_f(rsrc[(16 * I + 4 * g + ii) * SM::LDX + col0 + 16 * ct + n]);
+            }
+        }
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
@@ -454,12 +504,18 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_prep_kernel(PrepArgs a) {
                 if (t <= w) acc[t] = M::mma(fa, row_frag(sm.Ks + (16 * t + n) * SM::LDX, kb, g), acc[t]);
         }
         T *P = sm.P();
+        float gi[4], gj[4];
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            gi[ii] = sm.g[16 * w + 4 * g + ii];
+            gj[ii] = sm.g[16 * ii + n];
+        }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int i = 16 * w + 4 * g + ii, j = 16 * t + n;
-                P[i * SM::LDP + j] = (T)((j <= i) ? __expf(sm.g[i] - sm.g[j]) * acc[t][ii] : 0.f);
+                P[i * SM::LDP + j] = (T)((j <= i) ? __expf(gi[ii] - gj[t]) * acc[t][ii] : 0.f);
             }
         }
     }
@@ -467,78 +523,193 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_prep_kernel(PrepArgs a) {
 
     // ---- P X on this wave's columns: Q' = e^g Q - P W (W columns), O0 = P U~
     T *rec = static_cast<T *>(a.rec) + (((size_t)b * a.H + h) * a.NC + c) * (size_t)Rec<D>::SIZE;
-    {
+    if constexpr (sizeof(T) == 2) {
         const T *P = sm.P();
+        if (wave_k) {
+            // Q'^T = e^g Q^T - W^T P^T, computed transposed so that its C tiles
+            // (rows = key channels 4g.., column = token n) are the QP record's
+            // A fragments (row = token, K = key channels) without a transpose:
+            // the A operand -W^T over tokens is this wave's X tiles (negated),
+            // the B operand P^T is read as rows of P.
+            frag nxf[2][NCT];  // -W^T fragments over the 64 tokens: kb = 0, 1
 #pragma unroll
-        for (int R = 0; R < 4; ++R) {
-            frag pf[KBC];
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int kb = 0; kb < KBC; ++kb) pf[kb] = row_frag(P + (16 * R + n) * SM::LDP, kb, g);
+                for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                floatx4 acc = zero4();
-#pragma unroll
-                for (int kb = 0; kb < KBC; ++kb) {
-                    frag xb;
-#pragma unroll
-                    for (int j = 0; j < KPL; ++j) {
-                        const int e = kb * KPL + j;  // token block e/4, row 4g + e%4
-                        fset(xb, j, X[e >> 2][ct][e & 3]);
+                    for (int e = 0; e < 4; ++e) {
+                        nxf[kb][ct][e] = (T)(-X[2 * kb][ct][e]);
+                        nxf[kb][ct][4 + e] = (T)(-X[2 * kb + 1][ct][e]);
                     }
-                    acc = M::mma(pf[kb], xb, acc);
+#pragma unroll
+            for (int R = 0; R < 4; ++R) {
+                frag pf[KBC];
+#pragma unroll
+                for (int kb = 0; kb < KBC; ++kb) pf[kb] = row_frag(P + (16 * R + n) * SM::LDP, kb, g);
+                const float egn = sm.eg[16 * R + n];
+                floatx4 qt[NCT];
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    // e^g Q^T: token 16R + n, key channels col0 + 16ct + 4g.. (C-tile order as read)
+                    const kfrag qv = *reinterpret_cast<const kfrag *>(sm.Qs + (16 * R + n) * SM::LDX + col0 + 16 * ct + 4 * g);
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) qt[ct][ii] = egn * to_f(qv[ii]);
+#pragma unroll
+                    for (int kb = 0; kb < KBC; ++kb) qt[ct] = M::mma(nxf[kb][ct], pf[kb], qt[ct]);
                 }
-                if (wave_k) {
-                    // Q' rows 16R + 4g + ii, staged in Qs over the q^ values it replaces
-                    const int col = col0 + 16 * ct + n;
+#pragma unroll
+                for (int kq = 0; kq < NCT / 2; ++kq) {
+                    frag f;
 #pragma unroll
                     for (int ii = 0; ii < 4; ++ii) {
-                        const int t = 16 * R + 4 * g + ii;
-                        const float qv = sm.eg[t] * to_f(sm.Qs[t * SM::LDX + col]) - acc[ii];
-                        sm.Qs[t * SM::LDX + col] = (T)qv;
+                        f[ii] = (T)qt[2 * kq][ii];
+                        f[4 + ii] = (T)qt[2 * kq + 1][ii];
                     }
-                } else {
+                    *reinterpret_cast<frag *>(rec + Rec<D>::QP + ((R * KBD + col0 / 32 + kq) * 64 + lane) * KPL) = f;
+                }
+            }
+            // WN = -W: the transposes of X's tiles through -I are the A
+            // fragments (row = token, K = key channels)
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                floatx4 wt[NCT];
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) wt[ct] = K::mma(Xf[I][ct], nident, zero4());
+#pragma unroll
+                for (int kq = 0; kq < NCT / 2; ++kq) {
+                    frag f;
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) {
+                        f[ii] = (T)wt[2 * kq][ii];
+                        f[4 + ii] = (T)wt[2 * kq + 1][ii];
+                    }
+                    *reinterpret_cast<frag *>(rec + Rec<D>::WN + ((I * KBD + col0 / 32 + kq) * 64 + lane) * KPL) = f;
+                }
+            }
+        } else {
+            // O0 = P U~ and U~, in C-tile order
+#pragma unroll
+            for (int R = 0; R < 4; ++R) {
+                frag pf[KBC];
+#pragma unroll
+                for (int kb = 0; kb < KBC; ++kb) pf[kb] = row_frag(P + (16 * R + n) * SM::LDP, kb, g);
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    floatx4 acc = zero4();
+#pragma unroll
+                    for (int kb = 0; kb < KBC; ++kb) {
+                        frag xb;
+#pragma unroll
+                        for (int j = 0; j < KPL; ++j) {
+                            const int e = kb * KPL + j;  // token block e/4, row 4g + e%4
+                            fset(xb, j, X[e >> 2][ct][e & 3]);
+                        }
+                        acc = M::mma(pf[kb], xb, acc);
+                    }
                     const int vb = (col0 + 16 * ct) / 16;
                     store4(rec + Rec<D>::O0 + ((vb * 4 + R) * 64 + lane) * 4, acc);
                     store4(rec + Rec<D>::UT + ((vb * 4 + R) * 64 + lane) * 4, X[R][ct]);
                 }
             }
         }
-        // -W staged row-major in Vs (v^ is no longer needed)
-        if (wave_k) {
+        // DKT: A fragments of (D K)^T, rows = key channel w*D/4 + 16 mt + n, K =
+        // tokens; the tiles K[tokens 16I.., keys] come into C-tile order through I
 #pragma unroll
-            for (int I = 0; I < 4; ++I)
+        for (int mt = 0; mt < MT; ++mt) {
+            const int key0 = w * (D / 4) + 16 * mt;
+            floatx4 kt[4];
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
+            for (int I = 0; I < 4; ++I) {
+                const kfrag kf = *reinterpret_cast<const kfrag *>(sm.Ks + (16 * I + n) * SM::LDX + key0 + 4 * g);
+                kt[I] = K::mma(kf, ident, zero4());
 #pragma unroll
-                    for (int ii = 0; ii < 4; ++ii)
-                        sm.Vs[(16 * I + 4 * g + ii) * SM::LDX + col0 + 16 * ct + n] = (T)(-X[I][ct][ii]);
-        }
-    }
-    __syncthreads();
-
-    // ---- QP and WN as A fragments: rows = tokens 16w + n, K = key channels (chained)
-    {
-        const T *qrow = sm.Qs + (16 * w + n) * SM::LDX;
-        const T *wrow = sm.Vs + (16 * w + n) * SM::LDX;
-#pragma unroll
-        for (int kb = 0; kb < KBD; ++kb) {
-            *reinterpret_cast<frag *>(rec + Rec<D>::QP + ((w * KBD + kb) * 64 + lane) * KPL) = row_frag(qrow, kb, g);
-            *reinterpret_cast<frag *>(rec + Rec<D>::WN + ((w * KBD + kb) * 64 + lane) * KPL) = row_frag(wrow, kb, g);
-        }
-    }
-    // DKT: A fragments of (D K)^T, rows = key channel w*D/4 + 16 mt + n, K = tokens
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int dkc = w * (D / 4) + 16 * mt + n;
-#pragma unroll
-        for (int kb = 0; kb < KBC; ++kb) {
-            frag f;
-#pragma unroll
-            for (int j = 0; j < KPL; ++j) {
-                const int tok = kchain(kb * KPL + j, g);
-                fset(f, j, sm.dk[tok] * to_f(sm.Ks[tok * SM::LDX + dkc]));
+                for (int ii = 0; ii < 4; ++ii) kt[I][ii] *= sm.dk[16 * I + 4 * g + ii];
             }
-            *reinterpret_cast<frag *>(rec + Rec<D>::DKT + (((w * MT + mt) * KBC + kb) * 64 + lane) * KPL) = f;
+#pragma unroll
+            for (int kb = 0; kb < KBC; ++kb) {
+                frag f;
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    f[ii] = (T)kt[2 * kb][ii];
+                    f[4 + ii] = (T)kt[2 * kb + 1][ii];
+                }
+                *reinterpret_cast<frag *>(rec + Rec<D>::DKT + (((w * MT + mt) * KBC + kb) * 64 + lane) * KPL) = f;
+            }
+        }
+    } else {
+        {
+            const T *P = sm.P();
+#pragma unroll
+            for (int R = 0; R < 4; ++R) {
+                frag pf[KBC];
+#pragma unroll
+                for (int kb = 0; kb < KBC; ++kb) pf[kb] = row_frag(P + (16 * R + n) * SM::LDP, kb, g);
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    floatx4 acc = zero4();
+#pragma unroll
+                    for (int kb = 0; kb < KBC; ++kb) {
+                        frag xb;
+#pragma unroll
+                        for (int j = 0; j < KPL; ++j) {
+                            const int e = kb * KPL + j;  // token block e/4, row 4g + e%4
+                            fset(xb, j, X[e >> 2][ct][e & 3]);
+                        }
+                        acc = M::mma(pf[kb], xb, acc);
+                    }
+                    if (wave_k) {
+                        // Q' rows 16R + 4g + ii, staged in Qs over the q^ values it replaces
+                        const int col = col0 + 16 * ct + n;
+#pragma unroll
+                        for (int ii = 0; ii < 4; ++ii) {
+                            const int t = 16 * R + 4 * g + ii;
+                            const float qv = sm.eg[t] * to_f(sm.Qs[t * SM::LDX + col]) - acc[ii];
+                            sm.Qs[t * SM::LDX + col] = (T)qv;
+                        }
+                    } else {
+                        const int vb = (col0 + 16 * ct) / 16;
+                        store4(rec + Rec<D>::O0 + ((vb * 4 + R) * 64 + lane) * 4, acc);
+                        store4(rec + Rec<D>::UT + ((vb * 4 + R) * 64 + lane) * 4, X[R][ct]);
+                    }
+                }
+            }
+            // -W staged row-major in Vs (v^ is no longer needed)
+            if (wave_k) {
+#pragma unroll
+                for (int I = 0; I < 4; ++I)
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                        for (int ii = 0; ii < 4; ++ii)
+                            sm.Vs[(16 * I + 4 * g + ii) * SM::LDX + col0 + 16 * ct + n] = (T)(-X[I][ct][ii]);
+            }
+        }
+        __syncthreads();
+
+        // ---- QP and WN as A fragments: rows = tokens 16w + n, K = key channels (chained)
+        {
+            const T *qrow = sm.Qs + (16 * w + n) * SM::LDX;
+            const T *wrow = sm.Vs + (16 * w + n) * SM::LDX;
+#pragma unroll
+            for (int kb = 0; kb < KBD; ++kb) {
+                *reinterpret_cast<frag *>(rec + Rec<D>::QP + ((w * KBD + kb) * 64 + lane) * KPL) = row_frag(qrow, kb, g);
+                *reinterpret_cast<frag *>(rec + Rec<D>::WN + ((w * KBD + kb) * 64 + lane) * KPL) = row_frag(wrow, kb, g);
+            }
+        }
+        // DKT: A fragments of (D K)^T, rows = key channel w*D/4 + 16 mt + n, K = tokens
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int dkc = w * (D / 4) + 16 * mt + n;
+#pragma unroll
+            for (int kb = 0; kb < KBC; ++kb) {
+                frag f;
+#pragma unroll
+                for (int j = 0; j < KPL; ++j) {
+                    const int tok = kchain(kb * KPL + j, g);
+                    fset(f, j, sm.dk[tok] * to_f(sm.Ks[tok * SM::LDX + dkc]));
+                }
+                *reinterpret_cast<frag *>(rec + Rec<D>::DKT + (((w * MT + mt) * KBC + kb) * 64 + lane) * KPL) = f;
+            }
         }
     }
     if (tid == 0) a.gC[((size_t)b * a.H + h) * a.NC + c] = sm.eg[63];
@@ -767,14 +938,16 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_out_kernel(OutArgs a) {
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, n = lane % 16, g = lane / 16;
     const size_t bh = (size_t)b * a.H + h;
 
-    // stage the chunk-entry state of all value blocks
+    // stage the chunk-entry state of all value blocks: direct-to-LDS copies
+    // of 1 KB units (16 B per lane), all in flight with the loads below
     {
-        const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const T *>(a.sc) +
-                                                           (bh * a.NC + c) * (size_t)SL::PER_CHUNK);
-        uint4 *dst = reinterpret_cast<uint4 *>(sm.sc);
-        constexpr int N16 = SL::PER_CHUNK * (int)sizeof(T) / 16;
+        const unsigned char *src = reinterpret_cast<const unsigned char *>(
+            static_cast<const T *>(a.sc) + (bh * a.NC + c) * (size_t)SL::PER_CHUNK);
+        constexpr int UNITS = SL::PER_CHUNK * (int)sizeof(T) / 1024;
+        static_assert(UNITS % kWaves == 0, "state staging units per wave");
 #pragma unroll
-        for (int i = tid; i < N16; i += kThreads) dst[i] = src[i];
+        for (int u = w; u < UNITS; u += kWaves)
+            __builtin_amdgcn_global_load_lds(src + u * 1024 + lane * 16, smem_raw + u * 1024, 16, 0, 0);
     }
     const T *rec = static_cast<const T *>(a.rec) + (bh * a.NC + c) * (size_t)Rec<D>::SIZE;
     frag qp[KBD];
@@ -801,6 +974,15 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_out_kernel(OutArgs a) {
         load8(static_cast<const T *>(a.gate) + roff[pass], gv[pass]);
         if (a.mode == 2) load8(a.acc + roff[pass], prev[pass]);
     }
+    float wv[8];  // norm weights (4-byte aligned)
+    if (a.norm_w) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wv[i] = a.norm_w[h * D + 8 * cg + i];
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wv[i] = 1.f;
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's copies have landed
     __syncthreads();
     // O = O0 + Q' S^T for tokens 16w.., all value channels
 #pragma unroll
@@ -815,9 +997,6 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_out_kernel(OutArgs a) {
     __syncthreads();
 
     // gated RMS normalisation: G threads per token row, 8 channels each
-    float wv[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) wv[i] = a.norm_w ? a.norm_w[h * D + 8 * cg + i] : 1.f;
 #pragma unroll
     for (int pass = 0; pass < PASSES; ++pass) {
         const int r = pass * TPP + tid / G;
@@ -830,8 +1009,7 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_out_kernel(OutArgs a) {
         float ss = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) ss += ov[i] * ov[i];
-#pragma unroll
-        for (int m = 1; m < G; m <<= 1) ss += __shfl_xor(ss, m, 64);
+        ss = group_sum<G>(ss);
         const float inv = rsqrt_fast(ss * (1.0f / D) + a.eps);
         if (!live) continue;
         const size_t off = roff[pass];
