@@ -67,13 +67,14 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "linear_attention_token_fwd_amd", "csrc")
 
 
-KERNEL_SOURCES = ("frag.hpp", "sync.hpp", "kernels.hpp")        # the layer's kernels
-MIXER_SOURCES = KERNEL_SOURCES + ("gemm.hpp",)                   # + the projection GEMM
+# the layer's kernels, and the launch plan (its ranges set the work per dispatch)
+KERNEL_SOURCES = ("frag.hpp", "sync.hpp", "kernels.hpp", "gdn_api.hip")
+MIXER_SOURCES = KERNEL_SOURCES + ("gemm.hpp", "gdn_proj.hip")    # + the projection GEMM
 
 
 def csrc_hash(sources=KERNEL_SOURCES) -> str:
-    """sha256 over the kernel sources (device code only), to tell whether a
-    stored profile still describes the kernels being run."""
+    """sha256 over the kernel sources and the launch plan, to tell whether a
+    stored profile still describes the dispatches being run."""
     import hashlib
     h = hashlib.sha256()
     for name in sources:

@@ -326,10 +326,16 @@ gdn_status run_plan(const Plan &plan, hipStream_t caller, hipEvent_t *timing, bo
     return enqueue_ops(plan, streams, r, timing);
 }
 
-// Chunk ranges of a scan: ~64 chunks each, at most 16 ranges unless a range
-// would exceed the state kernel's limit.
+// Chunk ranges of a scan: ~128 chunks each, at most 16 ranges unless a range
+// would exceed the state kernel's limit.  Measured at T = 32760 (512 chunks),
+// H = 12, d = 128: ranges of 32 / 64 / 96 / 128 / 192 chunks take 0.765 /
+// 0.696 / 0.683 / 0.677 / 0.663 ms per call; 192 is slower than 128 at
+// T = 75600 (1.482 against 1.467 ms) and at H = 24 (0.912 against 0.901).
+// Each chain launch pays for filling its operand registers and for the
+// hand-over of the state; the first prep range and the last output range run
+// alone.
 int n_ranges(int NC) {
-    int R = (NC + 63) / 64;
+    int R = (NC + 127) / 128;
     R = R < 1 ? 1 : (R > 16 ? 16 : R);
     const int need = (NC + gdn::kStateMaxRange - 1) / gdn::kStateMaxRange;
     return R < need ? need : R;
