@@ -150,6 +150,43 @@ __device__ __forceinline__ floatx4 load4(const bf16 *p) {
     return floatx4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
 }
 __device__ __forceinline__ floatx4 load4(const float *p) { return *reinterpret_cast<const floatx4 *>(p); }
+// Streaming (non-temporal) accesses, which do not allocate in L2: for data
+// written once and read once much later or by another kernel (the chunk
+// records, the output, the bidirectional accumulator) and for data read once
+// (the output kernel's records and gate).  This keeps L2 for the state
+// chain's operands, which the value-block workgroups of a head share; at
+// T = 32760, H = 12, d = 128 the whole call takes 0.670 -> 0.640 ms.
+template <class V> __device__ __forceinline__ void st_nt(V *p, const V &v) { __builtin_nontemporal_store(v, p); }
+template <class V> __device__ __forceinline__ V ld_nt(const V *p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void store8_nt(bf16 *p, const float *x) {
+    bf16x8 v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (bf16)x[i];
+    st_nt(reinterpret_cast<bf16x8 *>(p), v);
+}
+__device__ __forceinline__ void store8_nt(float *p, const float *x) {
+    st_nt(reinterpret_cast<floatx4 *>(p), floatx4{x[0], x[1], x[2], x[3]});
+    st_nt(reinterpret_cast<floatx4 *>(p) + 1, floatx4{x[4], x[5], x[6], x[7]});
+}
+__device__ __forceinline__ void store4_nt(bf16 *p, floatx4 x) {
+    st_nt(reinterpret_cast<bf16x4 *>(p), bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]});
+}
+__device__ __forceinline__ void store4_nt(float *p, floatx4 x) { st_nt(reinterpret_cast<floatx4 *>(p), x); }
+__device__ __forceinline__ void load8_nt(const bf16 *p, float *x) {
+    const bf16x8 v = ld_nt(reinterpret_cast<const bf16x8 *>(p));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = (float)v[i];
+}
+__device__ __forceinline__ void load8_nt(const float *p, float *x) {
+    const floatx4 a = ld_nt(reinterpret_cast<const floatx4 *>(p)), b = ld_nt(reinterpret_cast<const floatx4 *>(p) + 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { x[i] = a[i]; x[4 + i] = b[i]; }
+}
+__device__ __forceinline__ floatx4 load4_nt(const bf16 *p) {
+    const bf16x4 v = ld_nt(reinterpret_cast<const bf16x4 *>(p));
+    return floatx4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+__device__ __forceinline__ floatx4 load4_nt(const float *p) { return ld_nt(reinterpret_cast<const floatx4 *>(p)); }
 // the same in two steps: the load, and the widening to fp32 when it is used
 template <class T> struct Vec4;
 template <> struct Vec4<bf16> {
@@ -565,7 +602,7 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_prep_kernel(PrepArgs a) {
                         f[ii] = (T)qt[2 * kq][ii];
                         f[4 + ii] = (T)qt[2 * kq + 1][ii];
                     }
-                    *reinterpret_cast<frag *>(rec + Rec<D>::QP + ((R * KBD + col0 / 32 + kq) * 64 + lane) * KPL) = f;
+                    st_nt(reinterpret_cast<frag *>(rec + Rec<D>::QP + ((R * KBD + col0 / 32 + kq) * 64 + lane) * KPL), f);
                 }
             }
             // WN = -W: the transposes of X's tiles through -I are the A
@@ -583,7 +620,7 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_prep_kernel(PrepArgs a) {
                         f[ii] = (T)wt[2 * kq][ii];
                         f[4 + ii] = (T)wt[2 * kq + 1][ii];
                     }
-                    *reinterpret_cast<frag *>(rec + Rec<D>::WN + ((I * KBD + col0 / 32 + kq) * 64 + lane) * KPL) = f;
+                    st_nt(reinterpret_cast<frag *>(rec + Rec<D>::WN + ((I * KBD + col0 / 32 + kq) * 64 + lane) * KPL), f);
                 }
             }
         } else {
@@ -607,8 +644,8 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_prep_kernel(PrepArgs a) {
                         acc = M::mma(pf[kb], xb, acc);
                     }
                     const int vb = (col0 + 16 * ct) / 16;
-                    store4(rec + Rec<D>::O0 + ((vb * 4 + R) * 64 + lane) * 4, acc);
-                    store4(rec + Rec<D>::UT + ((vb * 4 + R) * 64 + lane) * 4, X[R][ct]);
+                    store4_nt(rec + Rec<D>::O0 + ((vb * 4 + R) * 64 + lane) * 4, acc);
+                    store4_nt(rec + Rec<D>::UT + ((vb * 4 + R) * 64 + lane) * 4, X[R][ct]);
                 }
             }
         }
@@ -633,7 +670,7 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_prep_kernel(PrepArgs a) {
                     f[ii] = (T)kt[2 * kb][ii];
                     f[4 + ii] = (T)kt[2 * kb + 1][ii];
                 }
-                *reinterpret_cast<frag *>(rec + Rec<D>::DKT + (((w * MT + mt) * KBC + kb) * 64 + lane) * KPL) = f;
+                st_nt(reinterpret_cast<frag *>(rec + Rec<D>::DKT + (((w * MT + mt) * KBC + kb) * 64 + lane) * KPL), f);
             }
         }
     } else {
@@ -668,8 +705,8 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_prep_kernel(PrepArgs a) {
                         }
                     } else {
                         const int vb = (col0 + 16 * ct) / 16;
-                        store4(rec + Rec<D>::O0 + ((vb * 4 + R) * 64 + lane) * 4, acc);
-                        store4(rec + Rec<D>::UT + ((vb * 4 + R) * 64 + lane) * 4, X[R][ct]);
+                        store4_nt(rec + Rec<D>::O0 + ((vb * 4 + R) * 64 + lane) * 4, acc);
+                        store4_nt(rec + Rec<D>::UT + ((vb * 4 + R) * 64 + lane) * 4, X[R][ct]);
                     }
                 }
             }
@@ -692,8 +729,8 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_prep_kernel(PrepArgs a) {
             const T *wrow = sm.Vs + (16 * w + n) * SM::LDX;
 #pragma unroll
             for (int kb = 0; kb < KBD; ++kb) {
-                *reinterpret_cast<frag *>(rec + Rec<D>::QP + ((w * KBD + kb) * 64 + lane) * KPL) = row_frag(qrow, kb, g);
-                *reinterpret_cast<frag *>(rec + Rec<D>::WN + ((w * KBD + kb) * 64 + lane) * KPL) = row_frag(wrow, kb, g);
+                st_nt(reinterpret_cast<frag *>(rec + Rec<D>::QP + ((w * KBD + kb) * 64 + lane) * KPL), row_frag(qrow, kb, g));
+                st_nt(reinterpret_cast<frag *>(rec + Rec<D>::WN + ((w * KBD + kb) * 64 + lane) * KPL), row_frag(wrow, kb, g));
             }
         }
         // DKT: A fragments of (D K)^T, rows = key channel w*D/4 + 16 mt + n, K = tokens
@@ -708,7 +745,7 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_prep_kernel(PrepArgs a) {
                     const int tok = kchain(kb * KPL + j, g);
                     fset(f, j, sm.dk[tok] * to_f(sm.Ks[tok * SM::LDX + dkc]));
                 }
-                *reinterpret_cast<frag *>(rec + Rec<D>::DKT + (((w * MT + mt) * KBC + kb) * 64 + lane) * KPL) = f;
+                st_nt(reinterpret_cast<frag *>(rec + Rec<D>::DKT + (((w * MT + mt) * KBC + kb) * 64 + lane) * KPL), f);
             }
         }
     }
@@ -953,10 +990,10 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_out_kernel(OutArgs a) {
     frag qp[KBD];
 #pragma unroll
     for (int kb = 0; kb < KBD; ++kb)
-        qp[kb] = *reinterpret_cast<const frag *>(rec + Rec<D>::QP + ((w * KBD + kb) * 64 + lane) * KPL);
+        qp[kb] = ld_nt(reinterpret_cast<const frag *>(rec + Rec<D>::QP + ((w * KBD + kb) * 64 + lane) * KPL));
     floatx4 o[NV];
 #pragma unroll
-    for (int vb = 0; vb < NV; ++vb) o[vb] = load4(rec + Rec<D>::O0 + ((vb * 4 + w) * 64 + lane) * 4);
+    for (int vb = 0; vb < NV; ++vb) o[vb] = load4_nt(rec + Rec<D>::O0 + ((vb * 4 + w) * 64 + lane) * 4);
     // the gate (and, summing the second scan, the first scan's output) of the
     // rows this thread normalises below, loaded with the rest (rows clamped)
     constexpr int G = D / 8;
@@ -971,8 +1008,8 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_out_kernel(OutArgs a) {
         const int sc_ = s < sq.len ? s : sq.len - 1;
         const int t = a.reverse ? sq.len - 1 - sc_ : sc_;
         roff[pass] = (((size_t)sq.off + t) * a.H + h) * D + 8 * cg;
-        load8(static_cast<const T *>(a.gate) + roff[pass], gv[pass]);
-        if (a.mode == 2) load8(a.acc + roff[pass], prev[pass]);
+        load8_nt(static_cast<const T *>(a.gate) + roff[pass], gv[pass]);
+        if (a.mode == 2) load8_nt(a.acc + roff[pass], prev[pass]);
     }
     float wv[8];  // norm weights (4-byte aligned)
     if (a.norm_w) {
@@ -1017,13 +1054,13 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_out_kernel(OutArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) y[i] = ov[i] * inv * wv[i] * silu(gv[pass][i]);
         if (a.mode == 1) {
-            store8(a.acc + off, y);
+            store8_nt(a.acc + off, y);
         } else {
             if (a.mode == 2) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) y[i] += prev[pass][i];
             }
-            store8(static_cast<T *>(a.out) + off, y);
+            store8_nt(static_cast<T *>(a.out) + off, y);
         }
     }
 }
