@@ -798,8 +798,10 @@ template <class T, int D> struct StateOps {
 //      B fragments in LDS;                                       barrier;
 //   C: S^T[rows] <- e^{g_C} S^T[rows] + (D K)^T[rows] U.
 // Its operand fragments come straight from the chunk records in HBM into
-// registers, NB chunks ahead (four register sets used in turn); LDS holds
-// only the exchange.  Every wave passes 1 + 2 * chunks barriers.
+// registers, NB chunks ahead (four register sets used in turn; a set's -W
+// and U~ are reloaded right after phase A has used them, before the first
+// barrier's wait, its (D K)^T after phase C); LDS holds only the exchange.
+// Every wave passes 1 + 2 * chunks barriers.
 template <class T, int D>
 __global__ __launch_bounds__((StateCfg<T, D>::THREADS)) void gdn_state_kernel(StateArgs a) {
     typedef Mfma<T> M;
@@ -834,7 +836,7 @@ __global__ __launch_bounds__((StateCfg<T, D>::THREADS)) void gdn_state_kernel(St
     for (int i = tid; i < c_end - a.c_begin; i += C::THREADS) sm.gcs[i] = a.gC[bh * a.NC + a.c_begin + i];
 
     Ops ops[C::NB];
-    auto load_ops = [&](Ops &o, int c) {
+    auto load_w = [&](Ops &o, int c) {
         const T *rec = rec0 + (size_t)c * Rec<D>::SIZE;
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
@@ -842,13 +844,20 @@ __global__ __launch_bounds__((StateCfg<T, D>::THREADS)) void gdn_state_kernel(St
             for (int kb = 0; kb < KBQ; ++kb)
                 o.wf[tt][kb] = *reinterpret_cast<const frag *>(rec + Rec<D>::WN + ((tt * KBD + w * KBQ + kb) * 64 + lane) * KPL);
 #pragma unroll
+        for (int j = 0; j < TPW; ++j)
+            o.ut[j] = *reinterpret_cast<const typename Vec4<T>::type *>(rec + Rec<D>::UT + ((vb * 4 + w * TPW + j) * 64 + lane) * 4);
+    };
+    auto load_dk = [&](Ops &o, int c) {
+        const T *rec = rec0 + (size_t)c * Rec<D>::SIZE;
+#pragma unroll
         for (int mt = 0; mt < MQ; ++mt)
 #pragma unroll
             for (int kb = 0; kb < KBC; ++kb)
                 o.dkf[mt][kb] = *reinterpret_cast<const frag *>(rec + Rec<D>::DKT + (((w * MQ + mt) * KBC + kb) * 64 + lane) * KPL);
-#pragma unroll
-        for (int j = 0; j < TPW; ++j)
-            o.ut[j] = *reinterpret_cast<const typename Vec4<T>::type *>(rec + Rec<D>::UT + ((vb * 4 + w * TPW + j) * 64 + lane) * 4);
+    };
+    auto load_ops = [&](Ops &o, int c) {
+        load_w(o, c);
+        load_dk(o, c);
     };
 
     floatx4 S[MQ];
@@ -901,6 +910,8 @@ __global__ __launch_bounds__((StateCfg<T, D>::THREADS)) void gdn_state_kernel(St
             for (int kb = 0; kb < KBQ; ++kb) up[tt] = M::mma(o.wf[tt][kb], sB[kb], up[tt]);
             sm.part[w][tt][lane] = up[tt];
         }
+        // this register set's -W and U~ now take chunk c + NB (issued before the barrier wait)
+        load_w(o, min(c + C::NB, last));
         lds_barrier();
         // ---- B: U for this wave's token tiles (every wave's partial, its own included)
 #pragma unroll
@@ -923,8 +934,8 @@ __global__ __launch_bounds__((StateCfg<T, D>::THREADS)) void gdn_state_kernel(St
 #pragma unroll
             for (int kb = 0; kb < KBC; ++kb) S[mt] = M::mma(o.dkf[mt][kb], uB[kb], S[mt]);
         }
-        // this register set now takes chunk c + NB (past the range: the last chunk again, unused)
-        load_ops(o, min(c + C::NB, last));
+        // and its (D K)^T (past the range: the last chunk again, unused)
+        load_dk(o, min(c + C::NB, last));
     };
     // whole groups of NB chunks (one back edge, so the loads in flight at the
     // top of the loop are the same on every entry), then the rest
