@@ -10,15 +10,18 @@
 // weight.  The in-projection's epilogue also does the gate
 // parameterisation:  b = sigmoid(z_b),  log a = -exp(A_h) softplus(z_a).
 //
-// Tiling.  One workgroup of 4 waves computes a 256 x 256 output tile over K
-// in steps of 64.  The operand tiles of a step (256 rows of X and 256 rows of
+// Tiling.  One workgroup of 8 waves (two per SIMD, so one wave's LDS reads
+// hide behind the other's MFMAs) computes a 256 x 256 output tile over K in
+// steps of 64.  The operand tiles of a step (256 rows of X and 256 rows of
 // W, 128 bytes each, 64 KB) are copied global -> LDS by direct-to-LDS loads
 // (16 B per lane, 8 rows x 128 B per load, so each row is one whole cache
 // line) into a ring of 2 stages: the copy of step s + 1 runs while step s is
 // multiplied.  In LDS the 16-byte chunks of a row are XOR-swizzled by the row
 // so that the fragment reads are free of bank conflicts.  Wave (wm, wn) owns
-// the 128 x 128 sub-tile (8 x 8 MFMA tiles of 16 x 16) and reads each W
-// fragment from LDS while the MFMAs of the previous one run.
+// the 128 x 64 sub-tile (8 x 4 MFMA tiles of 16 x 16) and reads each W
+// fragment from LDS while the MFMAs of the previous one run.  (Four waves
+// with 128 x 128 sub-tiles: 853 against 1023 TFLOP/s for the in-projection
+// at M = 32760, N = 6168, K = 1536.)
 //
 // Operand order.  The MFMA's A operand is W and its B operand is X, so the
 // accumulator tile is out^T: lane (r, g) holds out[m + r][n + 4g .. 4g+3],
@@ -38,11 +41,11 @@ constexpr int UNIT = 1024;     // bytes of one copy unit: 8 rows x 128 B
 constexpr int XU = BM / 8;     // X units per step
 constexpr int WU = BN / 8;     // W units per step
 constexpr int STAGE_BYTES = (XU + WU) * UNIT;     // 64 KB
-constexpr int EPI_LD = 272;     // bytes per staged output row (128 bf16 + 16 B pad)
-constexpr int EPI_WAVE = 128 * EPI_LD;            // one wave's 128 x 128 output block
-constexpr int LDS_BYTES = STAGES * STAGE_BYTES > 4 * EPI_WAVE ? STAGES * STAGE_BYTES : 4 * EPI_WAVE;  // 136 KB
-constexpr int THREADS = 256;
-constexpr int DMA_PER_WAVE = (XU + WU) / (THREADS / 64);  // 16
+constexpr int EPI_LD = 144;     // bytes per staged output row (64 bf16 + 16 B pad)
+constexpr int EPI_WAVE = 128 * EPI_LD;            // one wave's 128 x 64 output block
+constexpr int LDS_BYTES = STAGES * STAGE_BYTES > 8 * EPI_WAVE ? STAGES * STAGE_BYTES : 8 * EPI_WAVE;  // 144 KB
+constexpr int THREADS = 512;
+constexpr int DMA_PER_WAVE = (XU + WU) / (THREADS / 64);  // 8
 constexpr int GROUP_M = 4;     // row tiles per group of the tile order
 }  // namespace gemm
 
@@ -95,7 +98,7 @@ __device__ __forceinline__ void store_bf16x4(bf16 *p, floatx4 v) {
 }
 
 template <int EPI>
-__global__ __launch_bounds__(gemm::THREADS, 1) void gdn_gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(gemm::THREADS, 2) void gdn_gemm_kernel(GemmArgs a) {
     using namespace gemm;
     typedef Mfma<bf16> Mf;
     typedef Mf::frag frag;
@@ -116,10 +119,10 @@ __global__ __launch_bounds__(gemm::THREADS, 1) void gdn_gemm_kernel(GemmArgs a) 
     // in slot 8 r' + (c ^ r').  A 128-bit LDS read is served 8 lanes at a
     // time, and the swizzle puts the 8 rows such a group reads (the same
     // chunk of rows r' = 0..7) on 8 distinct 16-byte bank groups.
-    // Waves 0, 1 copy the X units, waves 2, 3 the W units.  Rows past the end
+    // Waves 0-3 copy the X units, waves 4-7 the W units.  Rows past the end
     // read the last row (never stored).  Element offsets fit in 32 bits (the
     // host checks M K and N K).
-    const bf16 *base = w < 2 ? a.x : a.w;
+    const bf16 *base = w < 4 ? a.x : a.w;
     unsigned off[DMA_PER_WAVE];
     {
         const int rr = lane >> 3, chunk = (lane & 7) ^ rr;
@@ -145,9 +148,9 @@ __global__ __launch_bounds__(gemm::THREADS, 1) void gdn_gemm_kernel(GemmArgs a) 
         fo[kb] = hi * UNIT + (8 * rr + ((4 * kb + g) ^ rr)) * 16;
     }
 
-    floatx4 acc[8][8];
+    floatx4 acc[4][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = zero4();
 
@@ -158,17 +161,17 @@ __global__ __launch_bounds__(gemm::THREADS, 1) void gdn_gemm_kernel(GemmArgs a) 
     // step s, reading each W fragment while the MFMAs of the previous one run.
     const int S = a.K / BK;
     issue(0);
-    // A step is 16 groups (kb, i) of 8 MFMAs sharing W fragment (kb, i) and
+    // A step is 8 groups (kb, i) of 8 MFMAs sharing W fragment (kb, i) and
     // the 8 X fragments of kb.  W fragments are read two groups ahead, the X
-    // fragments of kb = 1 during the second half of kb = 0.
+    // fragments of kb = 1 during kb = 0.
     frag xf[2][8], wf[3];
     for (int s = 0; s < S; ++s) {
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         lds_barrier();
         if (s + 1 < S) issue(s + 1);
         const unsigned char *buf = smem + (s % STAGES) * STAGE_BYTES;
-        auto wfrag = [&](int q) {  // W fragment of group q = 8 kb + i
-            return *reinterpret_cast<const frag *>(buf + 2 * (XU / 2 + 8 * wn + (q & 7)) * UNIT + fo[q >> 3]);
+        auto wfrag = [&](int q) {  // W fragment of group q = 4 kb + i
+            return *reinterpret_cast<const frag *>(buf + 2 * (XU / 2 + 4 * wn + (q & 3)) * UNIT + fo[q >> 2]);
         };
         auto xfrag = [&](int kb, int j) {
             return *reinterpret_cast<const frag *>(buf + 2 * (8 * wm + j) * UNIT + fo[kb]);
@@ -178,30 +181,30 @@ __global__ __launch_bounds__(gemm::THREADS, 1) void gdn_gemm_kernel(GemmArgs a) 
         wf[0] = wfrag(0);
         wf[1] = wfrag(1);
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            if (q + 2 < 16) wf[(q + 2) % 3] = wfrag(q + 2);
-            if (q >= 4 && q < 8) {
-                xf[1][2 * (q - 4)] = xfrag(1, 2 * (q - 4));
-                xf[1][2 * (q - 4) + 1] = xfrag(1, 2 * (q - 4) + 1);
+        for (int q = 0; q < 8; ++q) {
+            if (q + 2 < 8) wf[(q + 2) % 3] = wfrag(q + 2);
+            if (q < 4) {
+                xf[1][2 * q] = xfrag(1, 2 * q);
+                xf[1][2 * q + 1] = xfrag(1, 2 * q + 1);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[q & 7][j] = Mf::mma(wf[q % 3], xf[q >> 3][j], acc[q & 7][j]);
+            for (int j = 0; j < 8; ++j) acc[q & 3][j] = Mf::mma(wf[q % 3], xf[q >> 2][j], acc[q & 3][j]);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
 
     // Epilogue.  acc[i][j]: lane (r, g) holds out[m0 + 128 wm + 16 j + r][n0 +
-    // 128 wn + 16 i + 4g .. +3].  The in-projection's gate columns (past
+    // 64 wn + 16 i + 4g .. +3].  The in-projection's gate columns (past
     // 4 H D) go out from registers, element by element; every other value,
-    // bias added, is staged as bf16 in LDS (each wave its own 128 x 128 block,
-    // rows padded to 272 B) and stored from there as 16-byte pieces of whole
-    // 256-byte row segments.
-    const int row0 = m0 + 128 * wm, col0 = n0 + 128 * wn;
+    // bias added, is staged as bf16 in LDS (each wave its own 128 x 64 block,
+    // rows padded to 144 B) and stored from there as 16-byte pieces of whole
+    // 128-byte row segments.
+    const int row0 = m0 + 128 * wm, col0 = n0 + 64 * wn;
     const int ncols = EPI == kEpiPlain ? a.N : min(a.N, 4 * a.HD);  // columns staged and stored from LDS
     if (EPI == kEpiInProj) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4; ++i) {
             const int tcol = col0 + 16 * i;  // wave-uniform
             if (tcol + 16 <= 4 * a.HD || tcol >= a.N) continue;
             const int col = tcol + 4 * g;
@@ -225,7 +228,7 @@ __global__ __launch_bounds__(gemm::THREADS, 1) void gdn_gemm_kernel(GemmArgs a) 
     lds_barrier();  // every wave is done with the operand stages
     unsigned char *stage = smem + w * EPI_WAVE;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
         const int col = col0 + 16 * i + 4 * g;
         const floatx4 bv = col + 4 <= ncols ? add_bias4(a.bias, col, zero4()) : zero4();
 #pragma unroll
@@ -236,8 +239,8 @@ __global__ __launch_bounds__(gemm::THREADS, 1) void gdn_gemm_kernel(GemmArgs a) 
         }
     }
     __builtin_amdgcn_s_waitcnt(kLgkm0);  // this wave's block is in LDS (only this wave reads it)
-    // 16 lanes per row, 8 columns (16 B) each, 4 rows per pass
-    const int lr = lane / 16, lc = 8 * (lane % 16);
+    // 8 lanes per row, 8 columns (16 B) each, 8 rows per pass
+    const int lr = lane / 8, lc = 8 * (lane % 8);
     const int col = col0 + lc;
     if (col < ncols) {
         bf16 *dst;
@@ -253,8 +256,8 @@ __global__ __launch_bounds__(gemm::THREADS, 1) void gdn_gemm_kernel(GemmArgs a) 
         }
         const bool full = col + 8 <= ncols;  // else 4 columns (ncols % 4 == 0)
 #pragma unroll 4
-        for (int pass = 0; pass < 32; ++pass) {
-            const int rr = 4 * pass + lr;
+        for (int pass = 0; pass < 16; ++pass) {
+            const int rr = 8 * pass + lr;
             const int row = row0 + rr;
             if (row >= a.M) break;
             const unsigned char *src = stage + rr * EPI_LD + lc * 2;
