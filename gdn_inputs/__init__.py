@@ -154,6 +154,27 @@ def generate(w: Workload | int, seed: int | None = None, T: int | None = None,
                 conv_k=conv_k, conv_v=conv_v, norm_w=norm_w, S0=S0)
 
 
+def generate_grads(w: Workload | int, seed: int, T: int | None = None, H: int | None = None,
+                   B: int | None = None, t_end: int | None = None, state: bool = True) -> dict:
+    """Draw the upstream gradients of a backward pass (seed as given): dy ~
+    N(0, 1) [B, T, H, D] (rounded to bf16 for bf16 workloads), zero from
+    token t_end on if t_end is given; dS_T ~ N(0, 1) [B, H, D, D], or None
+    if not state.  float32 numpy arrays."""
+    if isinstance(w, int):
+        w = WORKLOADS[w]
+    B = w.B if B is None else B
+    T = w.T if T is None else T
+    H = w.H if H is None else H
+    rng = np.random.default_rng(seed)
+    dy = rng.standard_normal((B, T, H, w.D), dtype=np.float32)
+    if t_end is not None:
+        dy[:, t_end:] = 0.0
+    if w.dtype == "bf16":
+        dy = round_bf16(dy)
+    dS_T = rng.standard_normal((B, H, w.D, w.D), dtype=np.float32) if state else None
+    return dict(dy=dy, dS_T=dS_T)
+
+
 def generate_mixer(w: MixerWorkload | int, seed: int | None = None, T: int | None = None,
                    B: int | None = None, bias: bool = True) -> dict:
     """Draw a token mixer's hidden states and weights (float32 numpy arrays

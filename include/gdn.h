@@ -299,6 +299,71 @@ gdn_status gdn_mixer_fwd_timed(const gdn_mixer_params *p, struct ihipEvent_t **e
 gdn_status gdn_set_graph_cache_limit(int max_graphs);
 int gdn_graph_cache_count(void);
 
+/*
+ * The layer's backward pass: the gradients of steps 1-5 (gdn_fwd with
+ * reverse = 0) with respect to every input, for equal-length batch rows.
+ * The pages train the converted GDN blocks (LinMorph project page,
+ * "Abstract": progressive distillation and joint recovery), which needs
+ * them; the Gated DeltaNet paper's chunkwise WY form (section 3.3) is the
+ * forward they differentiate.  Given dy = dL/dy and dS_T = dL/dS_T, one call
+ * writes
+ *   dq, dk, dv, dgate   [B, T, H, D]   io_dtype
+ *   dlog_a, dbeta       [B, T, H]      float32
+ *   dconv_q, dconv_k, dconv_v [H*D, 4] float32 (sums over batch rows and tokens)
+ *   dnorm_w             [H, Dv]        float32, the gradient at norm_w (ones
+ *                                      when norm_w is NULL); NULL: not written
+ *   dS0                 [B, H, Dv, Dk] float32, also when S0 is NULL (the
+ *                                      gradient at the zero state); NULL: not written
+ * The inputs have the layouts of gdn_fwd; dy is [B, T, H, Dv] in io_dtype,
+ * dS_T [B, H, Dv, Dk] float32 or NULL (zero).  The forward is recomputed
+ * inside the call (nothing is kept from a gdn_fwd call).
+ * Supported: Dk = Dv in {64, 128}, io_dtype GDN_BF16 or GDN_F32.  All
+ * arithmetic is fp32 (fp32 MFMA); bf16 inputs are read exactly and bf16
+ * outputs rounded to nearest even once.
+ * Execution: the 8 kernels run in order on `stream`; nothing else is used.
+ * The workspace (gdn_bwd_workspace_bytes(), 256-byte aligned) holds the
+ * recomputed chunk quantities in fp32: about (717 D + 8320 + 2 D^2) * 4
+ * bytes per (batch row, head, 64-token chunk), 3.2 GB at B = 1, T = 32760,
+ * H = 12, D = 128.
+ * Errors: as for gdn_fwd.  GDN_ERR_INVALID_ARG for a NULL required pointer,
+ * bad sizes, eps < 0 or not finite, or an output that overlaps an input,
+ * another output or the workspace; GDN_ERR_ALIGNMENT for a tensor not aligned
+ * to its element size; GDN_ERR_UNSUPPORTED for other D.
+ */
+typedef struct gdn_bwd_params {
+    int B, T, H, Dk, Dv;
+    gdn_dtype io_dtype;
+    const void *q, *k, *v;
+    const float *log_a, *beta;
+    const void *gate;
+    const float *conv_q, *conv_k, *conv_v;
+    const float *norm_w;      /* NULL: ones */
+    float eps_l2, eps_norm;
+    const float *S0;          /* NULL: zero initial state */
+    const void *dy;           /* gradient of the output y */
+    const float *dS_T;        /* gradient of the final state, or NULL */
+    void *dq, *dk, *dv, *dgate;
+    float *dlog_a, *dbeta;
+    float *dconv_q, *dconv_k, *dconv_v;
+    float *dnorm_w;           /* or NULL */
+    float *dS0;               /* or NULL */
+    void *workspace;
+    size_t workspace_bytes;
+} gdn_bwd_params;
+
+/* Workspace gdn_bwd needs (only B, T, H, Dk, Dv and io_dtype are read); 0 if
+ * the sizes are invalid. */
+size_t gdn_bwd_workspace_bytes(const gdn_bwd_params *p);
+gdn_status gdn_bwd(const gdn_bwd_params *p, struct ihipStream_t *stream);
+/* As gdn_bwd, with events[2 i] and events[2 i + 1] recorded on `stream`
+ * around kernel i (n_events >= 2 * gdn_bwd_launch_count()). */
+gdn_status gdn_bwd_timed(const gdn_bwd_params *p, struct ihipEvent_t **events, int n_events,
+                         struct ihipStream_t *stream);
+/* The number of kernels of a gdn_bwd call, and the name of kernel i
+ * (NULL out of range). */
+int gdn_bwd_launch_count(void);
+const char *gdn_bwd_launch_name(int i);
+
 /* Static, human-readable text for a status code. */
 const char *gdn_status_string(gdn_status s);
 

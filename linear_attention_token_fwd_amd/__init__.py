@@ -21,7 +21,8 @@ EXPORTS = ("gdn_fwd", "gdn_fwd_bidir", "gdn_fwd_workspace_bytes", "gdn_fwd_bidir
            "gdn_fwd_launch_count", "gdn_fwd_launch_name", "gdn_fwd_timed", "gdn_status_string",
            "gdn_in_proj", "gdn_out_proj", "gdn_mixer_workspace_bytes", "gdn_mixer_fwd", "gdn_mixer_fwd_timed",
            "gdn_fwd_varlen", "gdn_fwd_varlen_workspace_bytes", "gdn_set_graph_cache_limit",
-           "gdn_graph_cache_count")
+           "gdn_graph_cache_count", "gdn_bwd", "gdn_bwd_workspace_bytes", "gdn_bwd_timed",
+           "gdn_bwd_launch_count", "gdn_bwd_launch_name")
 
 
 class GdnFwdParams(ctypes.Structure):
@@ -65,6 +66,24 @@ class GdnMixerParams(ctypes.Structure):
         ("norm_w", ctypes.c_void_p), ("eps_l2", ctypes.c_float), ("eps_norm", ctypes.c_float),
         ("S0", ctypes.c_void_p), ("S_T", ctypes.c_void_p), ("w_out", ctypes.c_void_p), ("b_out", ctypes.c_void_p),
         ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class GdnBwdParams(ctypes.Structure):
+    """Mirror of ``gdn_bwd_params`` in include/gdn.h."""
+    _fields_ = [
+        ("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int),
+        ("Dk", ctypes.c_int), ("Dv", ctypes.c_int), ("io_dtype", ctypes.c_int),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("log_a", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("gate", ctypes.c_void_p),
+        ("conv_q", ctypes.c_void_p), ("conv_k", ctypes.c_void_p), ("conv_v", ctypes.c_void_p),
+        ("norm_w", ctypes.c_void_p), ("eps_l2", ctypes.c_float), ("eps_norm", ctypes.c_float),
+        ("S0", ctypes.c_void_p), ("dy", ctypes.c_void_p), ("dS_T", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p), ("dgate", ctypes.c_void_p),
+        ("dlog_a", ctypes.c_void_p), ("dbeta", ctypes.c_void_p),
+        ("dconv_q", ctypes.c_void_p), ("dconv_k", ctypes.c_void_p), ("dconv_v", ctypes.c_void_p),
+        ("dnorm_w", ctypes.c_void_p), ("dS0", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -118,6 +137,17 @@ def load(path: str | None = None):
     lib.gdn_mixer_fwd.restype = ctypes.c_int
     lib.gdn_mixer_fwd_timed.argtypes = [PM, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_void_p]
     lib.gdn_mixer_fwd_timed.restype = ctypes.c_int
+    PB = ctypes.POINTER(GdnBwdParams)
+    lib.gdn_bwd_workspace_bytes.argtypes = [PB]
+    lib.gdn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdn_bwd.argtypes = [PB, ctypes.c_void_p]
+    lib.gdn_bwd.restype = ctypes.c_int
+    lib.gdn_bwd_timed.argtypes = [PB, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_void_p]
+    lib.gdn_bwd_timed.restype = ctypes.c_int
+    lib.gdn_bwd_launch_count.argtypes = []
+    lib.gdn_bwd_launch_count.restype = ctypes.c_int
+    lib.gdn_bwd_launch_name.argtypes = [ctypes.c_int]
+    lib.gdn_bwd_launch_name.restype = ctypes.c_char_p
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_set_graph_cache_limit.argtypes = [ctypes.c_int]
@@ -441,3 +471,82 @@ def gdn_fwd_varlen(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, cu_seqlen
     if st != GDN_OK:
         raise GdnError(st, "gdn_fwd_varlen")
     return out, S_T
+
+
+# ---- backward pass
+
+BWD_GRADS = ("q", "k", "v", "log_a", "beta", "gate", "conv_q", "conv_k", "conv_v", "norm_w", "S0")
+
+
+def gdn_bwd_workspace_bytes(B: int, T: int, H: int, D: int, io_dtype: int = GDN_BF16) -> int:
+    p = GdnBwdParams()
+    p.B, p.T, p.H, p.Dk, p.Dv, p.io_dtype = B, T, H, D, D, io_dtype
+    return load().gdn_bwd_workspace_bytes(ctypes.byref(p))
+
+
+def gdn_bwd_launch_names() -> list:
+    lib = load()
+    return [lib.gdn_bwd_launch_name(i).decode() for i in range(lib.gdn_bwd_launch_count())]
+
+
+def bwd_params(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, dy, dS_T, grads: dict,
+               workspace, eps_l2=1e-6, eps_norm=1e-6) -> GdnBwdParams:
+    """Fill the backward params struct from torch tensors; grads maps the
+    names of BWD_GRADS to output tensors (norm_w and S0 may be None)."""
+    import torch
+    B, T, H, D = q.shape
+    p = GdnBwdParams()
+    p.B, p.T, p.H, p.Dk, p.Dv = B, T, H, D, v.shape[3]
+    p.io_dtype = GDN_BF16 if q.dtype == torch.bfloat16 else GDN_F32
+    p.q, p.k, p.v, p.gate = _ptr(q), _ptr(k), _ptr(v), _ptr(gate)
+    p.log_a, p.beta = _ptr(log_a), _ptr(beta)
+    p.conv_q, p.conv_k, p.conv_v = _ptr(conv_q), _ptr(conv_k), _ptr(conv_v)
+    p.norm_w, p.S0 = _ptr(norm_w), _ptr(S0)
+    p.eps_l2, p.eps_norm = eps_l2, eps_norm
+    p.dy, p.dS_T = _ptr(dy), _ptr(dS_T)
+    p.dq, p.dk, p.dv, p.dgate = (_ptr(grads.get(n)) for n in ("q", "k", "v", "gate"))
+    p.dlog_a, p.dbeta = _ptr(grads.get("log_a")), _ptr(grads.get("beta"))
+    p.dconv_q, p.dconv_k, p.dconv_v = (_ptr(grads.get(n)) for n in ("conv_q", "conv_k", "conv_v"))
+    p.dnorm_w, p.dS0 = _ptr(grads.get("norm_w")), _ptr(grads.get("S0"))
+    p.workspace = _ptr(workspace)
+    p.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return p
+
+
+def gdn_bwd(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, dy, dS_T=None,
+            eps_l2=1e-6, eps_norm=1e-6, want_norm_w=True, want_S0=True, out=None, workspace=None,
+            stream=None):
+    """Gradients of the layer forward (reverse = 0) given dy (and dS_T, the
+    final state's gradient, or None).  Returns a dict keyed by BWD_GRADS:
+    dq, dk, dv, dgate in the I/O dtype, the rest float32 (norm_w / S0: None
+    unless wanted).  out: an optional dict of preallocated output tensors
+    under the same keys."""
+    import torch
+    lib = load()
+    _prepare(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, None, None)
+    B, T, H, D = q.shape
+    _check(dy, "dy", q.dtype, (B, T, H, D))
+    _check(dS_T, "dS_T", torch.float32, (B, H, D, D))
+    dev, io, f32 = q.device, q.dtype, torch.float32
+    g = {n: torch.empty((B, T, H, D), dtype=io, device=dev) for n in ("q", "k", "v", "gate")}
+    g["log_a"] = torch.empty((B, T, H), dtype=f32, device=dev)
+    g["beta"] = torch.empty((B, T, H), dtype=f32, device=dev)
+    for n in ("conv_q", "conv_k", "conv_v"):
+        g[n] = torch.empty((H * D, 4), dtype=f32, device=dev)
+    g["norm_w"] = torch.empty((H, D), dtype=f32, device=dev) if want_norm_w else None
+    g["S0"] = torch.empty((B, H, D, D), dtype=f32, device=dev) if want_S0 else None
+    if out is not None:
+        for n, t in out.items():
+            if g.get(n) is not None:
+                _check(t, "d" + n, g[n].dtype, tuple(g[n].shape))
+            g[n] = t
+    need = gdn_bwd_workspace_bytes(B, T, H, D, GDN_BF16 if io == torch.bfloat16 else GDN_F32)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    p = bwd_params(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, dy, dS_T, g,
+                   workspace, eps_l2, eps_norm)
+    s = (stream if stream is not None else torch.cuda.current_stream(dev)).cuda_stream
+    st = lib.gdn_bwd(ctypes.byref(p), ctypes.c_void_p(s))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_bwd")
+    return g

@@ -9,8 +9,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdn.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("gdn_api.hip", "gdn_proj.hip")]
-HEADERS = [os.path.join(CSRC, f) for f in ("frag.hpp", "sync.hpp", "kernels.hpp", "gemm.hpp")] + [
+SOURCES = [os.path.join(CSRC, f) for f in ("gdn_api.hip", "gdn_proj.hip", "gdn_bwd.hip")]
+HEADERS = [os.path.join(CSRC, f) for f in ("frag.hpp", "sync.hpp", "kernels.hpp", "gemm.hpp", "bwd.hpp")] + [
     os.path.join(ROOT, "include", "gdn.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

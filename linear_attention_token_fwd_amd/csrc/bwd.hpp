@@ -1,0 +1,786 @@
+// bwd.hpp -- gfx950 kernels of the GDN layer's backward pass: the gradients
+// of the layer forward (short conv + SiLU, L2-normalised q and k, the gated
+// delta rule in 64-token chunks, the gated RMS normalisation) with respect to
+// every input.
+//
+// The backward follows the forward's chunking (Gated DeltaNet paper, section
+// 3.3, the chunkwise WY form; the LinMorph project page trains the converted
+// GDN blocks, which needs these gradients).  For chunk c with entry state S
+// (value rows, key columns), tokens as rows, g the cumulative log decay
+// inside the chunk, gam = e^g, gC = e^{g_last}, dl = e^{g_last - g}:
+//   A = strictly lower (b_i e^{g_i - g_j} k_i . k_j),  T = (I + A)^-1
+//   W = T diag(b gam) K,  U~ = T diag(b) V,  U = U~ - W S^T
+//   P = lower-inclusive (e^{g_i - g_j} q_i . k_j),  Q' = diag(gam) Q - P W
+//   O = Q' S^T + P U~,  S_next = gC S + U^T diag(dl) K
+// Given dO and dS_next, the entry-state gradient runs backwards over chunks,
+//   dS = gC dS_next - (dS_next (diag(dl) K)^T) W + dO^T Q',
+// and every other gradient of the chunk follows from S, dS_next and dO alone
+// (kernel bwd_grad_kernel lists the steps).
+//
+// Everything is fp32, on v_mfma_f32_16x16x4_f32.  The chunk quantities live
+// in the workspace as row-major fp32 arrays, one record per (batch row,
+// head, chunk).  Kernels, in launch order:
+//   bwd_prep_kernel      per chunk: recomputed q^, k^, v^; A, T, W, U~, P, Q', D K
+//   bwd_state_kernel     per 16 value rows: the forward chain, entry states
+//   bwd_out_kernel       per chunk: O, then the gated RMS norm's backward (dO, dgate)
+//   bwd_dstate_kernel    per 16 value rows: the entry-state gradients, last chunk first
+//   bwd_grad_kernel      per chunk: dq^, dk^, dv^, d log a, db
+//   bwd_norm_kernel      per token: L2 norm and SiLU backward, dz in place
+//   bwd_conv_kernel      per chunk: dq, dk, dv, conv-weight partial sums
+//   bwd_reduce_kernel    the conv-weight and norm-weight sums
+#pragma once
+#include "frag.hpp"
+
+namespace gdnb {
+
+using gdn::bf16;
+using gdn::floatx4;
+
+constexpr int C = 64;     // tokens per chunk
+constexpr int NT = 256;   // threads per workgroup (4 waves)
+
+// Offsets (in floats) inside one chunk record; all row-major.
+template <int D> struct Rec {
+    static constexpr int XQ = 0;             // q^  [64][D]
+    static constexpr int XK = 64 * D;        // k^
+    static constexpr int XV = 128 * D;       // v^
+    static constexpr int W = 192 * D;        // W
+    static constexpr int UT = 256 * D;       // U~
+    static constexpr int QP = 320 * D;       // Q'
+    static constexpr int DK = 384 * D;       // diag(dl) K
+    static constexpr int DO = 448 * D;       // dO
+    static constexpr int DXQ = 512 * D;      // dq^, then dz of q
+    static constexpr int DXK = 576 * D;      // dk^, then dz of k
+    static constexpr int DXV = 640 * D;      // dv^, then dz of v
+    static constexpr int TM = 704 * D;       // T [64][64]
+    static constexpr int P = TM + 64 * 64;   // P [64][64]
+    static constexpr int G = P + 64 * 64;    // g [64], then gC
+    static constexpr int SC = G + 128;       // entry state S [D][D]
+    static constexpr int DSN = SC + D * D;   // gradient of the exit state [D][D]
+    static constexpr int SIZE = DSN + D * D;
+};
+
+struct Args {
+    int B, T, H, NC;
+    const void *q, *k, *v, *gate, *dy;                 // [B, T, H, D], I/O dtype
+    const float *log_a, *beta;                         // [B, T, H]
+    const float *conv_q, *conv_k, *conv_v;             // [H D, 4]
+    const float *norm_w;                               // [H, D] or null (ones)
+    const float *S0, *dS_T;                            // [B, H, D, D] or null (zero)
+    float eps_l2, eps_norm;
+    void *dq, *dk, *dv, *dgate;                        // [B, T, H, D], I/O dtype
+    float *dlog_a, *dbeta;                             // [B, T, H]
+    float *dconv_q, *dconv_k, *dconv_v;                // [H D, 4]
+    float *dnorm_w;                                    // [H, D] or null
+    float *dS0;                                        // [B, H, D, D] or null
+    float *rec;                                        // B H NC chunk records
+    float *part_conv;                                  // [B NC H][3][D][4]
+    float *part_norm;                                  // [B NC H][D]
+};
+
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float sigm(float x) { return 1.0f / (1.0f + expf(-x)); }
+__device__ __forceinline__ float silu(float x) { return x * sigm(x); }
+__device__ __forceinline__ float dsilu(float x) {
+    const float s = sigm(x);
+    return s * (1.0f + x * (1.0f - s));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+// One 16 x 16 tile of acc + A B, A rows m0.. (16 x K), B columns n0.. (K x 16),
+// fp32 MFMA 16x16x4.  Lane (r, g) (r = lane % 16, g = lane / 16) supplies
+// k = k0 + 4 g + j to the j-th product of each 16-deep step, for A and B
+// alike, so the 4 products sum all 16 k.
+//   KA: A(m, k) at A[m lda + k] (k contiguous, read 4 at a time), else A[k lda + m]
+//   KB: B(k, n) at B[n ldb + k] (k contiguous), else B[k ldb + n]
+// acc[i] is the element (m0 + 4 g + i, n0 + r).
+template <bool KA, bool KB, int K>
+__device__ __forceinline__ floatx4 mm16(floatx4 acc, const float *A, int lda, int m0, const float *B, int ldb,
+                                        int n0) {
+    const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+#pragma unroll 4
+    for (int k0 = 0; k0 < K; k0 += 16) {
+        float a[4], b[4];
+        if constexpr (KA) {
+            const float4 t = *reinterpret_cast<const float4 *>(A + (size_t)(m0 + r) * lda + k0 + 4 * g);
+            a[0] = t.x; a[1] = t.y; a[2] = t.z; a[3] = t.w;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) a[j] = A[(size_t)(k0 + 4 * g + j) * lda + m0 + r];
+        }
+        if constexpr (KB) {
+            const float4 t = *reinterpret_cast<const float4 *>(B + (size_t)(n0 + r) * ldb + k0 + 4 * g);
+            b[0] = t.x; b[1] = t.y; b[2] = t.z; b[3] = t.w;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = B[(size_t)(k0 + 4 * g + j) * ldb + n0 + r];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+__device__ __forceinline__ floatx4 z4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
+
+template <int D> __device__ __forceinline__ float *record(const Args &a, int b, int h, int c) {
+    return a.rec + (((size_t)b * a.H + h) * a.NC + c) * (size_t)Rec<D>::SIZE;
+}
+
+// ---------------------------------------------------------------------------
+// Per chunk: q^, k^, v^ (short conv, SiLU, L2 norms, recomputed from the
+// inputs), the gates, A, T = (I + A)^-1, W, U~, P, Q' and D K.  Tokens past
+// the sequence's end are zero rows with b = 0 and log a = 0, which leave the
+// state and every gradient unchanged.
+template <class IO, int D>
+__global__ __launch_bounds__(NT) void bwd_prep_kernel(Args a) {
+    typedef Rec<D> R;
+    constexpr int LX = D + 4, LC = C + 4;
+    extern __shared__ __align__(16) float lds[];
+    float *sQ = lds, *sK = sQ + C * LX, *sV = sK + C * LX, *sT = sV + C * LX, *sM = sT + C * LC;
+    float *sg = sM + C * LC, *sb = sg + C, *sgam = sb + C;
+    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t0 = c * C;
+    const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, r = lane % 16, g = lane / 16;
+    float *rec = record<D>(a, b, h, c);
+
+    if (tid < 64) {
+        const int t = t0 + tid;
+        const bool valid = t < a.T;
+        float la = valid ? a.log_a[((size_t)b * a.T + t) * a.H + h] : 0.f;
+        const float be = valid ? a.beta[((size_t)b * a.T + t) * a.H + h] : 0.f;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const float y = __shfl_up(la, o, 64);
+            if (tid >= o) la += y;
+        }
+        sg[tid] = la;
+        sb[tid] = be;
+        sgam[tid] = expf(la);
+        rec[R::G + tid] = la;
+        if (tid == 63) rec[R::G + 64] = expf(la);
+    }
+    // short conv + SiLU of q, k, v (tap j multiplies x_{t-3+j}; zeros before the start)
+    {
+        const IO *src[3] = {static_cast<const IO *>(a.q), static_cast<const IO *>(a.k), static_cast<const IO *>(a.v)};
+        const float *cw[3] = {a.conv_q, a.conv_k, a.conv_v};
+        float *dst[3] = {sQ, sK, sV};
+        for (int idx = tid; idx < C * D; idx += NT) {
+            const int tl = idx / D, ch = idx % D, t = t0 + tl;
+#pragma unroll
+            for (int x = 0; x < 3; ++x) {
+                float out = 0.f;
+                if (t < a.T) {
+                    const float *wt = cw[x] + ((size_t)h * D + ch) * 4;
+                    float z = 0.f;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int s = t - 3 + j;
+                        if (s >= 0) z = fmaf(wt[j], to_f(src[x][(((size_t)b * a.T + s) * a.H + h) * D + ch]), z);
+                    }
+                    out = silu(z);
+                }
+                dst[x][tl * LX + ch] = out;
+            }
+        }
+    }
+    __syncthreads();
+    // L2 norms of the q and k rows: wave w takes rows 16w..16w+15
+    for (int rr = 0; rr < 16; ++rr) {
+        const int row = 16 * w + rr;
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            float *p = (x == 0 ? sQ : sK) + row * LX;
+            float ss = 0.f;
+            for (int ch = lane; ch < D; ch += 64) ss += p[ch] * p[ch];
+            ss = wave_sum(ss);
+            const float rho = 1.0f / sqrtf(ss + a.eps_l2);
+            for (int ch = lane; ch < D; ch += 64) p[ch] *= rho;
+        }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < C * D / 4; idx += NT) {
+        const int tl = idx / (D / 4), c4 = 4 * (idx % (D / 4));
+        *reinterpret_cast<float4 *>(rec + R::XQ + tl * D + c4) = *reinterpret_cast<const float4 *>(sQ + tl * LX + c4);
+        *reinterpret_cast<float4 *>(rec + R::XK + tl * D + c4) = *reinterpret_cast<const float4 *>(sK + tl * LX + c4);
+        *reinterpret_cast<float4 *>(rec + R::XV + tl * D + c4) = *reinterpret_cast<const float4 *>(sV + tl * LX + c4);
+    }
+    // A = strictly lower (b_i e^{g_i - g_j} k_i . k_j): wave w owns row block w
+    for (int nt = 0; nt < 4; ++nt) {
+        floatx4 acc = z4();
+        if (nt <= w) acc = mm16<true, true, D>(acc, sK, LX, 16 * w, sK, LX, 16 * nt);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * w + 4 * g + i, col = 16 * nt + r;
+            sM[row * LC + col] = col < row ? sb[row] * expf(sg[row] - sg[col]) * acc[i] : 0.f;
+        }
+    }
+    __syncthreads();
+    // T = (I + A)^-1 by forward substitution, column j on thread j
+    if (tid < 64) {
+        const int j = tid;
+        for (int i = 0; i < 64; ++i) sT[i * LC + j] = i == j ? 1.f : 0.f;
+        for (int i = j + 1; i < 64; ++i) {
+            float s = 0.f;
+            for (int m = j; m < i; ++m) s = fmaf(sM[i * LC + m], sT[m * LC + j], s);
+            sT[i * LC + j] = -s;
+        }
+    }
+    __syncthreads();
+    // T out; T' = T diag(b gam) into the A storage; diag(b) V in place
+    for (int idx = tid; idx < C * C; idx += NT) {
+        const int i = idx / C, j = idx % C;
+        const float t = sT[i * LC + j];
+        rec[R::TM + idx] = t;
+        sM[i * LC + j] = t * sb[j] * sgam[j];
+    }
+    for (int idx = tid; idx < C * D; idx += NT) {
+        const int tl = idx / D, ch = idx % D;
+        sV[tl * LX + ch] *= sb[tl];
+    }
+    __syncthreads();
+    // U~ = T diag(b) V
+    for (int nt = 0; nt < D / 16; ++nt) {
+        const floatx4 acc = mm16<true, false, C>(z4(), sT, LC, 16 * w, sV, LX, 16 * nt);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rec[R::UT + (16 * w + 4 * g + i) * D + 16 * nt + r] = acc[i];
+    }
+    __syncthreads();
+    // W = T diag(b gam) K, out and into the V storage
+    for (int nt = 0; nt < D / 16; ++nt) {
+        const floatx4 acc = mm16<true, false, C>(z4(), sM, LC, 16 * w, sK, LX, 16 * nt);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * w + 4 * g + i, col = 16 * nt + r;
+            rec[R::W + row * D + col] = acc[i];
+            sV[row * LX + col] = acc[i];
+        }
+    }
+    __syncthreads();
+    // P = lower-inclusive (e^{g_i - g_j} q_i . k_j), out and into the A storage
+    for (int nt = 0; nt < 4; ++nt) {
+        floatx4 acc = z4();
+        if (nt <= w) acc = mm16<true, true, D>(acc, sQ, LX, 16 * w, sK, LX, 16 * nt);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * w + 4 * g + i, col = 16 * nt + r;
+            const float p = col <= row ? expf(sg[row] - sg[col]) * acc[i] : 0.f;
+            sM[row * LC + col] = p;
+            rec[R::P + row * C + col] = p;
+        }
+    }
+    __syncthreads();
+    // Q' = diag(gam) Q - P W;  D K = diag(e^{g_last - g}) K
+    for (int nt = 0; nt < D / 16; ++nt) {
+        const floatx4 acc = mm16<true, false, C>(z4(), sM, LC, 16 * w, sV, LX, 16 * nt);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * w + 4 * g + i, col = 16 * nt + r;
+            rec[R::QP + row * D + col] = sgam[row] * sQ[row * LX + col] - acc[i];
+        }
+    }
+    const float glast = sg[63];
+    for (int idx = tid; idx < C * D; idx += NT) {
+        const int tl = idx / D, ch = idx % D;
+        rec[R::DK + idx] = expf(glast - sg[tl]) * sK[tl * LX + ch];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The forward chain over chunks for value rows 16 vb .. 16 vb + 15 of one
+// head: stores each chunk's entry state, then U = U~ - W S^T (wave w: tokens
+// 16w..) and S <- gC S + U^T D K.
+template <int D>
+__global__ __launch_bounds__(NT) void bwd_state_kernel(Args a) {
+    typedef Rec<D> R;
+    constexpr int LS = D + 4, LU = 16 + 4;
+    __shared__ __align__(16) float sS[16 * LS];
+    __shared__ __align__(16) float sU[C * LU];
+    const int vb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, r = lane % 16, g = lane / 16;
+    for (int idx = tid; idx < 16 * D; idx += NT) {
+        const int row = idx / D, col = idx % D;
+        sS[row * LS + col] = a.S0 ? a.S0[(((size_t)b * a.H + h) * D + 16 * vb + row) * D + col] : 0.f;
+    }
+    __syncthreads();
+    for (int c = 0; c < a.NC; ++c) {
+        float *rec = record<D>(a, b, h, c);
+        for (int idx = tid; idx < 16 * D; idx += NT) {
+            const int row = idx / D, col = idx % D;
+            rec[R::SC + (16 * vb + row) * D + col] = sS[row * LS + col];
+        }
+        {
+            const floatx4 acc = mm16<true, true, D>(z4(), rec + R::W, D, 16 * w, sS, LS, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tok = 16 * w + 4 * g + i;
+                sU[tok * LU + r] = rec[R::UT + tok * D + 16 * vb + r] - acc[i];
+            }
+        }
+        __syncthreads();
+        const float gC = rec[R::G + 64];
+        for (int nt = w; nt < D / 16; nt += 4) {
+            floatx4 acc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = gC * sS[(4 * g + i) * LS + 16 * nt + r];
+            acc = mm16<false, false, C>(acc, sU, LU, 0, rec + R::DK, D, 16 * nt);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sS[(4 * g + i) * LS + 16 * nt + r] = acc[i];
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Per chunk: O = Q' S^T + P U~ (wave w: tokens 16w..), then the backward of
+// y = O / sqrt(mean(O^2) + eps) * w * SiLU(gate): dO to the record, dgate
+// out, and this chunk's part of the norm weight's gradient.
+template <class IO, int D>
+__global__ __launch_bounds__(NT) void bwd_out_kernel(Args a) {
+    typedef Rec<D> R;
+    constexpr int NTL = D / 16;
+    __shared__ float sN[4][D];
+    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t0 = c * C;
+    const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, r = lane % 16, g = lane / 16;
+    float *rec = record<D>(a, b, h, c);
+    floatx4 o[NTL];
+    float ss[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nt = 0; nt < NTL; ++nt) {
+        o[nt] = mm16<true, true, D>(z4(), rec + R::QP, D, 16 * w, rec + R::SC, D, 16 * nt);
+        o[nt] = mm16<true, false, C>(o[nt], rec + R::P, C, 16 * w, rec + R::UT, D, 16 * nt);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ss[i] += o[nt][i] * o[nt][i];
+    }
+    float rr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rr[i] = 1.0f / sqrtf(gdn::group_sum<16>(ss[i]) / D + a.eps_norm);
+    const IO *gate = static_cast<const IO *>(a.gate);
+    const IO *dy = static_cast<const IO *>(a.dy);
+    IO *dgate = static_cast<IO *>(a.dgate);
+    float gt[NTL][4], dyv[NTL][4], dot[4] = {0.f, 0.f, 0.f, 0.f}, cs[NTL];
+#pragma unroll
+    for (int nt = 0; nt < NTL; ++nt) {
+        const int col = 16 * nt + r;
+        const float wn = a.norm_w ? a.norm_w[(size_t)h * D + col] : 1.f;
+        cs[nt] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = t0 + 16 * w + 4 * g + i;
+            const size_t off = (((size_t)b * a.T + t) * a.H + h) * D + col;
+            gt[nt][i] = t < a.T ? to_f(gate[off]) : 0.f;
+            dyv[nt][i] = t < a.T ? to_f(dy[off]) : 0.f;
+            const float n = o[nt][i] * rr[i], sgt = silu(gt[nt][i]);
+            dot[i] += dyv[nt][i] * wn * sgt * n;
+            cs[nt] += dyv[nt][i] * n * sgt;
+            if (t < a.T) dgate[off] = (IO)(dyv[nt][i] * n * wn * dsilu(gt[nt][i]));
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dot[i] = gdn::group_sum<16>(dot[i]) / D;
+#pragma unroll
+    for (int nt = 0; nt < NTL; ++nt) {
+        const int col = 16 * nt + r;
+        const float wn = a.norm_w ? a.norm_w[(size_t)h * D + col] : 1.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * w + 4 * g + i;
+            const float n = o[nt][i] * rr[i];
+            const float dn = dyv[nt][i] * wn * silu(gt[nt][i]);
+            rec[R::DO + row * D + col] = rr[i] * (dn - n * dot[i]);
+        }
+        // column sums over the wave's 16 rows: lanes r, r + 16, r + 32, r + 48
+        float s = cs[nt];
+        s += __shfl_xor(s, 16, 64);
+        s += __shfl_xor(s, 32, 64);
+        if (g == 0) sN[w][col] = s;
+    }
+    __syncthreads();
+    if (tid < D)
+        a.part_norm[(((size_t)b * a.NC + c) * a.H + h) * D + tid] = sN[0][tid] + sN[1][tid] + sN[2][tid] + sN[3][tid];
+}
+
+// ---------------------------------------------------------------------------
+// Entry-state gradients for value rows 16 vb .. of one head, last chunk
+// first: stores the exit-state gradient of each chunk, then
+// dS <- gC dS - (dS (D K)^T) W + dO^T Q'.
+template <int D>
+__global__ __launch_bounds__(NT) void bwd_dstate_kernel(Args a) {
+    typedef Rec<D> R;
+    constexpr int LS = D + 4, LXX = C + 4;
+    __shared__ __align__(16) float sD[16 * LS];
+    __shared__ __align__(16) float sX[16 * LXX];
+    const int vb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, r = lane % 16, g = lane / 16;
+    for (int idx = tid; idx < 16 * D; idx += NT) {
+        const int row = idx / D, col = idx % D;
+        sD[row * LS + col] = a.dS_T ? a.dS_T[(((size_t)b * a.H + h) * D + 16 * vb + row) * D + col] : 0.f;
+    }
+    __syncthreads();
+    for (int c = a.NC - 1; c >= 0; --c) {
+        float *rec = record<D>(a, b, h, c);
+        for (int idx = tid; idx < 16 * D; idx += NT) {
+            const int row = idx / D, col = idx % D;
+            rec[R::DSN + (16 * vb + row) * D + col] = sD[row * LS + col];
+        }
+        {
+            // X = dS (D K)^T: 16 value rows x 64 tokens, wave w tokens 16w..
+            const floatx4 acc = mm16<true, true, D>(z4(), sD, LS, 0, rec + R::DK, D, 16 * w);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sX[(4 * g + i) * LXX + 16 * w + r] = acc[i];
+        }
+        __syncthreads();
+        const float gC = rec[R::G + 64];
+        for (int nt = w; nt < D / 16; nt += 4) {
+            const floatx4 xw = mm16<true, false, C>(z4(), sX, LXX, 0, rec + R::W, D, 16 * nt);
+            const floatx4 oq = mm16<false, false, C>(z4(), rec + R::DO + 16 * vb, D, 0, rec + R::QP, D, 16 * nt);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float *p = sD + (4 * g + i) * LS + 16 * nt + r;
+                *p = gC * *p - xw[i] + oq[i];
+            }
+        }
+        __syncthreads();
+    }
+    if (a.dS0)
+        for (int idx = tid; idx < 16 * D; idx += NT) {
+            const int row = idx / D, col = idx % D;
+            a.dS0[(((size_t)b * a.H + h) * D + 16 * vb + row) * D + col] = sD[row * LS + col];
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Per chunk, given S (entry), dS' (exit-state gradient) and dO, wave w
+// owning tokens 16w..16w+15 of every [64 x D] and [64 x 64] result:
+//   U = U~ - W S^T
+//   dU = P^T dO + diag(dl) K dS'^T          d dl = rowdot(K dS'^T, U)
+//   dq^ = diag(gam) dO S + G K               d gam = rowdot(dO S, Q) + b rowdot(dR_W, K)
+//   dk^ = diag(dl) U dS' + diag(b gam) dR_W + F K + F^T K + G^T Q
+//   dW = -dU S,  dR_W = T^T dW,  dR_U = T^T dU,  dv^ = diag(b) dR_U
+//   db = gam rowdot(dR_W, K) + rowdot(dR_U, V) + rowsum(dA o E o K K^T)
+//   dA = -(dR_W W^T + dR_U U~^T) (strictly lower),  F = diag(b) (E o dA)
+//   dP = dO U^T (lower-inclusive),  G = E o dP     (E_ij = e^{g_i - g_j})
+//   dg = gam d gam - dl d dl + rowsum(M) - colsum(M),  M = dP o P + dA o A,
+//        plus gC <dS', S> + sum(dl d dl) on the last token;
+//   d log a = the suffix sums of dg inside the chunk.
+template <int D>
+__global__ __launch_bounds__(NT) void bwd_grad_kernel(Args a) {
+    typedef Rec<D> R;
+    constexpr int LX = D + 4, LC = C + 4, NTL = D / 16;
+    extern __shared__ __align__(16) float lds[];
+    float *L1 = lds, *L2 = L1 + C * LX, *L3 = L2 + C * LX;   // U then dR_W; dU; dW then dR_U
+    float *La = L3 + C * LX, *Lb = La + C * LC, *Lc = Lb + C * LC;  // G; F; M
+    float *vg = Lc + C * LC, *vb_ = vg + C, *vgam = vb_ + C, *vdl = vgam + C;
+    float *vdgam = vdl + C, *vddl = vdgam + C, *vdb = vddl + C, *vred = vdb + C;
+    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t0 = c * C;
+    const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, r = lane % 16, g = lane / 16;
+    const float *rec = record<D>(a, b, h, c);
+
+    if (tid < 64) {
+        const int t = t0 + tid;
+        const float gg = rec[R::G + tid];
+        vg[tid] = gg;
+        vb_[tid] = t < a.T ? a.beta[((size_t)b * a.T + t) * a.H + h] : 0.f;
+        vgam[tid] = expf(gg);
+        vdl[tid] = expf(rec[R::G + 63] - gg);
+    }
+    // <dS', S>
+    {
+        float s = 0.f;
+        for (int idx = tid; idx < D * D; idx += NT) s += rec[R::DSN + idx] * rec[R::SC + idx];
+        s = wave_sum(s);
+        if (lane == 0) vred[w] = s;
+    }
+    __syncthreads();
+    const float gC = rec[R::G + 64];
+
+    // U = U~ - W S^T
+#pragma unroll 1
+    for (int nt = 0; nt < NTL; ++nt) {
+        const floatx4 acc = mm16<true, true, D>(z4(), rec + R::W, D, 16 * w, rec + R::SC, D, 16 * nt);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * w + 4 * g + i, col = 16 * nt + r;
+            L1[row * LX + col] = rec[R::UT + row * D + col] - acc[i];
+        }
+    }
+    __syncthreads();
+
+    float pgam[4] = {0.f, 0.f, 0.f, 0.f}, pdl[4] = {0.f, 0.f, 0.f, 0.f}, pdb[4] = {0.f, 0.f, 0.f, 0.f};
+    floatx4 dQ[NTL], dK[NTL];
+    float rgam[4], rdl[4], rb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 16 * w + 4 * g + i;
+        rgam[i] = vgam[row];
+        rdl[i] = vdl[row];
+        rb[i] = vb_[row];
+    }
+#pragma unroll
+    for (int nt = 0; nt < NTL; ++nt) {
+        const int col = 16 * nt + r;
+        // dU, d dl
+        const floatx4 kd = mm16<true, true, D>(z4(), rec + R::XK, D, 16 * w, rec + R::DSN, D, 16 * nt);
+        const floatx4 pt = mm16<false, false, C>(z4(), rec + R::P, C, 16 * w, rec + R::DO, D, 16 * nt);
+        // dO S
+        const floatx4 dos = mm16<true, false, D>(z4(), rec + R::DO, D, 16 * w, rec + R::SC, D, 16 * nt);
+        // U dS'
+        const floatx4 uds = mm16<true, false, D>(z4(), L1, LX, 16 * w, rec + R::DSN, D, 16 * nt);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * w + 4 * g + i;
+            L2[row * LX + col] = pt[i] + rdl[i] * kd[i];
+            pdl[i] += kd[i] * L1[row * LX + col];
+            dQ[nt][i] = rgam[i] * dos[i];
+            pgam[i] += dos[i] * rec[R::XQ + row * D + col];
+            dK[nt][i] = rdl[i] * uds[i];
+        }
+    }
+    // dP = dO U^T (lower-inclusive): G = E o dP, M = dP o P
+#pragma unroll 1
+    for (int nt = 0; nt < 4; ++nt) {
+        floatx4 acc = z4();
+        if (nt <= w) acc = mm16<true, true, D>(acc, rec + R::DO, D, 16 * w, L1, LX, 16 * nt);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * w + 4 * g + i, col = 16 * nt + r;
+            const bool on = col <= row;
+            La[row * LC + col] = on ? expf(vg[row] - vg[col]) * acc[i] : 0.f;
+            Lc[row * LC + col] = on ? acc[i] * rec[R::P + row * C + col] : 0.f;
+        }
+    }
+    __syncthreads();
+    // dW = -dU S
+#pragma unroll 1
+    for (int nt = 0; nt < NTL; ++nt) {
+        const floatx4 acc = mm16<true, false, D>(z4(), L2, LX, 16 * w, rec + R::SC, D, 16 * nt);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) L3[(16 * w + 4 * g + i) * LX + 16 * nt + r] = -acc[i];
+    }
+    __syncthreads();
+    // dR_W = T^T dW (into the U storage)
+#pragma unroll
+    for (int nt = 0; nt < NTL; ++nt) {
+        const int col = 16 * nt + r;
+        const floatx4 acc = mm16<false, false, C>(z4(), rec + R::TM, C, 16 * w, L3, LX, 16 * nt);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * w + 4 * g + i;
+            L1[row * LX + col] = acc[i];
+            dK[nt][i] += rb[i] * rgam[i] * acc[i];
+            const float rk = acc[i] * rec[R::XK + row * D + col];
+            pgam[i] += rb[i] * rk;
+            pdb[i] += rgam[i] * rk;
+        }
+    }
+    __syncthreads();
+    // dR_U = T^T dU (into the dW storage), dv^ = diag(b) dR_U
+    float *dxv = const_cast<float *>(rec) + R::DXV;
+#pragma unroll 1
+    for (int nt = 0; nt < NTL; ++nt) {
+        const int col = 16 * nt + r;
+        const floatx4 acc = mm16<false, false, C>(z4(), rec + R::TM, C, 16 * w, L2, LX, 16 * nt);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * w + 4 * g + i;
+            L3[row * LX + col] = acc[i];
+            dxv[row * D + col] = rb[i] * acc[i];
+            pdb[i] += acc[i] * rec[R::XV + row * D + col];
+        }
+    }
+    __syncthreads();
+    // dA = -(dR_W W^T + dR_U U~^T) (strictly lower), F = diag(b) (E o dA), M += dA o A
+#pragma unroll 1
+    for (int nt = 0; nt < 4; ++nt) {
+        floatx4 acc = z4(), kk = z4();
+        if (nt <= w) {
+            acc = mm16<true, true, D>(acc, L1, LX, 16 * w, rec + R::W, D, 16 * nt);
+            acc = mm16<true, true, D>(acc, L3, LX, 16 * w, rec + R::UT, D, 16 * nt);
+            kk = mm16<true, true, D>(kk, rec + R::XK, D, 16 * w, rec + R::XK, D, 16 * nt);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * w + 4 * g + i, col = 16 * nt + r;
+            float f = 0.f;
+            if (col < row) {
+                const float e = expf(vg[row] - vg[col]), da = -acc[i];
+                f = rb[i] * e * da;
+                pdb[i] += e * da * kk[i];
+                Lc[row * LC + col] += f * kk[i];
+            }
+            Lb[row * LC + col] = f;
+        }
+    }
+    __syncthreads();
+    // dk^ += F K + F^T K + G^T Q;  dq^ += G K
+    float *dxq = const_cast<float *>(rec) + R::DXQ, *dxk = const_cast<float *>(rec) + R::DXK;
+#pragma unroll
+    for (int nt = 0; nt < NTL; ++nt) {
+        dK[nt] = mm16<true, false, C>(dK[nt], Lb, LC, 16 * w, rec + R::XK, D, 16 * nt);
+        dK[nt] = mm16<false, false, C>(dK[nt], Lb, LC, 16 * w, rec + R::XK, D, 16 * nt);
+        dK[nt] = mm16<false, false, C>(dK[nt], La, LC, 16 * w, rec + R::XQ, D, 16 * nt);
+        dQ[nt] = mm16<true, false, C>(dQ[nt], La, LC, 16 * w, rec + R::XK, D, 16 * nt);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * w + 4 * g + i, col = 16 * nt + r;
+            dxq[row * D + col] = dQ[nt][i];
+            dxk[row * D + col] = dK[nt][i];
+        }
+    }
+    // per-row sums over the 16 lanes of a row
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float sg_ = gdn::group_sum<16>(pgam[i]), sd = gdn::group_sum<16>(pdl[i]), sb = gdn::group_sum<16>(pdb[i]);
+        if (r == 0) {
+            const int row = 16 * w + 4 * g + i;
+            vdgam[row] = sg_;
+            vddl[row] = sd;
+            vdb[row] = sb;
+        }
+    }
+    __syncthreads();
+    if (tid < 64) {
+        const int t = tid;
+        float rs = 0.f, cs = 0.f;
+        for (int j = 0; j < 64; ++j) {
+            rs += Lc[t * LC + j];
+            cs += Lc[j * LC + t];
+        }
+        const float e = vdl[t] * vddl[t];
+        float dg = vgam[t] * vdgam[t] - e + rs - cs;
+        const float tot = wave_sum(e);
+        if (t == 63) dg += gC * (vred[0] + vred[1] + vred[2] + vred[3]) + tot;
+        // suffix sums: d log a_t = sum over r >= t of dg_r
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const float y = __shfl_down(dg, o, 64);
+            if (t + o < 64) dg += y;
+        }
+        const int tt = t0 + t;
+        if (tt < a.T) {
+            a.dlog_a[((size_t)b * a.T + tt) * a.H + h] = dg;
+            a.dbeta[((size_t)b * a.T + tt) * a.H + h] = vdb[t];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Per token row (wave = one token of one head): the backward of the L2 norm
+// (q, k) and of SiLU; dz replaces dq^, dk^, dv^ in the record.
+template <class IO, int D>
+__global__ __launch_bounds__(NT) void bwd_norm_kernel(Args a) {
+    typedef Rec<D> R;
+    constexpr int PER = D / 64;
+    const int h = blockIdx.y, b = blockIdx.z, w = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const int t = blockIdx.x * 4 + w;
+    if (t >= a.T) return;
+    float *rec = record<D>(a, b, h, t / C);
+    const int tl = t % C;
+    const IO *src[3] = {static_cast<const IO *>(a.q), static_cast<const IO *>(a.k), static_cast<const IO *>(a.v)};
+    const float *cw[3] = {a.conv_q, a.conv_k, a.conv_v};
+    const int dxo[3] = {R::DXQ, R::DXK, R::DXV};
+#pragma unroll
+    for (int x = 0; x < 3; ++x) {
+        float z[PER], s[PER], dx[PER], ss = 0.f, dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int ch = lane + 64 * e;
+            const float *wt = cw[x] + ((size_t)h * D + ch) * 4;
+            float zz = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int sp = t - 3 + j;
+                if (sp >= 0) zz = fmaf(wt[j], to_f(src[x][(((size_t)b * a.T + sp) * a.H + h) * D + ch]), zz);
+            }
+            z[e] = zz;
+            s[e] = silu(zz);
+            dx[e] = rec[dxo[x] + tl * D + ch];
+            ss += s[e] * s[e];
+        }
+        if (x < 2) {
+            ss = wave_sum(ss);
+            const float rho = 1.0f / sqrtf(ss + a.eps_l2);
+#pragma unroll
+            for (int e = 0; e < PER; ++e) dot += s[e] * rho * dx[e];
+            dot = wave_sum(dot);
+#pragma unroll
+            for (int e = 0; e < PER; ++e) dx[e] = rho * (dx[e] - s[e] * rho * dot);
+        }
+#pragma unroll
+        for (int e = 0; e < PER; ++e) rec[dxo[x] + tl * D + lane + 64 * e] = dx[e] * dsilu(z[e]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Per chunk: dx_t = sum_j w_j dz_{t+3-j} (dz zero past the end) for q, k, v,
+// and this chunk's sums dz_t x_{t-3+j} for the conv weights.  Thread: one
+// channel, a slice of the chunk's tokens.
+template <class IO, int D>
+__global__ __launch_bounds__(NT) void bwd_conv_kernel(Args a) {
+    typedef Rec<D> R;
+    constexpr int SL = NT / D, TPS = C / SL;  // token slices, tokens per slice
+    __shared__ float sP[SL][3 * D * 4];
+    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t0 = c * C;
+    const int ch = threadIdx.x % D, sl = threadIdx.x / D;
+    const IO *src[3] = {static_cast<const IO *>(a.q), static_cast<const IO *>(a.k), static_cast<const IO *>(a.v)};
+    IO *dst[3] = {static_cast<IO *>(a.dq), static_cast<IO *>(a.dk), static_cast<IO *>(a.dv)};
+    const float *cw[3] = {a.conv_q, a.conv_k, a.conv_v};
+    const int dxo[3] = {R::DXQ, R::DXK, R::DXV};
+#pragma unroll
+    for (int x = 0; x < 3; ++x) {
+        float wt[4], pw[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wt[j] = cw[x][((size_t)h * D + ch) * 4 + j];
+        for (int tl = sl * TPS; tl < (sl + 1) * TPS; ++tl) {
+            const int t = t0 + tl;
+            if (t >= a.T) break;
+            const float dz = record<D>(a, b, h, c)[dxo[x] + tl * D + ch];
+            float dx = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int u = t + 3 - j;  // the output that x_t feeds through tap j
+                if (u < a.T) dx = fmaf(wt[j], record<D>(a, b, h, u / C)[dxo[x] + (u % C) * D + ch], dx);
+                const int sp = t - 3 + j;
+                if (sp >= 0) pw[j] = fmaf(dz, to_f(src[x][(((size_t)b * a.T + sp) * a.H + h) * D + ch]), pw[j]);
+            }
+            dst[x][(((size_t)b * a.T + t) * a.H + h) * D + ch] = (IO)dx;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sP[sl][(x * D + ch) * 4 + j] = pw[j];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 3 * D * 4; idx += NT) {
+        float s = 0.f;
+#pragma unroll
+        for (int q = 0; q < SL; ++q) s += sP[q][idx];
+        a.part_conv[(((size_t)b * a.NC + c) * a.H + h) * (3 * D * 4) + idx] = s;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The conv weights' and the norm weight's gradients: sums of the per-chunk
+// parts over batch rows and chunks, in a fixed order.
+template <int D>
+__global__ __launch_bounds__(NT) void bwd_reduce_kernel(Args a) {
+    const int idx = blockIdx.x * NT + threadIdx.x;
+    const int nconv = a.H * 3 * D * 4;
+    if (idx < nconv) {
+        const int h = idx / (3 * D * 4), rem = idx % (3 * D * 4), x = rem / (D * 4), e = rem % (D * 4);
+        float s = 0.f;
+        for (int bc = 0; bc < a.B * a.NC; ++bc) s += a.part_conv[((size_t)bc * a.H + h) * (3 * D * 4) + rem];
+        float *dst = x == 0 ? a.dconv_q : (x == 1 ? a.dconv_k : a.dconv_v);
+        dst[(size_t)h * D * 4 + e] = s;
+    } else if (idx < nconv + a.H * D && a.dnorm_w) {
+        const int j = idx - nconv;
+        const int h = j / D, ch = j % D;
+        float s = 0.f;
+        for (int bc = 0; bc < a.B * a.NC; ++bc) s += a.part_norm[((size_t)bc * a.H + h) * D + ch];
+        a.dnorm_w[j] = s;
+    }
+}
+
+}  // namespace gdnb

@@ -1,0 +1,228 @@
+// gdn_bwd.hip -- host side of gdn_bwd (include/gdn.h): argument checks,
+// workspace carve-up and the eight launches of the backward pass.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+
+#include "../../include/gdn.h"
+#include "bwd.hpp"
+
+namespace {
+
+using gdn::bf16;
+using gdnb::NT;
+
+constexpr size_t kAlign = 256;
+constexpr int kLaunches = 8;
+const char *const kNames[kLaunches] = {"bwd_prep_kernel", "bwd_state_kernel", "bwd_out_kernel", "bwd_dstate_kernel",
+                                       "bwd_grad_kernel", "bwd_norm_kernel",  "bwd_conv_kernel", "bwd_reduce_kernel"};
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int n_chunks(int T) { return (T + gdnb::C - 1) / gdnb::C; }
+size_t elem_size(gdn_dtype d) { return d == GDN_BF16 ? 2 : 4; }
+
+size_t rec_floats(int D) { return D == 128 ? gdnb::Rec<128>::SIZE : gdnb::Rec<64>::SIZE; }
+
+struct Layout {
+    size_t rec, part_conv, part_norm, total;
+};
+
+Layout layout(const gdn_bwd_params *p) {
+    const size_t B = p->B, H = p->H, D = p->Dk, NC = n_chunks(p->T);
+    Layout L;
+    L.rec = 0;
+    L.part_conv = round_up(B * H * NC * rec_floats(p->Dk) * sizeof(float));
+    L.part_norm = L.part_conv + round_up(B * NC * H * 12 * D * sizeof(float));
+    L.total = L.part_norm + round_up(B * NC * H * D * sizeof(float));
+    return L;
+}
+
+bool sizes_ok(const gdn_bwd_params *p) {
+    if (!p) return false;
+    if (p->B < 1 || p->T < 1 || p->H < 1 || p->Dk < 1 || p->Dv < 1) return false;
+    if (p->io_dtype != GDN_F32 && p->io_dtype != GDN_BF16) return false;
+    if (p->H > 65535 || p->B > 65535) return false;
+    // element counts inside one launch's index arithmetic, and the chunk grid
+    if ((double)p->B * p->T * p->H * (double)p->Dk > 4.0e12) return false;
+    if (n_chunks(p->T) > 1 << 30) return false;
+    return true;
+}
+
+struct Span {
+    uintptr_t lo, hi;
+};
+Span span(const void *ptr, size_t bytes) { return Span{(uintptr_t)ptr, (uintptr_t)ptr + bytes}; }
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+bool aligned(const void *ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+gdn_status validate(const gdn_bwd_params *p) {
+    if (!sizes_ok(p)) return GDN_ERR_INVALID_ARG;
+    if (p->Dk != p->Dv) return GDN_ERR_UNSUPPORTED;
+    if (p->Dk != 64 && p->Dk != 128) return GDN_ERR_UNSUPPORTED;
+    if (!p->q || !p->k || !p->v || !p->log_a || !p->beta || !p->gate || !p->conv_q || !p->conv_k || !p->conv_v ||
+        !p->dy || !p->dq || !p->dk || !p->dv || !p->dgate || !p->dlog_a || !p->dbeta || !p->dconv_q ||
+        !p->dconv_k || !p->dconv_v)
+        return GDN_ERR_INVALID_ARG;
+    if (!(p->eps_l2 >= 0.f) || !(p->eps_norm >= 0.f) || !std::isfinite(p->eps_l2) || !std::isfinite(p->eps_norm))
+        return GDN_ERR_INVALID_ARG;
+    const size_t B = p->B, T = p->T, H = p->H, D = p->Dk, es = elem_size(p->io_dtype);
+    const size_t tok = B * T * H * D * es, gates = B * T * H * 4, conv = H * D * 16, st = B * H * D * D * 4;
+    const Span in[] = {span(p->q, tok),      span(p->k, tok),      span(p->v, tok),
+                       span(p->gate, tok),   span(p->dy, tok),     span(p->log_a, gates),
+                       span(p->beta, gates), span(p->conv_q, conv), span(p->conv_k, conv),
+                       span(p->conv_v, conv), span(p->norm_w, p->norm_w ? H * D * 4 : 0),
+                       span(p->S0, p->S0 ? st : 0), span(p->dS_T, p->dS_T ? st : 0)};
+    const Span out[] = {span(p->dq, tok),          span(p->dk, tok),          span(p->dv, tok),
+                        span(p->dgate, tok),       span(p->dlog_a, gates),    span(p->dbeta, gates),
+                        span(p->dconv_q, conv),    span(p->dconv_k, conv),    span(p->dconv_v, conv),
+                        span(p->dnorm_w, p->dnorm_w ? H * D * 4 : 0), span(p->dS0, p->dS0 ? st : 0),
+                        span(p->workspace, p->workspace ? p->workspace_bytes : 0)};
+    const int nout = sizeof(out) / sizeof(out[0]);
+    for (int i = 0; i < nout; ++i) {
+        for (const Span &s : in)
+            if (overlap(out[i], s)) return GDN_ERR_INVALID_ARG;
+        for (int j = i + 1; j < nout; ++j)
+            if (overlap(out[i], out[j])) return GDN_ERR_INVALID_ARG;
+    }
+    const void *io[] = {p->q, p->k, p->v, p->gate, p->dy, p->dq, p->dk, p->dv, p->dgate};
+    for (const void *ptr : io)
+        if (!aligned(ptr, es)) return GDN_ERR_ALIGNMENT;
+    const void *f32[] = {p->log_a, p->beta, p->conv_q, p->conv_k, p->conv_v, p->norm_w, p->S0, p->dS_T,
+                         p->dlog_a, p->dbeta, p->dconv_q, p->dconv_k, p->dconv_v, p->dnorm_w, p->dS0};
+    for (const void *ptr : f32)
+        if (ptr && !aligned(ptr, 4)) return GDN_ERR_ALIGNMENT;
+    if (!p->workspace || p->workspace_bytes < layout(p).total) return GDN_ERR_WORKSPACE;
+    if (!aligned(p->workspace, kAlign)) return GDN_ERR_ALIGNMENT;
+    return GDN_OK;
+}
+
+template <int D> size_t prep_lds() { return (3 * 64 * (D + 4) + 2 * 64 * 68 + 3 * 64) * sizeof(float); }
+template <int D> size_t grad_lds() { return (3 * 64 * (D + 4) + 3 * 64 * 68 + 8 * 64) * sizeof(float); }
+
+gdn_status set_attributes() {
+    static std::once_flag once;
+    static gdn_status result = GDN_OK;
+    std::call_once(once, [] {
+        struct A {
+            const void *fn;
+            size_t lds;
+        } attrs[] = {
+            {reinterpret_cast<const void *>(&gdnb::bwd_prep_kernel<bf16, 128>), prep_lds<128>()},
+            {reinterpret_cast<const void *>(&gdnb::bwd_prep_kernel<bf16, 64>), prep_lds<64>()},
+            {reinterpret_cast<const void *>(&gdnb::bwd_prep_kernel<float, 128>), prep_lds<128>()},
+            {reinterpret_cast<const void *>(&gdnb::bwd_prep_kernel<float, 64>), prep_lds<64>()},
+            {reinterpret_cast<const void *>(&gdnb::bwd_grad_kernel<128>), grad_lds<128>()},
+            {reinterpret_cast<const void *>(&gdnb::bwd_grad_kernel<64>), grad_lds<64>()},
+        };
+        for (const A &a : attrs)
+            if (hipFuncSetAttribute(a.fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)a.lds) != hipSuccess)
+                result = GDN_ERR_HIP;
+    });
+    return result;
+}
+
+template <class IO, int D>
+gdn_status launch_all(const gdn_bwd_params *p, hipEvent_t *ev, hipStream_t s) {
+    using namespace gdnb;
+    const Layout L = layout(p);
+    Args a;
+    a.B = p->B, a.T = p->T, a.H = p->H, a.NC = n_chunks(p->T);
+    a.q = p->q, a.k = p->k, a.v = p->v, a.gate = p->gate, a.dy = p->dy;
+    a.log_a = p->log_a, a.beta = p->beta;
+    a.conv_q = p->conv_q, a.conv_k = p->conv_k, a.conv_v = p->conv_v, a.norm_w = p->norm_w;
+    a.S0 = p->S0, a.dS_T = p->dS_T;
+    a.eps_l2 = p->eps_l2, a.eps_norm = p->eps_norm;
+    a.dq = p->dq, a.dk = p->dk, a.dv = p->dv, a.dgate = p->dgate;
+    a.dlog_a = p->dlog_a, a.dbeta = p->dbeta;
+    a.dconv_q = p->dconv_q, a.dconv_k = p->dconv_k, a.dconv_v = p->dconv_v;
+    a.dnorm_w = p->dnorm_w, a.dS0 = p->dS0;
+    char *ws = static_cast<char *>(p->workspace);
+    a.rec = reinterpret_cast<float *>(ws + L.rec);
+    a.part_conv = reinterpret_cast<float *>(ws + L.part_conv);
+    a.part_norm = reinterpret_cast<float *>(ws + L.part_norm);
+
+    const dim3 chunks(a.NC, p->H, p->B), rows(D / 16, p->H, p->B), tokens((p->T + 3) / 4, p->H, p->B);
+    const int nred = p->H * D * 13;
+    const dim3 red((nred + NT - 1) / NT);
+    int i = 0;
+    auto pre = [&] {
+        if (ev) (void)hipEventRecord(ev[2 * i], s);
+    };
+    auto post = [&]() -> bool {
+        if (hipGetLastError() != hipSuccess) return false;
+        if (ev) (void)hipEventRecord(ev[2 * i + 1], s);
+        ++i;
+        return true;
+    };
+    pre();
+    bwd_prep_kernel<IO, D><<<chunks, NT, prep_lds<D>(), s>>>(a);
+    if (!post()) return GDN_ERR_HIP;
+    pre();
+    bwd_state_kernel<D><<<rows, NT, 0, s>>>(a);
+    if (!post()) return GDN_ERR_HIP;
+    pre();
+    bwd_out_kernel<IO, D><<<chunks, NT, 0, s>>>(a);
+    if (!post()) return GDN_ERR_HIP;
+    pre();
+    bwd_dstate_kernel<D><<<rows, NT, 0, s>>>(a);
+    if (!post()) return GDN_ERR_HIP;
+    pre();
+    bwd_grad_kernel<D><<<chunks, NT, grad_lds<D>(), s>>>(a);
+    if (!post()) return GDN_ERR_HIP;
+    pre();
+    bwd_norm_kernel<IO, D><<<tokens, NT, 0, s>>>(a);
+    if (!post()) return GDN_ERR_HIP;
+    pre();
+    bwd_conv_kernel<IO, D><<<chunks, NT, 0, s>>>(a);
+    if (!post()) return GDN_ERR_HIP;
+    pre();
+    bwd_reduce_kernel<D><<<red, NT, 0, s>>>(a);
+    if (!post()) return GDN_ERR_HIP;
+    return GDN_OK;
+}
+
+gdn_status call(const gdn_bwd_params *p, hipEvent_t *ev, int n_ev, hipStream_t s) {
+    gdn_status st = validate(p);
+    if (st != GDN_OK) return st;
+    if (ev && n_ev < 2 * kLaunches) return GDN_ERR_INVALID_ARG;
+    st = set_attributes();
+    if (st != GDN_OK) return st;
+    if (p->io_dtype == GDN_BF16)
+        return p->Dk == 128 ? launch_all<bf16, 128>(p, ev, s) : launch_all<bf16, 64>(p, ev, s);
+    return p->Dk == 128 ? launch_all<float, 128>(p, ev, s) : launch_all<float, 64>(p, ev, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gdn_bwd_workspace_bytes(const gdn_bwd_params *p) {
+    if (!sizes_ok(p) || p->Dk != p->Dv || (p->Dk != 64 && p->Dk != 128)) return 0;
+    return layout(p).total;
+}
+
+gdn_status gdn_bwd(const gdn_bwd_params *p, struct ihipStream_t *stream) {
+    try {
+        return call(p, nullptr, 0, stream);
+    } catch (...) {
+        return GDN_ERR_HIP;
+    }
+}
+
+gdn_status gdn_bwd_timed(const gdn_bwd_params *p, struct ihipEvent_t **events, int n_events,
+                         struct ihipStream_t *stream) {
+    if (!events) return GDN_ERR_INVALID_ARG;
+    try {
+        return call(p, events, n_events, stream);
+    } catch (...) {
+        return GDN_ERR_HIP;
+    }
+}
+
+int gdn_bwd_launch_count(void) { return kLaunches; }
+
+const char *gdn_bwd_launch_name(int i) { return i >= 0 && i < kLaunches ? kNames[i] : nullptr; }
+
+}  // extern "C"

@@ -34,7 +34,7 @@ def lib():
 
 def test_every_declared_function_is_exported_and_bound(lib):
     decl = declared_functions()
-    assert len(decl) == 17, decl
+    assert len(decl) == 22, decl
     assert set(decl) == set(gdn.EXPORTS)
     for name in decl:
         fn = getattr(lib, name)  # AttributeError if the library does not export it
@@ -308,3 +308,80 @@ def test_varlen_validation(lib):
     q.Dk = q.Dv = 96
     q.workspace_bytes = 1 << 30
     assert lib.gdn_fwd_varlen(ctypes.byref(q), cu, None) == gdn.GDN_ERR_UNSUPPORTED
+
+
+# ---- the backward pass
+
+def fake_bwd(lib, B=2, T=300, H=3, D=128, io=gdn.GDN_BF16):
+    p = gdn.GdnBwdParams()
+    p.B, p.T, p.H, p.Dk, p.Dv, p.io_dtype = B, T, H, D, D, io
+    base, step = 1 << 44, 1 << 36
+    names = [f[0] for f in gdn.GdnBwdParams._fields_ if f[1] is ctypes.c_void_p]
+    for i, nm in enumerate(names):
+        setattr(p, nm, base + i * step)
+    p.eps_l2 = p.eps_norm = 1e-6
+    p.workspace_bytes = lib.gdn_bwd_workspace_bytes(ctypes.byref(p))
+    assert p.workspace_bytes > 0
+    return p
+
+
+def test_bwd_workspace_bytes(lib):
+    p = fake_bwd(lib, B=1, T=32760, H=12, D=128)
+    NC, D = 512, 128
+    per_chunk = (717 * D + 8320 + 2 * D * D) * 4
+    assert abs(p.workspace_bytes - 12 * NC * per_chunk) <= 3 * 256
+    q = gdn.GdnBwdParams()
+    q.B, q.T, q.H, q.Dk, q.Dv, q.io_dtype = 1, 100, 2, 96, 96, gdn.GDN_BF16
+    assert lib.gdn_bwd_workspace_bytes(ctypes.byref(q)) == 0
+    assert lib.gdn_bwd_workspace_bytes(None) == 0
+
+
+def test_bwd_launch_names(lib):
+    assert lib.gdn_bwd_launch_count() == 8
+    names = gdn.gdn_bwd_launch_names()
+    assert names[0] == "bwd_prep_kernel" and names[-1] == "bwd_reduce_kernel" and len(set(names)) == 8
+    assert lib.gdn_bwd_launch_name(8) is None and lib.gdn_bwd_launch_name(-1) is None
+
+
+BWD_CASES = [
+    ("dy NULL", lambda p: setattr(p, "dy", None), gdn.GDN_ERR_INVALID_ARG),
+    ("dq NULL", lambda p: setattr(p, "dq", None), gdn.GDN_ERR_INVALID_ARG),
+    ("dconv_v NULL", lambda p: setattr(p, "dconv_v", None), gdn.GDN_ERR_INVALID_ARG),
+    ("eps_norm < 0", lambda p: setattr(p, "eps_norm", -1.0), gdn.GDN_ERR_INVALID_ARG),
+    ("eps_l2 inf", lambda p: setattr(p, "eps_l2", float("inf")), gdn.GDN_ERR_INVALID_ARG),
+    ("B = 0", lambda p: setattr(p, "B", 0), gdn.GDN_ERR_INVALID_ARG),
+    ("io dtype 7", lambda p: setattr(p, "io_dtype", 7), gdn.GDN_ERR_INVALID_ARG),
+    ("Dk != Dv", lambda p: setattr(p, "Dv", 64), gdn.GDN_ERR_UNSUPPORTED),
+    ("D = 32", lambda p: (setattr(p, "Dk", 32), setattr(p, "Dv", 32)), gdn.GDN_ERR_UNSUPPORTED),
+    ("dq misaligned", lambda p: setattr(p, "dq", p.dq + 1), gdn.GDN_ERR_ALIGNMENT),
+    ("dlog_a misaligned", lambda p: setattr(p, "dlog_a", p.dlog_a + 2), gdn.GDN_ERR_ALIGNMENT),
+    ("workspace NULL", lambda p: setattr(p, "workspace", None), gdn.GDN_ERR_WORKSPACE),
+    ("workspace too small", lambda p: setattr(p, "workspace_bytes", p.workspace_bytes - 1), gdn.GDN_ERR_WORKSPACE),
+    ("workspace misaligned", lambda p: setattr(p, "workspace", p.workspace + 16), gdn.GDN_ERR_ALIGNMENT),
+    ("dk overlaps k", lambda p: setattr(p, "dk", p.k + 512), gdn.GDN_ERR_INVALID_ARG),
+    ("dgate overlaps dq", lambda p: setattr(p, "dgate", p.dq + 512), gdn.GDN_ERR_INVALID_ARG),
+    ("dS0 overlaps the workspace", lambda p: setattr(p, "dS0", p.workspace + 4096), gdn.GDN_ERR_INVALID_ARG),
+    ("dnorm_w overlaps dS_T", lambda p: setattr(p, "dnorm_w", p.dS_T), gdn.GDN_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("name,mutate,expect", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_bwd_validation_errors(lib, name, mutate, expect):
+    p = fake_bwd(lib)
+    mutate(p)
+    assert lib.gdn_bwd(ctypes.byref(p), None) == expect, name
+
+
+def test_bwd_optional_outputs_may_be_null(lib):
+    # with the optional pointers NULL the call still fails only on the fake workspace size
+    p = fake_bwd(lib)
+    p.dnorm_w = p.dS0 = p.norm_w = p.S0 = p.dS_T = None
+    p.workspace_bytes -= 1
+    assert lib.gdn_bwd(ctypes.byref(p), None) == gdn.GDN_ERR_WORKSPACE
+
+
+def test_bwd_timed_needs_events(lib):
+    p = fake_bwd(lib)
+    events = (ctypes.c_void_p * 15)()
+    assert lib.gdn_bwd_timed(ctypes.byref(p), events, 15, None) == gdn.GDN_ERR_INVALID_ARG
+    assert lib.gdn_bwd_timed(ctypes.byref(p), None, 16, None) == gdn.GDN_ERR_INVALID_ARG

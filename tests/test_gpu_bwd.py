@@ -1,0 +1,117 @@
+"""Parity of the backward pass (gdn_bwd, through the C ABI) with the fp64
+backward oracle (oracle/bwd.py: torch.autograd on the layer forward written
+token by token).
+
+Bars, per gradient: relative L2 error <= 1e-2 with bf16 I/O and <= 1e-4 with
+fp32 I/O.  Every output buffer starts as NaN, so an element the library
+fails to write fails the test.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs
+from oracle import bwd as obwd
+from tests.gpu_common import TOL, rel_l2, say, torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+W = gdn_inputs.WORKLOADS
+
+
+def _workload(dtype, D):
+    return gdn_inputs.Workload(91, f"{dtype} d{D}", 1, 1000, 2, D, dtype)
+
+
+def run_bwd(inp, grads, dtype):
+    """The library's gradients as float64 numpy arrays (keyed like the oracle)."""
+    import linear_attention_token_fwd_amd as gdn
+    d = gdn.to_device(inp, dtype=torch_dtype(dtype))
+    dy = torch.from_numpy(grads["dy"]).to(torch_dtype(dtype)).cuda()
+    dS = None if grads["dS_T"] is None else torch.from_numpy(grads["dS_T"]).cuda()
+    B, T, H, D = inp["q"].shape
+    io = torch_dtype(dtype)
+    out = {n: torch.full((B, T, H, D), float("nan"), dtype=io, device="cuda") for n in ("q", "k", "v", "gate")}
+    out.update({n: torch.full((B, T, H), float("nan"), device="cuda") for n in ("log_a", "beta")})
+    out.update({n: torch.full((H * D, 4), float("nan"), device="cuda") for n in ("conv_q", "conv_k", "conv_v")})
+    out["norm_w"] = torch.full((H, D), float("nan"), device="cuda")
+    out["S0"] = torch.full((B, H, D, D), float("nan"), device="cuda")
+    g = gdn.gdn_bwd(d["q"], d["k"], d["v"], d["log_a"], d["beta"], d["gate"], d["conv_q"], d["conv_k"],
+                    d["conv_v"], d["norm_w"], d["S0"], dy, dS, out=out)
+    torch.cuda.synchronize()
+    return {n: g[n].double().cpu().numpy() for n in obwd.NAMES}
+
+
+def oracle_grads(inp, grads):
+    ref_in = {n: inp.get(n) for n in obwd.NAMES}
+    _, _, ref = obwd.backward(ref_in, grads["dy"], grads["dS_T"])
+    # the library reports the gradient at norm_w = ones and at S0 = 0 as well
+    if ref["norm_w"] is None or ref["S0"] is None:
+        filled = dict(ref_in)
+        if filled["norm_w"] is None:
+            filled["norm_w"] = np.ones(inp["q"].shape[2:], np.float32)
+        if filled["S0"] is None:
+            B, _, H, D = inp["q"].shape
+            filled["S0"] = np.zeros((B, H, D, D), np.float32)
+        _, _, ref2 = obwd.backward(filled, grads["dy"], grads["dS_T"])
+        ref["norm_w"], ref["S0"] = ref2["norm_w"], ref2["S0"]
+    return ref
+
+
+def compare(got, ref, dtype, label):
+    bar = TOL[dtype]
+    errs = {n: rel_l2(got[n], ref[n]) for n in obwd.NAMES}
+    say(f"{label}: " + ", ".join(f"{n} {e:.1e}" for n, e in errs.items()))
+    for n in obwd.NAMES:
+        assert np.isfinite(got[n]).all(), (label, n, "not finite (unwritten)")
+        assert errs[n] <= bar, (label, n, errs[n])
+
+
+CASES = [
+    # dtype, D, T, H, B, S0, norm_w, dS_T
+    ("bf16", 128, 64 * 3 + 17, 2, 1, True, True, True),
+    ("bf16", 128, 64, 1, 2, False, False, True),
+    ("bf16", 64, 150, 2, 2, True, True, False),
+    ("f32", 64, 64 * 2 + 5, 2, 2, True, True, True),
+    ("f32", 128, 100, 1, 1, False, True, True),
+    ("f32", 64, 3, 2, 1, True, False, True),
+    ("bf16", 128, 1, 1, 1, True, True, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-d{c[1]}-T{c[2]}-H{c[3]}-B{c[4]}" for c in CASES])
+def test_bwd_matches_oracle(case):
+    dtype, D, T, H, B, with_s0, with_nw, with_ds = case
+    w = _workload(dtype, D)
+    seed = 300 + T + D
+    inp = gdn_inputs.generate(w, T=T, H=H, B=B, seed=seed)
+    rng = np.random.default_rng(seed)
+    inp["S0"] = (0.1 * rng.standard_normal((B, H, D, D))).astype(np.float32) if with_s0 else None
+    inp["norm_w"] = (1 + 0.3 * rng.standard_normal((H, D))).astype(np.float32) if with_nw else None
+    grads = gdn_inputs.generate_grads(w, seed=seed + 1, T=T, H=H, B=B, state=with_ds)
+    say(f"case: bwd {dtype} D={D} T={T} H={H} B={B}")
+    got = run_bwd(inp, grads, dtype)
+    ref = oracle_grads(inp, grads)
+    compare(got, ref, dtype, f"{dtype} D={D} T={T}")
+
+
+def test_bwd_full_size_causal():
+    """At the full 480x832 size (T = 32760, H = 12, d = 128, bf16), with dy
+    zero from token 200 on and dS_T = 0: every gradient equals the oracle's
+    on the first 200 tokens (the loss does not see the rest), and the
+    per-token gradients from token 200 on are exactly zero."""
+    w = W[1]
+    t1 = 200
+    inp = gdn_inputs.generate(w, seed=1234)
+    grads = gdn_inputs.generate_grads(w, seed=1235, t_end=t1, state=False)
+    say("case: bwd full size T=32760 H=12 d=128, dy zero from t=200")
+    got = run_bwd(inp, grads, "bf16")
+    for n in ("q", "k", "v", "gate", "log_a", "beta"):
+        tail = got[n][:, t1:]
+        assert np.isfinite(tail).all() and (tail == 0).all(), n
+    short = {n: (None if a is None else (a[:, :t1] if n in ("q", "k", "v", "gate", "log_a", "beta") else a))
+             for n, a in inp.items()}
+    g_short = dict(dy=grads["dy"][:, :t1], dS_T=None)
+    ref = oracle_grads(short, g_short)
+    head = {n: (got[n][:, :t1] if n in ("q", "k", "v", "gate", "log_a", "beta") else got[n]) for n in obwd.NAMES}
+    compare(head, ref, "bf16", "full size, first 200 tokens")
