@@ -146,6 +146,8 @@ def main() -> int:
     ap.add_argument("--mixer", action="store_true",
                     help="time the whole token mixer (in-projection with the gate parameterisation, the layer, "
                          "out-projection) at T=32760, C=1536, H=12, d=128 instead of the layer alone")
+    ap.add_argument("--bwd", action="store_true",
+                    help="time the backward pass (gdn_bwd) on the workload instead of the forward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB (read 1 GiB, write 1 GiB) three times, to "
                          "calibrate the FETCH_SIZE / WRITE_SIZE counters")
@@ -175,6 +177,8 @@ def main() -> int:
         return 0
     if args.no_graph_cache:
         gdn.gdn_set_graph_cache_limit(0)
+    if args.bwd:
+        return run_bwd(args)
     if args.mixer:
         return run_mixer(args)
     w = gdn_inputs.WORKLOADS[args.workload]
@@ -467,6 +471,148 @@ def run_mixer(args) -> int:
         "kernels": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
         "cpu_baseline": cpu, "parity": parity,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+BWD_SOURCES = ("frag.hpp", "bwd.hpp", "gdn_bwd.hip")
+MFMA_F32_PEAK_TFLOPS = 157.3
+
+
+def bwd_flops_per_chunk_head(D: int) -> dict:
+    """fp32 MFMA flops per (chunk, head) of the backward's kernels, as
+    executed (the triangular 64 x 64 products in 10 of their 16 tiles):
+      prep : K K^T (tri), P = Q K^T (tri), U~ = T V, W = T K, P W
+      state: U = W S^T, S += U^T D K              (per chunk and head)
+      out  : Q' S^T, P U~
+      dstate: dS (D K)^T, X W, dO^T Q'
+      grad : W S^T, K dS'^T, dO S, U dS', dW = dU S (64 D^2 each); P^T dO,
+             T^T dW, T^T dU, F K, F^T K, G^T Q, G K (64 64 D each);
+             dO U^T, dR_W W^T, dR_U U~^T, K K^T (tri)."""
+    t, tri = 64 * 64 * D, 64 * 64 * D * 10 / 16
+    sq = 64 * D * D
+    return {"bwd_prep_kernel": 2 * (2 * tri + 3 * t), "bwd_state_kernel": 2 * (2 * sq),
+            "bwd_out_kernel": 2 * (sq + t), "bwd_dstate_kernel": 2 * (3 * sq),
+            "bwd_grad_kernel": 2 * (5 * sq + 7 * t + 4 * tri)}
+
+
+def run_bwd(args) -> int:
+    """One step = one gdn_bwd call (the layer's gradients with respect to
+    all inputs, the forward recomputed inside) on the workload."""
+    import numpy as np
+    import torch
+
+    import gdn_inputs
+    import linear_attention_token_fwd_amd as gdn
+
+    w = gdn_inputs.WORKLOADS[args.workload]
+    if w.bidirectional:
+        log("the backward covers the single-direction layer; use another workload")
+        return 2
+    log(f"backward workload: {w.name}")
+    inp = gdn_inputs.generate(w, B=args.batch or None)
+    B, T, H, D = inp["q"].shape
+    grads = gdn_inputs.generate_grads(w, seed=5000 + w.id, T=T, H=H, B=B)
+    io = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    d = gdn.to_device(inp, dtype=io)
+    dy = torch.from_numpy(grads["dy"]).to(io).cuda()
+    dS = torch.from_numpy(grads["dS_T"]).cuda()
+    out = {n: torch.empty((B, T, H, D), dtype=io, device="cuda") for n in ("q", "k", "v", "gate")}
+    out.update({n: torch.empty((B, T, H), device="cuda") for n in ("log_a", "beta")})
+    out.update({n: torch.empty((H * D, 4), device="cuda") for n in ("conv_q", "conv_k", "conv_v")})
+    out["norm_w"] = torch.empty((H, D), device="cuda")
+    out["S0"] = torch.empty((B, H, D, D), device="cuda")
+    ws = torch.empty(gdn.gdn_bwd_workspace_bytes(B, T, H, D, gdn.GDN_BF16 if io == torch.bfloat16 else gdn.GDN_F32),
+                     dtype=torch.uint8, device="cuda")
+    lib = gdn.load()
+    p = gdn.bwd_params(d["q"], d["k"], d["v"], d["log_a"], d["beta"], d["gate"], d["conv_q"], d["conv_k"],
+                       d["conv_v"], d["norm_w"], d["S0"], dy, dS, out, ws)
+    stream = torch.cuda.Stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+
+    def step():
+        st = lib.gdn_bwd(ctypes.byref(p), sptr)
+        if st != gdn.GDN_OK:
+            raise gdn.GdnError(st, "gdn_bwd")
+
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done")
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t_start) * 1e3 / args.steps
+    tokens_per_s = B * T / (ms_per_step * 1e-3)
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step, {tokens_per_s:.4e} tokens/s")
+
+    # ---- per-kernel durations (HIP events on the launch stream)
+    ev = HipEvents()
+    names = gdn.gdn_bwd_launch_names()
+    reps = min(args.steps, 10)
+    nev = 2 * len(names)
+    evs = [ev.create(nev) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for i in range(reps):
+        st = lib.gdn_bwd_timed(ctypes.byref(p), evs[i], nev, sptr)
+        if st != gdn.GDN_OK:
+            raise gdn.GdnError(st, "gdn_bwd_timed")
+    torch.cuda.synchronize()
+    per = {nm: [] for nm in names}
+    for i in range(reps):
+        for j, nm in enumerate(names):
+            ev.sync(evs[i][2 * j + 1])
+            per[nm].append(ev.elapsed_ms(evs[i][2 * j], evs[i][2 * j + 1]))
+    NC = (T + 63) // 64
+    fl = bwd_flops_per_chunk_head(D)
+    kernels = {}
+    for nm in names:
+        k = {"avg_ms": float(np.mean(per[nm]))}
+        if nm in fl:
+            k["flops_per_launch"] = fl[nm] * B * H * NC
+            k["TFLOPs"] = k["flops_per_launch"] / (k["avg_ms"] * 1e-3) / 1e12
+        kernels[nm] = k
+        log(f"  {nm}: {k['avg_ms']:.4f} ms" + (f", {k['TFLOPs']:.1f} TFLOP/s" if "TFLOPs" in k else ""))
+    dom = max(kernels, key=lambda k: kernels[k]["avg_ms"])
+    kd = kernels[dom]
+    achieved = kd.get("TFLOPs", 0.0)
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F32_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_F32_PEAK_TFLOPS, 4), "traffic": None,
+                "avg_launch_ms": round(kd["avg_ms"], 5)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the autograd oracle on a bounded sample: the first 256 tokens of one head
+        from oracle import bwd as obwd
+        Ts = min(T, 6144)
+        sample = {n: (None if inp[n] is None else
+                      (inp[n][:1, :Ts, :1] if n in ("q", "k", "v", "gate", "log_a", "beta") else
+                       inp[n][:D] if n.startswith("conv") else inp[n][:1] if n == "norm_w" else inp[n][:1, :1]))
+                  for n in obwd.NAMES}
+        threads = torch.get_num_threads()
+        log("running the backward oracle on a sample ...")
+        t1 = time.perf_counter()
+        obwd.backward(sample, grads["dy"][:1, :Ts, :1], grads["dS_T"][:1, :1])
+        cpu_s = time.perf_counter() - t1
+        cpu = {"value": round(Ts / cpu_s / H, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"one head, first {Ts} tokens (torch fp64 autograd, token loop), {cpu_s:.2f} s wall; "
+                         f"tokens/s of the {H}-head layer = sampled token-heads/s / {H}"}
+        log(f"oracle sample {cpu_s:.2f} s")
+
+    res = {
+        "metric": f"GDN layer backward tokens/s at T={T},H={H},d={D} {w.dtype} I/O",
+        "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name + " (backward: all gradients, forward recomputed)", "B": B, "T": T, "H": H,
+                   "d": D, "io": w.dtype, "chunk": 64},
+        "roofline": roofline,
+        "kernels": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kernels.items()},
+        "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
     return 0

@@ -327,8 +327,9 @@ int gdn_graph_cache_count(void);
  * H = 12, D = 128.
  * Errors: as for gdn_fwd.  GDN_ERR_INVALID_ARG for a NULL required pointer,
  * bad sizes, eps < 0 or not finite, or an output that overlaps an input,
- * another output or the workspace; GDN_ERR_ALIGNMENT for a tensor not aligned
- * to its element size; GDN_ERR_UNSUPPORTED for other D.
+ * another output or the workspace; GDN_ERR_ALIGNMENT for a tensor not
+ * 16-byte aligned or a workspace not 256-byte aligned; GDN_ERR_UNSUPPORTED
+ * for other D.
  */
 typedef struct gdn_bwd_params {
     int B, T, H, Dk, Dv;

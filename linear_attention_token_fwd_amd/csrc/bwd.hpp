@@ -30,6 +30,7 @@
 //   bwd_reduce_kernel    the conv-weight and norm-weight sums
 #pragma once
 #include "frag.hpp"
+#include "sync.hpp"
 
 namespace gdnb {
 
@@ -128,6 +129,28 @@ __device__ __forceinline__ floatx4 mm16(floatx4 acc, const float *A, int lda, in
 
 __device__ __forceinline__ floatx4 z4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
 
+// 8 consecutive channels of one token row, loaded with one (bf16) or two
+// (fp32) 16-byte loads; a row outside the sequence reads as zeros.
+template <class IO> struct Row8;
+template <> struct Row8<bf16> {
+    uint4 u;
+    __device__ __forceinline__ void load(const bf16 *p, bool ok) {
+        u = ok ? *reinterpret_cast<const uint4 *>(p) : make_uint4(0, 0, 0, 0);
+    }
+    __device__ __forceinline__ float get(int i) const {
+        const unsigned w = (&u.x)[i >> 1];
+        return __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
+    }
+};
+template <> struct Row8<float> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const float *p, bool ok) {
+        a = ok ? *reinterpret_cast<const float4 *>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
+        b = ok ? *reinterpret_cast<const float4 *>(p + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __device__ __forceinline__ float get(int i) const { return i < 4 ? (&a.x)[i] : (&b.x)[i - 4]; }
+};
+
 template <int D> __device__ __forceinline__ float *record(const Args &a, int b, int h, int c) {
     return a.rec + (((size_t)b * a.H + h) * a.NC + c) * (size_t)Rec<D>::SIZE;
 }
@@ -143,7 +166,7 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(Args a) {
     constexpr int LX = D + 4, LC = C + 4;
     extern __shared__ __align__(16) float lds[];
     float *sQ = lds, *sK = sQ + C * LX, *sV = sK + C * LX, *sT = sV + C * LX, *sM = sT + C * LC;
-    float *sg = sM + C * LC, *sb = sg + C, *sgam = sb + C;
+    float *sg = sM + C * LC, *sb = sg + C, *sgam = sb + C, *sTmp = sgam + C;
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t0 = c * C;
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, r = lane % 16, g = lane / 16;
     float *rec = record<D>(a, b, h, c);
@@ -164,27 +187,47 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(Args a) {
         rec[R::G + tid] = la;
         if (tid == 63) rec[R::G + 64] = expf(la);
     }
-    // short conv + SiLU of q, k, v (tap j multiplies x_{t-3+j}; zeros before the start)
+    // short conv + SiLU of q, k, v (tap j multiplies x_{t-3+j}; zeros before the
+    // start).  Thread: 8 channels (one 16- or 32-byte load per row) of RUN
+    // consecutive tokens; its RUN + 3 input rows of q, k and v are all loaded
+    // before any arithmetic.
     {
+        constexpr int G = D / 8, RUN = 64 / (NT / G), ROWS = RUN + 3;
+        const int cg = tid % G, run = tid / G, s0 = t0 + run * RUN;
         const IO *src[3] = {static_cast<const IO *>(a.q), static_cast<const IO *>(a.k), static_cast<const IO *>(a.v)};
         const float *cw[3] = {a.conv_q, a.conv_k, a.conv_v};
         float *dst[3] = {sQ, sK, sV};
-        for (int idx = tid; idx < C * D; idx += NT) {
-            const int tl = idx / D, ch = idx % D, t = t0 + tl;
+        Row8<IO> raw[3][ROWS];
 #pragma unroll
-            for (int x = 0; x < 3; ++x) {
-                float out = 0.f;
-                if (t < a.T) {
-                    const float *wt = cw[x] + ((size_t)h * D + ch) * 4;
+        for (int rr = 0; rr < ROWS; ++rr) {
+            const int sp = s0 - 3 + rr;
+            const bool ok = sp >= 0 && sp < a.T;
+            const size_t off = ((((size_t)b * a.T + (ok ? sp : 0)) * a.H + h) * D) + 8 * cg;
+#pragma unroll
+            for (int x = 0; x < 3; ++x) raw[x][rr].load(src[x] + off, ok);
+        }
+#pragma unroll
+        for (int x = 0; x < 3; ++x) {
+            float wt[8][4];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float4 wv = *reinterpret_cast<const float4 *>(cw[x] + ((size_t)h * D + 8 * cg + i) * 4);
+                wt[i][0] = wv.x; wt[i][1] = wv.y; wt[i][2] = wv.z; wt[i][3] = wv.w;
+            }
+#pragma unroll
+            for (int rt = 0; rt < RUN; ++rt) {
+                const bool valid = s0 + rt < a.T;
+                float out[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
                     float z = 0.f;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int s = t - 3 + j;
-                        if (s >= 0) z = fmaf(wt[j], to_f(src[x][(((size_t)b * a.T + s) * a.H + h) * D + ch]), z);
-                    }
-                    out = silu(z);
+                    for (int j = 0; j < 4; ++j) z = fmaf(wt[i][j], raw[x][rt + j].get(i), z);
+                    out[i] = valid ? silu(z) : 0.f;
                 }
-                dst[x][tl * LX + ch] = out;
+                float *row = dst[x] + (run * RUN + rt) * LX + 8 * cg;
+                *reinterpret_cast<float4 *>(row) = make_float4(out[0], out[1], out[2], out[3]);
+                *reinterpret_cast<float4 *>(row + 4) = make_float4(out[4], out[5], out[6], out[7]);
             }
         }
     }
@@ -220,17 +263,47 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(Args a) {
         }
     }
     __syncthreads();
-    // T = (I + A)^-1 by forward substitution, column j on thread j
-    if (tid < 64) {
-        const int j = tid;
-        for (int i = 0; i < 64; ++i) sT[i * LC + j] = i == j ? 1.f : 0.f;
-        for (int i = j + 1; i < 64; ++i) {
+    // T = (I + A)^-1 in 16 x 16 blocks.  Diagonal blocks: wave w inverts
+    // (I + A_ww) by forward substitution, column n on lane n (lanes 0..15);
+    // the blocks above the diagonal are zero.
+    for (int idx = lane; idx < 16 * 64; idx += 64) {
+        const int i = 16 * w + idx / 64, j = idx % 64;
+        if (j < 16 * w || j >= 16 * w + 16) sT[i * LC + j] = 0.f;
+    }
+    if (lane < 16) {
+        const int n = lane;
+        const float *Aw = sM + 16 * w * LC + 16 * w;
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
             float s = 0.f;
-            for (int m = j; m < i; ++m) s = fmaf(sM[i * LC + m], sT[m * LC + j], s);
-            sT[i * LC + j] = -s;
+#pragma unroll
+            for (int m = 0; m < i; ++m) s = fmaf(Aw[i * LC + m], x[m], s);
+            x[i] = i < n ? 0.f : (i == n ? 1.f : -s);
         }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sT[(16 * w + i) * LC + 16 * w + n] = x[i];
     }
     __syncthreads();
+    // Blocks below the diagonal, block row by block row:
+    //   T_IJ = -T_II (sum_{J <= K < I} A_IK T_KJ),  wave J computes T_IJ
+    float *tmp = sTmp + w * 16 * 20;
+    for (int I = 1; I < 4; ++I) {
+        if (w < I) {
+            floatx4 acc = z4();
+            for (int K = w; K < I; ++K)
+                acc = mm16<true, false, 16>(acc, sM + 16 * I * LC + 16 * K, LC, 0, sT + 16 * K * LC + 16 * w, LC, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tmp[(4 * g + i) * 20 + r] = acc[i];
+        }
+        __syncthreads();
+        if (w < I) {
+            const floatx4 t = mm16<true, false, 16>(z4(), sT + 16 * I * LC + 16 * I, LC, 0, tmp, 20, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sT[(16 * I + 4 * g + i) * LC + 16 * w + r] = -t[i];
+        }
+        __syncthreads();
+    }
     // T out; T' = T diag(b gam) into the A storage; diag(b) V in place
     for (int idx = tid; idx < C * C; idx += NT) {
         const int i = idx / C, j = idx % C;
@@ -291,47 +364,104 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(Args a) {
 }
 
 // ---------------------------------------------------------------------------
+// Chain operands: whole [64][D] record matrices and a 16-column slice of one,
+// copied from a chunk record into LDS through registers, so that the next
+// chunk's loads are in flight while the current chunk computes.
+template <int D> constexpr int kPerM = 64 * D / 4 / NT;   // floatx4 per thread per matrix
+
+template <int D>
+__device__ __forceinline__ void stage_load(floatx4 (&m)[kPerM<D>], const float *src) {
+#pragma unroll
+    for (int e = 0; e < kPerM<D>; ++e) {
+        const int idx = threadIdx.x + NT * e, row = idx / (D / 4), c4 = 4 * (idx % (D / 4));
+        m[e] = *reinterpret_cast<const floatx4 *>(src + row * D + c4);
+    }
+}
+template <int D>
+__device__ __forceinline__ void stage_store(const floatx4 (&m)[kPerM<D>], float *dst) {
+#pragma unroll
+    for (int e = 0; e < kPerM<D>; ++e) {
+        const int idx = threadIdx.x + NT * e, row = idx / (D / 4), c4 = 4 * (idx % (D / 4));
+        *reinterpret_cast<floatx4 *>(dst + row * (D + 4) + c4) = m[e];
+    }
+}
+// the 16 columns col0.. of a [64][D] matrix: one floatx4 per thread
+template <int D> __device__ __forceinline__ floatx4 slice_load(const float *src, int col0) {
+    return *reinterpret_cast<const floatx4 *>(src + (threadIdx.x / 4) * D + col0 + 4 * (threadIdx.x % 4));
+}
+__device__ __forceinline__ void slice_store(floatx4 v, float *dst) {
+    *reinterpret_cast<floatx4 *>(dst + (threadIdx.x / 4) * 20 + 4 * (threadIdx.x % 4)) = v;
+}
+
+// ---------------------------------------------------------------------------
 // The forward chain over chunks for value rows 16 vb .. 16 vb + 15 of one
 // head: stores each chunk's entry state, then U = U~ - W S^T (wave w: tokens
 // 16w..) and S <- gC S + U^T D K.
 template <int D>
 __global__ __launch_bounds__(NT) void bwd_state_kernel(Args a) {
     typedef Rec<D> R;
-    constexpr int LS = D + 4, LU = 16 + 4;
-    __shared__ __align__(16) float sS[16 * LS];
-    __shared__ __align__(16) float sU[C * LU];
-    const int vb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    constexpr int LX = D + 4, LSL = 16 + 4, LS = D + 4, LU = 16 + 4;
+    extern __shared__ __align__(16) float lds[];
+    float *sW = lds, *sDK = sW + 64 * LX, *sUT = sDK + 64 * LX, *sS = sUT + 64 * LSL, *sU = sS + 16 * LS;
+    // one work item per (batch row, head, 16 value rows); the items of a head
+    // are neighbours in the list, so they share one XCD's L2
+    constexpr int NV = D / 16;
+    int pos;
+    if (!gdn::xcd_position(blockIdx.x, a.B * a.H * NV, gridDim.x, pos)) return;
+    const int vb = pos % NV, h = (pos / NV) % a.H, b = pos / NV / a.H;
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, r = lane % 16, g = lane / 16;
     for (int idx = tid; idx < 16 * D; idx += NT) {
         const int row = idx / D, col = idx % D;
         sS[row * LS + col] = a.S0 ? a.S0[(((size_t)b * a.H + h) * D + 16 * vb + row) * D + col] : 0.f;
     }
+    floatx4 pw[kPerM<D>], pk[kPerM<D>], pu;
+    {
+        const float *r0 = record<D>(a, b, h, 0);
+        stage_load<D>(pw, r0 + R::W);
+        stage_load<D>(pk, r0 + R::DK);
+        pu = slice_load<D>(r0 + R::UT, 16 * vb);
+        stage_store<D>(pw, sW);
+        stage_store<D>(pk, sDK);
+        slice_store(pu, sUT);
+    }
     __syncthreads();
     for (int c = 0; c < a.NC; ++c) {
         float *rec = record<D>(a, b, h, c);
+        if (c + 1 < a.NC) {
+            const float *rn = record<D>(a, b, h, c + 1);
+            stage_load<D>(pw, rn + R::W);
+            stage_load<D>(pk, rn + R::DK);
+            pu = slice_load<D>(rn + R::UT, 16 * vb);
+        }
+        const float gC = rec[R::G + 64];
         for (int idx = tid; idx < 16 * D; idx += NT) {
             const int row = idx / D, col = idx % D;
             rec[R::SC + (16 * vb + row) * D + col] = sS[row * LS + col];
         }
         {
-            const floatx4 acc = mm16<true, true, D>(z4(), rec + R::W, D, 16 * w, sS, LS, 0);
+            const floatx4 acc = mm16<true, true, D>(z4(), sW, LX, 16 * w, sS, LS, 0);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int tok = 16 * w + 4 * g + i;
-                sU[tok * LU + r] = rec[R::UT + tok * D + 16 * vb + r] - acc[i];
+                sU[tok * LU + r] = sUT[tok * LSL + r] - acc[i];
             }
         }
-        __syncthreads();
-        const float gC = rec[R::G + 64];
+        gdn::lds_barrier();
         for (int nt = w; nt < D / 16; nt += 4) {
             floatx4 acc;
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[i] = gC * sS[(4 * g + i) * LS + 16 * nt + r];
-            acc = mm16<false, false, C>(acc, sU, LU, 0, rec + R::DK, D, 16 * nt);
+            acc = mm16<false, false, C>(acc, sU, LU, 0, sDK, LX, 16 * nt);
 #pragma unroll
             for (int i = 0; i < 4; ++i) sS[(4 * g + i) * LS + 16 * nt + r] = acc[i];
         }
-        __syncthreads();
+        gdn::lds_barrier();
+        if (c + 1 < a.NC) {
+            stage_store<D>(pw, sW);
+            stage_store<D>(pk, sDK);
+            slice_store(pu, sUT);
+        }
+        gdn::lds_barrier();
     }
 }
 
@@ -411,40 +541,72 @@ __global__ __launch_bounds__(NT) void bwd_out_kernel(Args a) {
 template <int D>
 __global__ __launch_bounds__(NT) void bwd_dstate_kernel(Args a) {
     typedef Rec<D> R;
-    constexpr int LS = D + 4, LXX = C + 4;
-    __shared__ __align__(16) float sD[16 * LS];
-    __shared__ __align__(16) float sX[16 * LXX];
-    const int vb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    constexpr int LX = D + 4, LSL = 16 + 4, LS = D + 4, LXX = C + 4;
+    extern __shared__ __align__(16) float lds[];
+    float *sDK = lds, *sW = sDK + 64 * LX, *sQP = sW + 64 * LX, *sDO = sQP + 64 * LX, *sD = sDO + 64 * LSL;
+    float *sX = sD + 16 * LS;
+    // one work item per (batch row, head, 16 value rows); the items of a head
+    // are neighbours in the list, so they share one XCD's L2
+    constexpr int NV = D / 16;
+    int pos;
+    if (!gdn::xcd_position(blockIdx.x, a.B * a.H * NV, gridDim.x, pos)) return;
+    const int vb = pos % NV, h = (pos / NV) % a.H, b = pos / NV / a.H;
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, r = lane % 16, g = lane / 16;
     for (int idx = tid; idx < 16 * D; idx += NT) {
         const int row = idx / D, col = idx % D;
         sD[row * LS + col] = a.dS_T ? a.dS_T[(((size_t)b * a.H + h) * D + 16 * vb + row) * D + col] : 0.f;
     }
+    floatx4 pk[kPerM<D>], pw[kPerM<D>], pq[kPerM<D>], po;
+    {
+        const float *r0 = record<D>(a, b, h, a.NC - 1);
+        stage_load<D>(pk, r0 + R::DK);
+        stage_load<D>(pw, r0 + R::W);
+        stage_load<D>(pq, r0 + R::QP);
+        po = slice_load<D>(r0 + R::DO, 16 * vb);
+        stage_store<D>(pk, sDK);
+        stage_store<D>(pw, sW);
+        stage_store<D>(pq, sQP);
+        slice_store(po, sDO);
+    }
     __syncthreads();
     for (int c = a.NC - 1; c >= 0; --c) {
         float *rec = record<D>(a, b, h, c);
+        if (c > 0) {
+            const float *rn = record<D>(a, b, h, c - 1);
+            stage_load<D>(pk, rn + R::DK);
+            stage_load<D>(pw, rn + R::W);
+            stage_load<D>(pq, rn + R::QP);
+            po = slice_load<D>(rn + R::DO, 16 * vb);
+        }
+        const float gC = rec[R::G + 64];
         for (int idx = tid; idx < 16 * D; idx += NT) {
             const int row = idx / D, col = idx % D;
             rec[R::DSN + (16 * vb + row) * D + col] = sD[row * LS + col];
         }
         {
             // X = dS (D K)^T: 16 value rows x 64 tokens, wave w tokens 16w..
-            const floatx4 acc = mm16<true, true, D>(z4(), sD, LS, 0, rec + R::DK, D, 16 * w);
+            const floatx4 acc = mm16<true, true, D>(z4(), sD, LS, 0, sDK, LX, 16 * w);
 #pragma unroll
             for (int i = 0; i < 4; ++i) sX[(4 * g + i) * LXX + 16 * w + r] = acc[i];
         }
-        __syncthreads();
-        const float gC = rec[R::G + 64];
+        gdn::lds_barrier();
         for (int nt = w; nt < D / 16; nt += 4) {
-            const floatx4 xw = mm16<true, false, C>(z4(), sX, LXX, 0, rec + R::W, D, 16 * nt);
-            const floatx4 oq = mm16<false, false, C>(z4(), rec + R::DO + 16 * vb, D, 0, rec + R::QP, D, 16 * nt);
+            const floatx4 xw = mm16<true, false, C>(z4(), sX, LXX, 0, sW, LX, 16 * nt);
+            const floatx4 oq = mm16<false, false, C>(z4(), sDO, LSL, 0, sQP, LX, 16 * nt);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float *p = sD + (4 * g + i) * LS + 16 * nt + r;
                 *p = gC * *p - xw[i] + oq[i];
             }
         }
-        __syncthreads();
+        gdn::lds_barrier();
+        if (c > 0) {
+            stage_store<D>(pk, sDK);
+            stage_store<D>(pw, sW);
+            stage_store<D>(pq, sQP);
+            slice_store(po, sDO);
+        }
+        gdn::lds_barrier();
     }
     if (a.dS0)
         for (int idx = tid; idx < 16 * D; idx += NT) {

@@ -86,19 +86,22 @@ gdn_status validate(const gdn_bwd_params *p) {
         for (int j = i + 1; j < nout; ++j)
             if (overlap(out[i], out[j])) return GDN_ERR_INVALID_ARG;
     }
-    const void *io[] = {p->q, p->k, p->v, p->gate, p->dy, p->dq, p->dk, p->dv, p->dgate};
-    for (const void *ptr : io)
-        if (!aligned(ptr, es)) return GDN_ERR_ALIGNMENT;
-    const void *f32[] = {p->log_a, p->beta, p->conv_q, p->conv_k, p->conv_v, p->norm_w, p->S0, p->dS_T,
-                         p->dlog_a, p->dbeta, p->dconv_q, p->dconv_k, p->dconv_v, p->dnorm_w, p->dS0};
-    for (const void *ptr : f32)
-        if (ptr && !aligned(ptr, 4)) return GDN_ERR_ALIGNMENT;
+    // 16-byte vector loads of q, k, v and the conv weights; every tensor is
+    // held to the same rule
+    const void *all[] = {p->q,      p->k,      p->v,       p->gate,    p->dy,      p->dq,    p->dk,
+                         p->dv,     p->dgate,  p->log_a,   p->beta,    p->conv_q,  p->conv_k, p->conv_v,
+                         p->norm_w, p->S0,     p->dS_T,    p->dlog_a,  p->dbeta,   p->dconv_q, p->dconv_k,
+                         p->dconv_v, p->dnorm_w, p->dS0};
+    for (const void *ptr : all)
+        if (ptr && !aligned(ptr, 16)) return GDN_ERR_ALIGNMENT;
     if (!p->workspace || p->workspace_bytes < layout(p).total) return GDN_ERR_WORKSPACE;
     if (!aligned(p->workspace, kAlign)) return GDN_ERR_ALIGNMENT;
     return GDN_OK;
 }
 
-template <int D> size_t prep_lds() { return (3 * 64 * (D + 4) + 2 * 64 * 68 + 3 * 64) * sizeof(float); }
+template <int D> size_t prep_lds() { return (3 * 64 * (D + 4) + 2 * 64 * 68 + 3 * 64 + 4 * 16 * 20) * sizeof(float); }
+template <int D> size_t state_lds() { return (2 * 64 * (D + 4) + 64 * 20 + 16 * (D + 4) + 64 * 20) * sizeof(float); }
+template <int D> size_t dstate_lds() { return (3 * 64 * (D + 4) + 64 * 20 + 16 * (D + 4) + 16 * 68) * sizeof(float); }
 template <int D> size_t grad_lds() { return (3 * 64 * (D + 4) + 3 * 64 * 68 + 8 * 64) * sizeof(float); }
 
 gdn_status set_attributes() {
@@ -113,6 +116,10 @@ gdn_status set_attributes() {
             {reinterpret_cast<const void *>(&gdnb::bwd_prep_kernel<bf16, 64>), prep_lds<64>()},
             {reinterpret_cast<const void *>(&gdnb::bwd_prep_kernel<float, 128>), prep_lds<128>()},
             {reinterpret_cast<const void *>(&gdnb::bwd_prep_kernel<float, 64>), prep_lds<64>()},
+            {reinterpret_cast<const void *>(&gdnb::bwd_state_kernel<128>), state_lds<128>()},
+            {reinterpret_cast<const void *>(&gdnb::bwd_state_kernel<64>), state_lds<64>()},
+            {reinterpret_cast<const void *>(&gdnb::bwd_dstate_kernel<128>), dstate_lds<128>()},
+            {reinterpret_cast<const void *>(&gdnb::bwd_dstate_kernel<64>), dstate_lds<64>()},
             {reinterpret_cast<const void *>(&gdnb::bwd_grad_kernel<128>), grad_lds<128>()},
             {reinterpret_cast<const void *>(&gdnb::bwd_grad_kernel<64>), grad_lds<64>()},
         };
@@ -143,7 +150,9 @@ gdn_status launch_all(const gdn_bwd_params *p, hipEvent_t *ev, hipStream_t s) {
     a.part_conv = reinterpret_cast<float *>(ws + L.part_conv);
     a.part_norm = reinterpret_cast<float *>(ws + L.part_norm);
 
-    const dim3 chunks(a.NC, p->H, p->B), rows(D / 16, p->H, p->B), tokens((p->T + 3) / 4, p->H, p->B);
+    // chains: 8 equal slices of the work list (whole heads each), one per XCD
+    const int heads_per_xcd = (p->B * p->H + 7) / 8;
+    const dim3 chunks(a.NC, p->H, p->B), rows(8 * heads_per_xcd * (D / 16)), tokens((p->T + 3) / 4, p->H, p->B);
     const int nred = p->H * D * 13;
     const dim3 red((nred + NT - 1) / NT);
     int i = 0;
@@ -160,13 +169,13 @@ gdn_status launch_all(const gdn_bwd_params *p, hipEvent_t *ev, hipStream_t s) {
     bwd_prep_kernel<IO, D><<<chunks, NT, prep_lds<D>(), s>>>(a);
     if (!post()) return GDN_ERR_HIP;
     pre();
-    bwd_state_kernel<D><<<rows, NT, 0, s>>>(a);
+    bwd_state_kernel<D><<<rows, NT, state_lds<D>(), s>>>(a);
     if (!post()) return GDN_ERR_HIP;
     pre();
     bwd_out_kernel<IO, D><<<chunks, NT, 0, s>>>(a);
     if (!post()) return GDN_ERR_HIP;
     pre();
-    bwd_dstate_kernel<D><<<rows, NT, 0, s>>>(a);
+    bwd_dstate_kernel<D><<<rows, NT, dstate_lds<D>(), s>>>(a);
     if (!post()) return GDN_ERR_HIP;
     pre();
     bwd_grad_kernel<D><<<chunks, NT, grad_lds<D>(), s>>>(a);
