@@ -629,17 +629,21 @@ __global__ __launch_bounds__(NT) void bwd_dstate_kernel(Args a) {
 //   dg = gam d gam - dl d dl + rowsum(M) - colsum(M),  M = dP o P + dA o A,
 //        plus gC <dS', S> + sum(dl d dl) on the last token;
 //   d log a = the suffix sums of dg inside the chunk.
+constexpr int GW = 8, GNT = 64 * GW;  // waves and threads of bwd_grad_kernel
+
 template <int D>
-__global__ __launch_bounds__(NT) void bwd_grad_kernel(Args a) {
+__global__ __launch_bounds__(GNT) void bwd_grad_kernel(Args a) {
     typedef Rec<D> R;
-    constexpr int LX = D + 4, LC = C + 4, NTL = D / 16;
+    constexpr int LX = D + 4, LC = C + 4, NTH = D / 32;  // column tiles per wave
     extern __shared__ __align__(16) float lds[];
     float *L1 = lds, *L2 = L1 + C * LX, *L3 = L2 + C * LX;   // U then dR_W; dU; dW then dR_U
     float *La = L3 + C * LX, *Lb = La + C * LC, *Lc = Lb + C * LC;  // G; F; M
     float *vg = Lc + C * LC, *vb_ = vg + C, *vgam = vb_ + C, *vdl = vgam + C;
-    float *vdgam = vdl + C, *vddl = vdgam + C, *vdb = vddl + C, *vred = vdb + C;
+    float *vdgam = vdl + C, *vddl = vdgam + 2 * C, *vdb = vddl + 2 * C, *vred = vdb + 2 * C;
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t0 = c * C;
+    // wave w: row block rb (tokens 16 rb ..), column tiles hf, hf + 2, hf + 4, ...
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, r = lane % 16, g = lane / 16;
+    const int rb = w % 4, hf = w / 4;
     const float *rec = record<D>(a, b, h, c);
 
     if (tid < 64) {
@@ -653,63 +657,80 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(Args a) {
     // <dS', S>
     {
         float s = 0.f;
-        for (int idx = tid; idx < D * D; idx += NT) s += rec[R::DSN + idx] * rec[R::SC + idx];
+        for (int idx = 4 * tid; idx < D * D; idx += 4 * GNT) {
+            const floatx4 x = *reinterpret_cast<const floatx4 *>(rec + R::DSN + idx);
+            const floatx4 y = *reinterpret_cast<const floatx4 *>(rec + R::SC + idx);
+            s += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
+        }
         s = wave_sum(s);
         if (lane == 0) vred[w] = s;
     }
-    __syncthreads();
-    const float gC = rec[R::G + 64];
-
     // U = U~ - W S^T
 #pragma unroll 1
-    for (int nt = 0; nt < NTL; ++nt) {
-        const floatx4 acc = mm16<true, true, D>(z4(), rec + R::W, D, 16 * w, rec + R::SC, D, 16 * nt);
+    for (int j = 0; j < NTH; ++j) {
+        const int nt = 2 * j + hf;
+        const floatx4 acc = mm16<true, true, D>(z4(), rec + R::W, D, 16 * rb, rec + R::SC, D, 16 * nt);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = 16 * w + 4 * g + i, col = 16 * nt + r;
+            const int row = 16 * rb + 4 * g + i, col = 16 * nt + r;
             L1[row * LX + col] = rec[R::UT + row * D + col] - acc[i];
         }
     }
     __syncthreads();
 
     float pgam[4] = {0.f, 0.f, 0.f, 0.f}, pdl[4] = {0.f, 0.f, 0.f, 0.f}, pdb[4] = {0.f, 0.f, 0.f, 0.f};
-    floatx4 dQ[NTL], dK[NTL];
-    float rgam[4], rdl[4], rb[4];
+    floatx4 dQ[NTH], dK[NTH];
+    float rgam[4], rdl[4], rbb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int row = 16 * w + 4 * g + i;
+        const int row = 16 * rb + 4 * g + i;
         rgam[i] = vgam[row];
         rdl[i] = vdl[row];
-        rb[i] = vb_[row];
+        rbb[i] = vb_[row];
     }
-#pragma unroll
-    for (int nt = 0; nt < NTL; ++nt) {
-        const int col = 16 * nt + r;
-        // dU, d dl
-        const floatx4 kd = mm16<true, true, D>(z4(), rec + R::XK, D, 16 * w, rec + R::DSN, D, 16 * nt);
-        const floatx4 pt = mm16<false, false, C>(z4(), rec + R::P, C, 16 * w, rec + R::DO, D, 16 * nt);
-        // dO S
-        const floatx4 dos = mm16<true, false, D>(z4(), rec + R::DO, D, 16 * w, rec + R::SC, D, 16 * nt);
-        // U dS'
-        const floatx4 uds = mm16<true, false, D>(z4(), L1, LX, 16 * w, rec + R::DSN, D, 16 * nt);
+    // dU = P^T dO + diag(dl) K dS'^T, d dl
+#pragma unroll 1
+    for (int j = 0; j < NTH; ++j) {
+        const int nt = 2 * j + hf, col = 16 * nt + r;
+        const floatx4 kd = mm16<true, true, D>(z4(), rec + R::XK, D, 16 * rb, rec + R::DSN, D, 16 * nt);
+        const floatx4 pt = mm16<false, false, C>(z4(), rec + R::P, C, 16 * rb, rec + R::DO, D, 16 * nt);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = 16 * w + 4 * g + i;
+            const int row = 16 * rb + 4 * g + i;
             L2[row * LX + col] = pt[i] + rdl[i] * kd[i];
             pdl[i] += kd[i] * L1[row * LX + col];
-            dQ[nt][i] = rgam[i] * dos[i];
-            pgam[i] += dos[i] * rec[R::XQ + row * D + col];
-            dK[nt][i] = rdl[i] * uds[i];
         }
     }
-    // dP = dO U^T (lower-inclusive): G = E o dP, M = dP o P
-#pragma unroll 1
-    for (int nt = 0; nt < 4; ++nt) {
-        floatx4 acc = z4();
-        if (nt <= w) acc = mm16<true, true, D>(acc, rec + R::DO, D, 16 * w, L1, LX, 16 * nt);
+    // dq^ = diag(gam) dO S, d gam;  dk^ = diag(dl) U dS'
+#pragma unroll
+    for (int j = 0; j < NTH; ++j) {
+        const int nt = 2 * j + hf, col = 16 * nt + r;
+        const floatx4 dos = mm16<true, false, D>(z4(), rec + R::DO, D, 16 * rb, rec + R::SC, D, 16 * nt);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = 16 * w + 4 * g + i, col = 16 * nt + r;
+            const int row = 16 * rb + 4 * g + i;
+            dQ[j][i] = rgam[i] * dos[i];
+            pgam[i] += dos[i] * rec[R::XQ + row * D + col];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = 0; j < NTH; ++j) {
+        const int nt = 2 * j + hf;
+        const floatx4 uds = mm16<true, false, D>(z4(), L1, LX, 16 * rb, rec + R::DSN, D, 16 * nt);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dK[j][i] = rdl[i] * uds[i];
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // dP = dO U^T (lower-inclusive): G = E o dP, M = dP o P; tiles hf, hf + 2
+#pragma unroll 1
+    for (int j = 0; j < 2; ++j) {
+        const int nt = 2 * j + hf;
+        floatx4 acc = z4();
+        if (nt <= rb) acc = mm16<true, true, D>(acc, rec + R::DO, D, 16 * rb, L1, LX, 16 * nt);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * rb + 4 * g + i, col = 16 * nt + r;
             const bool on = col <= row;
             La[row * LC + col] = on ? expf(vg[row] - vg[col]) * acc[i] : 0.f;
             Lc[row * LC + col] = on ? acc[i] * rec[R::P + row * C + col] : 0.f;
@@ -718,59 +739,62 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(Args a) {
     __syncthreads();
     // dW = -dU S
 #pragma unroll 1
-    for (int nt = 0; nt < NTL; ++nt) {
-        const floatx4 acc = mm16<true, false, D>(z4(), L2, LX, 16 * w, rec + R::SC, D, 16 * nt);
+    for (int j = 0; j < NTH; ++j) {
+        const int nt = 2 * j + hf;
+        const floatx4 acc = mm16<true, false, D>(z4(), L2, LX, 16 * rb, rec + R::SC, D, 16 * nt);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) L3[(16 * w + 4 * g + i) * LX + 16 * nt + r] = -acc[i];
+        for (int i = 0; i < 4; ++i) L3[(16 * rb + 4 * g + i) * LX + 16 * nt + r] = -acc[i];
     }
     __syncthreads();
     // dR_W = T^T dW (into the U storage)
 #pragma unroll
-    for (int nt = 0; nt < NTL; ++nt) {
-        const int col = 16 * nt + r;
-        const floatx4 acc = mm16<false, false, C>(z4(), rec + R::TM, C, 16 * w, L3, LX, 16 * nt);
+    for (int j = 0; j < NTH; ++j) {
+        const int nt = 2 * j + hf, col = 16 * nt + r;
+        const floatx4 acc = mm16<false, false, C>(z4(), rec + R::TM, C, 16 * rb, L3, LX, 16 * nt);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = 16 * w + 4 * g + i;
+            const int row = 16 * rb + 4 * g + i;
             L1[row * LX + col] = acc[i];
-            dK[nt][i] += rb[i] * rgam[i] * acc[i];
+            dK[j][i] += rbb[i] * rgam[i] * acc[i];
             const float rk = acc[i] * rec[R::XK + row * D + col];
-            pgam[i] += rb[i] * rk;
+            pgam[i] += rbb[i] * rk;
             pdb[i] += rgam[i] * rk;
         }
+        __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
     // dR_U = T^T dU (into the dW storage), dv^ = diag(b) dR_U
     float *dxv = const_cast<float *>(rec) + R::DXV;
 #pragma unroll 1
-    for (int nt = 0; nt < NTL; ++nt) {
-        const int col = 16 * nt + r;
-        const floatx4 acc = mm16<false, false, C>(z4(), rec + R::TM, C, 16 * w, L2, LX, 16 * nt);
+    for (int j = 0; j < NTH; ++j) {
+        const int nt = 2 * j + hf, col = 16 * nt + r;
+        const floatx4 acc = mm16<false, false, C>(z4(), rec + R::TM, C, 16 * rb, L2, LX, 16 * nt);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = 16 * w + 4 * g + i;
+            const int row = 16 * rb + 4 * g + i;
             L3[row * LX + col] = acc[i];
-            dxv[row * D + col] = rb[i] * acc[i];
+            dxv[row * D + col] = rbb[i] * acc[i];
             pdb[i] += acc[i] * rec[R::XV + row * D + col];
         }
     }
     __syncthreads();
     // dA = -(dR_W W^T + dR_U U~^T) (strictly lower), F = diag(b) (E o dA), M += dA o A
 #pragma unroll 1
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int j = 0; j < 2; ++j) {
+        const int nt = 2 * j + hf;
         floatx4 acc = z4(), kk = z4();
-        if (nt <= w) {
-            acc = mm16<true, true, D>(acc, L1, LX, 16 * w, rec + R::W, D, 16 * nt);
-            acc = mm16<true, true, D>(acc, L3, LX, 16 * w, rec + R::UT, D, 16 * nt);
-            kk = mm16<true, true, D>(kk, rec + R::XK, D, 16 * w, rec + R::XK, D, 16 * nt);
+        if (nt <= rb) {
+            acc = mm16<true, true, D>(acc, L1, LX, 16 * rb, rec + R::W, D, 16 * nt);
+            acc = mm16<true, true, D>(acc, L3, LX, 16 * rb, rec + R::UT, D, 16 * nt);
+            kk = mm16<true, true, D>(kk, rec + R::XK, D, 16 * rb, rec + R::XK, D, 16 * nt);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = 16 * w + 4 * g + i, col = 16 * nt + r;
+            const int row = 16 * rb + 4 * g + i, col = 16 * nt + r;
             float f = 0.f;
             if (col < row) {
                 const float e = expf(vg[row] - vg[col]), da = -acc[i];
-                f = rb[i] * e * da;
+                f = rbb[i] * e * da;
                 pdb[i] += e * da * kk[i];
                 Lc[row * LC + col] += f * kk[i];
             }
@@ -781,27 +805,29 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(Args a) {
     // dk^ += F K + F^T K + G^T Q;  dq^ += G K
     float *dxq = const_cast<float *>(rec) + R::DXQ, *dxk = const_cast<float *>(rec) + R::DXK;
 #pragma unroll
-    for (int nt = 0; nt < NTL; ++nt) {
-        dK[nt] = mm16<true, false, C>(dK[nt], Lb, LC, 16 * w, rec + R::XK, D, 16 * nt);
-        dK[nt] = mm16<false, false, C>(dK[nt], Lb, LC, 16 * w, rec + R::XK, D, 16 * nt);
-        dK[nt] = mm16<false, false, C>(dK[nt], La, LC, 16 * w, rec + R::XQ, D, 16 * nt);
-        dQ[nt] = mm16<true, false, C>(dQ[nt], La, LC, 16 * w, rec + R::XK, D, 16 * nt);
+    for (int j = 0; j < NTH; ++j) {
+        const int nt = 2 * j + hf;
+        dK[j] = mm16<true, false, C>(dK[j], Lb, LC, 16 * rb, rec + R::XK, D, 16 * nt);
+        dK[j] = mm16<false, false, C>(dK[j], Lb, LC, 16 * rb, rec + R::XK, D, 16 * nt);
+        dK[j] = mm16<false, false, C>(dK[j], La, LC, 16 * rb, rec + R::XQ, D, 16 * nt);
+        dQ[j] = mm16<true, false, C>(dQ[j], La, LC, 16 * rb, rec + R::XK, D, 16 * nt);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = 16 * w + 4 * g + i, col = 16 * nt + r;
-            dxq[row * D + col] = dQ[nt][i];
-            dxk[row * D + col] = dK[nt][i];
+            const int row = 16 * rb + 4 * g + i, col = 16 * nt + r;
+            dxq[row * D + col] = dQ[j][i];
+            dxk[row * D + col] = dK[j][i];
         }
+        __builtin_amdgcn_sched_barrier(0);
     }
-    // per-row sums over the 16 lanes of a row
+    // per-row sums over the 16 lanes of a row, one set per column half
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const float sg_ = gdn::group_sum<16>(pgam[i]), sd = gdn::group_sum<16>(pdl[i]), sb = gdn::group_sum<16>(pdb[i]);
         if (r == 0) {
-            const int row = 16 * w + 4 * g + i;
-            vdgam[row] = sg_;
-            vddl[row] = sd;
-            vdb[row] = sb;
+            const int row = 16 * rb + 4 * g + i;
+            vdgam[hf * C + row] = sg_;
+            vddl[hf * C + row] = sd;
+            vdb[hf * C + row] = sb;
         }
     }
     __syncthreads();
@@ -812,10 +838,14 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(Args a) {
             rs += Lc[t * LC + j];
             cs += Lc[j * LC + t];
         }
-        const float e = vdl[t] * vddl[t];
-        float dg = vgam[t] * vdgam[t] - e + rs - cs;
+        const float ddl = vddl[t] + vddl[C + t], dgam = vdgam[t] + vdgam[C + t];
+        const float e = vdl[t] * ddl;
+        float dg = vgam[t] * dgam - e + rs - cs;
         const float tot = wave_sum(e);
-        if (t == 63) dg += gC * (vred[0] + vred[1] + vred[2] + vred[3]) + tot;
+        float red = 0.f;
+#pragma unroll
+        for (int q = 0; q < GW; ++q) red += vred[q];
+        if (t == 63) dg += rec[R::G + 64] * red + tot;
         // suffix sums: d log a_t = sum over r >= t of dg_r
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
@@ -825,7 +855,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(Args a) {
         const int tt = t0 + t;
         if (tt < a.T) {
             a.dlog_a[((size_t)b * a.T + tt) * a.H + h] = dg;
-            a.dbeta[((size_t)b * a.T + tt) * a.H + h] = vdb[t];
+            a.dbeta[((size_t)b * a.T + tt) * a.H + h] = vdb[t] + vdb[C + t];
         }
     }
 }

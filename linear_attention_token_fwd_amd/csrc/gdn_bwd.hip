@@ -102,7 +102,7 @@ gdn_status validate(const gdn_bwd_params *p) {
 template <int D> size_t prep_lds() { return (3 * 64 * (D + 4) + 2 * 64 * 68 + 3 * 64 + 4 * 16 * 20) * sizeof(float); }
 template <int D> size_t state_lds() { return (2 * 64 * (D + 4) + 64 * 20 + 16 * (D + 4) + 64 * 20) * sizeof(float); }
 template <int D> size_t dstate_lds() { return (3 * 64 * (D + 4) + 64 * 20 + 16 * (D + 4) + 16 * 68) * sizeof(float); }
-template <int D> size_t grad_lds() { return (3 * 64 * (D + 4) + 3 * 64 * 68 + 8 * 64) * sizeof(float); }
+template <int D> size_t grad_lds() { return (3 * 64 * (D + 4) + 3 * 64 * 68 + 11 * 64) * sizeof(float); }
 
 gdn_status set_attributes() {
     static std::once_flag once;
@@ -178,7 +178,7 @@ gdn_status launch_all(const gdn_bwd_params *p, hipEvent_t *ev, hipStream_t s) {
     bwd_dstate_kernel<D><<<rows, NT, dstate_lds<D>(), s>>>(a);
     if (!post()) return GDN_ERR_HIP;
     pre();
-    bwd_grad_kernel<D><<<chunks, NT, grad_lds<D>(), s>>>(a);
+    bwd_grad_kernel<D><<<chunks, gdnb::GNT, grad_lds<D>(), s>>>(a);
     if (!post()) return GDN_ERR_HIP;
     pre();
     bwd_norm_kernel<IO, D><<<tokens, NT, 0, s>>>(a);
