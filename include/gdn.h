@@ -320,7 +320,7 @@ int gdn_graph_cache_count(void);
  * Supported: Dk = Dv in {64, 128}, io_dtype GDN_BF16 or GDN_F32.  All
  * arithmetic is fp32 (fp32 MFMA); bf16 inputs are read exactly and bf16
  * outputs rounded to nearest even once.
- * Execution: the 8 kernels run in order on `stream`; nothing else is used.
+ * Execution: the 7 kernels run in order on `stream`; nothing else is used.
  * The workspace (gdn_bwd_workspace_bytes(), 256-byte aligned) holds the
  * recomputed chunk quantities in fp32: about (717 D + 8320 + 2 D^2) * 4
  * bytes per (batch row, head, 64-token chunk), 3.2 GB at B = 1, T = 32760,

@@ -25,8 +25,8 @@
 //   bwd_out_kernel       per chunk: O, then the gated RMS norm's backward (dO, dgate)
 //   bwd_dstate_kernel    per 16 value rows: the entry-state gradients, last chunk first
 //   bwd_grad_kernel      per chunk: dq^, dk^, dv^, d log a, db
-//   bwd_norm_kernel      per token: L2 norm and SiLU backward, dz in place
-//   bwd_conv_kernel      per chunk: dq, dk, dv, conv-weight partial sums
+//   bwd_prologue_kernel  per chunk: L2 norm, SiLU and conv backward: dq, dk,
+//                        dv, conv-weight partial sums
 //   bwd_reduce_kernel    the conv-weight and norm-weight sums
 #pragma once
 #include "frag.hpp"
@@ -50,9 +50,9 @@ template <int D> struct Rec {
     static constexpr int QP = 320 * D;       // Q'
     static constexpr int DK = 384 * D;       // diag(dl) K
     static constexpr int DO = 448 * D;       // dO
-    static constexpr int DXQ = 512 * D;      // dq^, then dz of q
-    static constexpr int DXK = 576 * D;      // dk^, then dz of k
-    static constexpr int DXV = 640 * D;      // dv^, then dz of v
+    static constexpr int DXQ = 512 * D;      // dq^
+    static constexpr int DXK = 576 * D;      // dk^
+    static constexpr int DXV = 640 * D;      // dv^
     static constexpr int TM = 704 * D;       // T [64][64]
     static constexpr int P = TM + 64 * 64;   // P [64][64]
     static constexpr int G = P + 64 * 64;    // g [64], then gC
@@ -861,95 +861,132 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// Per token row (wave = one token of one head): the backward of the L2 norm
-// (q, k) and of SiLU; dz replaces dq^, dk^, dv^ in the record.
-template <class IO, int D>
-__global__ __launch_bounds__(NT) void bwd_norm_kernel(Args a) {
-    typedef Rec<D> R;
-    constexpr int PER = D / 64;
-    const int h = blockIdx.y, b = blockIdx.z, w = threadIdx.x / 64, lane = threadIdx.x % 64;
-    const int t = blockIdx.x * 4 + w;
-    if (t >= a.T) return;
-    float *rec = record<D>(a, b, h, t / C);
-    const int tl = t % C;
-    const IO *src[3] = {static_cast<const IO *>(a.q), static_cast<const IO *>(a.k), static_cast<const IO *>(a.v)};
-    const float *cw[3] = {a.conv_q, a.conv_k, a.conv_v};
-    const int dxo[3] = {R::DXQ, R::DXK, R::DXV};
-#pragma unroll
-    for (int x = 0; x < 3; ++x) {
-        float z[PER], s[PER], dx[PER], ss = 0.f, dot = 0.f;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            const int ch = lane + 64 * e;
-            const float *wt = cw[x] + ((size_t)h * D + ch) * 4;
-            float zz = 0.f;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int sp = t - 3 + j;
-                if (sp >= 0) zz = fmaf(wt[j], to_f(src[x][(((size_t)b * a.T + sp) * a.H + h) * D + ch]), zz);
-            }
-            z[e] = zz;
-            s[e] = silu(zz);
-            dx[e] = rec[dxo[x] + tl * D + ch];
-            ss += s[e] * s[e];
-        }
-        if (x < 2) {
-            ss = wave_sum(ss);
-            const float rho = 1.0f / sqrtf(ss + a.eps_l2);
-#pragma unroll
-            for (int e = 0; e < PER; ++e) dot += s[e] * rho * dx[e];
-            dot = wave_sum(dot);
-#pragma unroll
-            for (int e = 0; e < PER; ++e) dx[e] = rho * (dx[e] - s[e] * rho * dot);
-        }
-#pragma unroll
-        for (int e = 0; e < PER; ++e) rec[dxo[x] + tl * D + lane + 64 * e] = dx[e] * dsilu(z[e]);
-    }
-}
+// Per chunk, for q, k and v in turn: the backward of the L2 norm (q, k) and
+// of SiLU for the chunk's 64 tokens and the next 3 (dz, kept in LDS), then
+// dx_t = sum_j w_j dz_{t+3-j} (dz zero past the end) and the chunk's sums
+// dz_t x_{t-3+j} for the conv weights.  Thread: 8 channels of RUN
+// consecutive rows; its raw rows (RUN + 3, with the conv history) are loaded
+// once and serve the conv, its recomputation and the weight sums.
+template <int D> struct PrologueCfg {
+    static constexpr int G = D / 8, RUNS = NT / G, RUN = (C + 3 + RUNS - 1) / RUNS, ROWS = RUN + 3;
+    static constexpr int LZ = D + 4;
+};
 
-// ---------------------------------------------------------------------------
-// Per chunk: dx_t = sum_j w_j dz_{t+3-j} (dz zero past the end) for q, k, v,
-// and this chunk's sums dz_t x_{t-3+j} for the conv weights.  Thread: one
-// channel, a slice of the chunk's tokens.
 template <class IO, int D>
-__global__ __launch_bounds__(NT) void bwd_conv_kernel(Args a) {
+__global__ __launch_bounds__(NT) void bwd_prologue_kernel(Args a) {
     typedef Rec<D> R;
-    constexpr int SL = NT / D, TPS = C / SL;  // token slices, tokens per slice
-    __shared__ float sP[SL][3 * D * 4];
+    typedef PrologueCfg<D> P;
+    constexpr int G = P::G, RUN = P::RUN, ROWS = P::ROWS, LZ = P::LZ;
+    extern __shared__ __align__(16) float lds[];
+    float *sZ = lds;                    // dz, rows 0..66 of the chunk
+    float *sW = sZ + (C + 3) * LZ;      // conv-weight partial sums [RUNS][D * 4]
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t0 = c * C;
-    const int ch = threadIdx.x % D, sl = threadIdx.x / D;
+    const int tid = threadIdx.x, cg = tid % G, run = tid / G, r0 = run * RUN;
     const IO *src[3] = {static_cast<const IO *>(a.q), static_cast<const IO *>(a.k), static_cast<const IO *>(a.v)};
     IO *dst[3] = {static_cast<IO *>(a.dq), static_cast<IO *>(a.dk), static_cast<IO *>(a.dv)};
     const float *cw[3] = {a.conv_q, a.conv_k, a.conv_v};
     const int dxo[3] = {R::DXQ, R::DXK, R::DXV};
-#pragma unroll
+#pragma unroll 1
     for (int x = 0; x < 3; ++x) {
-        float wt[4], pw[4] = {0.f, 0.f, 0.f, 0.f};
+        Row8<IO> raw[ROWS];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) wt[j] = cw[x][((size_t)h * D + ch) * 4 + j];
-        for (int tl = sl * TPS; tl < (sl + 1) * TPS; ++tl) {
-            const int t = t0 + tl;
-            if (t >= a.T) break;
-            const float dz = record<D>(a, b, h, c)[dxo[x] + tl * D + ch];
-            float dx = 0.f;
+        for (int rr = 0; rr < ROWS; ++rr) {
+            const int sp = t0 + r0 - 3 + rr;
+            const bool ok = sp >= 0 && sp < a.T;
+            raw[rr].load(src[x] + ((((size_t)b * a.T + (ok ? sp : 0)) * a.H + h) * D) + 8 * cg, ok);
+        }
+        floatx4 dxh[RUN][2];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int u = t + 3 - j;  // the output that x_t feeds through tap j
-                if (u < a.T) dx = fmaf(wt[j], record<D>(a, b, h, u / C)[dxo[x] + (u % C) * D + ch], dx);
-                const int sp = t - 3 + j;
-                if (sp >= 0) pw[j] = fmaf(dz, to_f(src[x][(((size_t)b * a.T + sp) * a.H + h) * D + ch]), pw[j]);
+        for (int rt = 0; rt < RUN; ++rt) {
+            const int t = t0 + r0 + rt;
+            const bool ok = t < a.T && r0 + rt < C + 3;
+            const float *pr = ok ? record<D>(a, b, h, t / C) + dxo[x] + (t % C) * D + 8 * cg : nullptr;
+            dxh[rt][0] = ok ? *reinterpret_cast<const floatx4 *>(pr) : z4();
+            dxh[rt][1] = ok ? *reinterpret_cast<const floatx4 *>(pr + 4) : z4();
+        }
+        float wt[8][4];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float4 wv = *reinterpret_cast<const float4 *>(cw[x] + ((size_t)h * D + 8 * cg + i) * 4);
+            wt[i][0] = wv.x; wt[i][1] = wv.y; wt[i][2] = wv.z; wt[i][3] = wv.w;
+        }
+        float pw[8][4];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pw[i][j] = 0.f;
+#pragma unroll
+        for (int rt = 0; rt < RUN; ++rt) {
+            const int tl = r0 + rt, t = t0 + tl;
+            float z[8], sv[8], dv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float zz = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) zz = fmaf(wt[i][j], raw[rt + j].get(i), zz);
+                z[i] = zz;
+                sv[i] = silu(zz);
+                dv[i] = dxh[rt][i / 4][i % 4];
             }
-            dst[x][(((size_t)b * a.T + t) * a.H + h) * D + ch] = (IO)dx;
+            if (x < 2) {
+                float ss = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ss += sv[i] * sv[i];
+                ss = gdn::group_sum<G>(ss);
+                const float rho = 1.0f / sqrtf(ss + a.eps_l2);
+                float dot = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) dot += sv[i] * rho * dv[i];
+                dot = gdn::group_sum<G>(dot);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) dv[i] = rho * (dv[i] - sv[i] * rho * dot);
+            }
+            const bool valid = t < a.T;
+            float dz[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) dz[i] = valid ? dv[i] * dsilu(z[i]) : 0.f;
+            if (tl < C + 3) {
+                float *row = sZ + tl * LZ + 8 * cg;
+                *reinterpret_cast<float4 *>(row) = make_float4(dz[0], dz[1], dz[2], dz[3]);
+                *reinterpret_cast<float4 *>(row + 4) = make_float4(dz[4], dz[5], dz[6], dz[7]);
+            }
+            if (tl < C) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) pw[i][j] = fmaf(dz[i], raw[rt + j].get(i), pw[i][j]);
+            }
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sP[sl][(x * D + ch) * 4 + j] = pw[j];
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < 3 * D * 4; idx += NT) {
-        float s = 0.f;
+        for (int i = 0; i < 8; ++i)
+            *reinterpret_cast<float4 *>(sW + run * (D * 4) + (8 * cg + i) * 4) =
+                make_float4(pw[i][0], pw[i][1], pw[i][2], pw[i][3]);
+        __syncthreads();
+        // dx for the chunk's tokens
 #pragma unroll
-        for (int q = 0; q < SL; ++q) s += sP[q][idx];
-        a.part_conv[(((size_t)b * a.NC + c) * a.H + h) * (3 * D * 4) + idx] = s;
+        for (int rt = 0; rt < RUN; ++rt) {
+            const int tl = r0 + rt, t = t0 + tl;
+            if (tl < C && t < a.T) {
+                float dx[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    float acc = 0.f;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc = fmaf(wt[i][j], sZ[(tl + 3 - j) * LZ + 8 * cg + i], acc);
+                    dx[i] = acc;
+                }
+                IO *o = dst[x] + (((size_t)b * a.T + t) * a.H + h) * D + 8 * cg;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) o[i] = (IO)dx[i];
+            }
+        }
+        // the chunk's conv-weight sums, over the runs in a fixed order
+        for (int e = tid; e < D * 4; e += NT) {
+            float sum = 0.f;
+            for (int q = 0; q < P::RUNS; ++q) sum += sW[q * (D * 4) + e];
+            a.part_conv[(((size_t)b * a.NC + c) * a.H + h) * (3 * D * 4) + x * D * 4 + e] = sum;
+        }
+        __syncthreads();
     }
 }
 

@@ -1,5 +1,5 @@
 // gdn_bwd.hip -- host side of gdn_bwd (include/gdn.h): argument checks,
-// workspace carve-up and the eight launches of the backward pass.
+// workspace carve-up and the seven launches of the backward pass.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -15,9 +15,9 @@ using gdn::bf16;
 using gdnb::NT;
 
 constexpr size_t kAlign = 256;
-constexpr int kLaunches = 8;
-const char *const kNames[kLaunches] = {"bwd_prep_kernel", "bwd_state_kernel", "bwd_out_kernel", "bwd_dstate_kernel",
-                                       "bwd_grad_kernel", "bwd_norm_kernel",  "bwd_conv_kernel", "bwd_reduce_kernel"};
+constexpr int kLaunches = 7;
+const char *const kNames[kLaunches] = {"bwd_prep_kernel", "bwd_state_kernel",    "bwd_out_kernel",   "bwd_dstate_kernel",
+                                       "bwd_grad_kernel", "bwd_prologue_kernel", "bwd_reduce_kernel"};
 
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int n_chunks(int T) { return (T + gdnb::C - 1) / gdnb::C; }
@@ -102,6 +102,10 @@ gdn_status validate(const gdn_bwd_params *p) {
 template <int D> size_t prep_lds() { return (3 * 64 * (D + 4) + 2 * 64 * 68 + 3 * 64 + 4 * 16 * 20) * sizeof(float); }
 template <int D> size_t state_lds() { return (2 * 64 * (D + 4) + 64 * 20 + 16 * (D + 4) + 64 * 20) * sizeof(float); }
 template <int D> size_t dstate_lds() { return (3 * 64 * (D + 4) + 64 * 20 + 16 * (D + 4) + 16 * 68) * sizeof(float); }
+template <int D> size_t prologue_lds() {
+    typedef gdnb::PrologueCfg<D> P;
+    return ((64 + 3) * P::LZ + P::RUNS * D * 4) * sizeof(float);
+}
 template <int D> size_t grad_lds() { return (3 * 64 * (D + 4) + 3 * 64 * 68 + 11 * 64) * sizeof(float); }
 
 gdn_status set_attributes() {
@@ -120,6 +124,10 @@ gdn_status set_attributes() {
             {reinterpret_cast<const void *>(&gdnb::bwd_state_kernel<64>), state_lds<64>()},
             {reinterpret_cast<const void *>(&gdnb::bwd_dstate_kernel<128>), dstate_lds<128>()},
             {reinterpret_cast<const void *>(&gdnb::bwd_dstate_kernel<64>), dstate_lds<64>()},
+            {reinterpret_cast<const void *>(&gdnb::bwd_prologue_kernel<bf16, 128>), prologue_lds<128>()},
+            {reinterpret_cast<const void *>(&gdnb::bwd_prologue_kernel<bf16, 64>), prologue_lds<64>()},
+            {reinterpret_cast<const void *>(&gdnb::bwd_prologue_kernel<float, 128>), prologue_lds<128>()},
+            {reinterpret_cast<const void *>(&gdnb::bwd_prologue_kernel<float, 64>), prologue_lds<64>()},
             {reinterpret_cast<const void *>(&gdnb::bwd_grad_kernel<128>), grad_lds<128>()},
             {reinterpret_cast<const void *>(&gdnb::bwd_grad_kernel<64>), grad_lds<64>()},
         };
@@ -152,7 +160,7 @@ gdn_status launch_all(const gdn_bwd_params *p, hipEvent_t *ev, hipStream_t s) {
 
     // chains: 8 equal slices of the work list (whole heads each), one per XCD
     const int heads_per_xcd = (p->B * p->H + 7) / 8;
-    const dim3 chunks(a.NC, p->H, p->B), rows(8 * heads_per_xcd * (D / 16)), tokens((p->T + 3) / 4, p->H, p->B);
+    const dim3 chunks(a.NC, p->H, p->B), rows(8 * heads_per_xcd * (D / 16));
     const int nred = p->H * D * 13;
     const dim3 red((nred + NT - 1) / NT);
     int i = 0;
@@ -181,10 +189,7 @@ gdn_status launch_all(const gdn_bwd_params *p, hipEvent_t *ev, hipStream_t s) {
     bwd_grad_kernel<D><<<chunks, gdnb::GNT, grad_lds<D>(), s>>>(a);
     if (!post()) return GDN_ERR_HIP;
     pre();
-    bwd_norm_kernel<IO, D><<<tokens, NT, 0, s>>>(a);
-    if (!post()) return GDN_ERR_HIP;
-    pre();
-    bwd_conv_kernel<IO, D><<<chunks, NT, 0, s>>>(a);
+    bwd_prologue_kernel<IO, D><<<chunks, NT, prologue_lds<D>(), s>>>(a);
     if (!post()) return GDN_ERR_HIP;
     pre();
     bwd_reduce_kernel<D><<<red, NT, 0, s>>>(a);

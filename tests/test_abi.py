@@ -337,10 +337,11 @@ def test_bwd_workspace_bytes(lib):
 
 
 def test_bwd_launch_names(lib):
-    assert lib.gdn_bwd_launch_count() == 8
+    n = lib.gdn_bwd_launch_count()
+    assert n == 7
     names = gdn.gdn_bwd_launch_names()
-    assert names[0] == "bwd_prep_kernel" and names[-1] == "bwd_reduce_kernel" and len(set(names)) == 8
-    assert lib.gdn_bwd_launch_name(8) is None and lib.gdn_bwd_launch_name(-1) is None
+    assert names[0] == "bwd_prep_kernel" and names[-1] == "bwd_reduce_kernel" and len(set(names)) == n
+    assert lib.gdn_bwd_launch_name(n) is None and lib.gdn_bwd_launch_name(-1) is None
 
 
 BWD_CASES = [
@@ -382,6 +383,7 @@ def test_bwd_optional_outputs_may_be_null(lib):
 
 def test_bwd_timed_needs_events(lib):
     p = fake_bwd(lib)
-    events = (ctypes.c_void_p * 15)()
-    assert lib.gdn_bwd_timed(ctypes.byref(p), events, 15, None) == gdn.GDN_ERR_INVALID_ARG
-    assert lib.gdn_bwd_timed(ctypes.byref(p), None, 16, None) == gdn.GDN_ERR_INVALID_ARG
+    n = 2 * lib.gdn_bwd_launch_count()
+    events = (ctypes.c_void_p * (n - 1))()
+    assert lib.gdn_bwd_timed(ctypes.byref(p), events, n - 1, None) == gdn.GDN_ERR_INVALID_ARG
+    assert lib.gdn_bwd_timed(ctypes.byref(p), None, n, None) == gdn.GDN_ERR_INVALID_ARG
