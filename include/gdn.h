@@ -322,8 +322,8 @@ int gdn_graph_cache_count(void);
  * outputs rounded to nearest even once.
  * Execution: the 7 kernels run in order on `stream`; nothing else is used.
  * The workspace (gdn_bwd_workspace_bytes(), 256-byte aligned) holds the
- * recomputed chunk quantities in fp32: about (717 D + 8320 + 2 D^2) * 4
- * bytes per (batch row, head, 64-token chunk), 3.2 GB at B = 1, T = 32760,
+ * recomputed chunk quantities in fp32: about (909 D + 8320 + 2 D^2) * 4
+ * bytes per (batch row, head, 64-token chunk), 3.6 GB at B = 1, T = 32760,
  * H = 12, D = 128.
  * Errors: as for gdn_fwd.  GDN_ERR_INVALID_ARG for a NULL required pointer,
  * bad sizes, eps < 0 or not finite, or an output that overlaps an input,

@@ -58,7 +58,10 @@ template <int D> struct Rec {
     static constexpr int G = P + 64 * 64;    // g [64], then gC
     static constexpr int SC = G + 128;       // entry state S [D][D]
     static constexpr int DSN = SC + D * D;   // gradient of the exit state [D][D]
-    static constexpr int SIZE = DSN + D * D;
+    static constexpr int WT = DSN + D * D;   // W, key-major [D][64]
+    static constexpr int DKT = WT + 64 * D;  // D K, key-major
+    static constexpr int QPT = DKT + 64 * D; // Q', key-major
+    static constexpr int SIZE = QPT + 64 * D;
 };
 
 struct Args {
@@ -77,6 +80,7 @@ struct Args {
     float *rec;                                        // B H NC chunk records
     float *part_conv;                                  // [B NC H][3][D][4]
     float *part_norm;                                  // [B NC H][D]
+    float *sink;                                       // [B, H, D, D]: the chains' stores past either end
 };
 
 __device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
@@ -353,7 +357,9 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(Args a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * w + 4 * g + i, col = 16 * nt + r;
-            rec[R::QP + row * D + col] = sgam[row] * sQ[row * LX + col] - acc[i];
+            const float qp = sgam[row] * sQ[row * LX + col] - acc[i];
+            rec[R::QP + row * D + col] = qp;
+            sQ[row * LX + col] = qp;
         }
     }
     const float glast = sg[63];
@@ -361,107 +367,119 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(Args a) {
         const int tl = idx / D, ch = idx % D;
         rec[R::DK + idx] = expf(glast - sg[tl]) * sK[tl * LX + ch];
     }
+    __syncthreads();
+    // key-major copies of W, D K and Q' (the chains read them as B operands)
+    for (int idx = tid; idx < C * D; idx += NT) {
+        const int key = idx / C, tl = idx % C;
+        rec[R::WT + idx] = sV[tl * LX + key];
+        rec[R::DKT + idx] = expf(glast - sg[tl]) * sK[tl * LX + key];
+        rec[R::QPT + idx] = sQ[tl * LX + key];
+    }
 }
 
 // ---------------------------------------------------------------------------
-// Chain operands: whole [64][D] record matrices and a 16-column slice of one,
-// copied from a chunk record into LDS through registers, so that the next
-// chunk's loads are in flight while the current chunk computes.
-template <int D> constexpr int kPerM = 64 * D / 4 / NT;   // floatx4 per thread per matrix
+// The chains.  A workgroup owns 16 value rows of one head's state (4 waves);
+// each wave loads its own MFMA operands of a chunk straight into registers,
+// one chunk ahead (two register sets used in turn), so that a step waits for
+// no memory.  The items of a head are neighbours in the work list and share
+// one XCD's L2 (the 8 workgroups of a head read the same W and D K).
+template <int D> struct FwdOps {
+    static constexpr int KS = D / 16, NTW = D / 64;
+    floatx4 wa[KS];         // W rows 16 w + r, keys 16 ks + 4 g ..: A of W S^T
+    floatx4 kb[NTW][4];     // (D K)^T rows 16 nt + r (nt = w + 4 j), tokens 16 ks + 4 g ..: B of U^T D K
+    float ut[4];            // U~ (token 16 w + 4 g + i, value 16 vb + r)
+    float gC;
+};
 
 template <int D>
-__device__ __forceinline__ void stage_load(floatx4 (&m)[kPerM<D>], const float *src) {
+__device__ __forceinline__ void fwd_ops_load(FwdOps<D> &o, const float *rc, int vb) {
+    typedef Rec<D> R;
+    const int w = threadIdx.x / 64, lane = threadIdx.x % 64, r = lane % 16, g = lane / 16;
 #pragma unroll
-    for (int e = 0; e < kPerM<D>; ++e) {
-        const int idx = threadIdx.x + NT * e, row = idx / (D / 4), c4 = 4 * (idx % (D / 4));
-        m[e] = *reinterpret_cast<const floatx4 *>(src + row * D + c4);
-    }
-}
-template <int D>
-__device__ __forceinline__ void stage_store(const floatx4 (&m)[kPerM<D>], float *dst) {
+    for (int ks = 0; ks < FwdOps<D>::KS; ++ks)
+        o.wa[ks] = *reinterpret_cast<const floatx4 *>(rc + R::W + (16 * w + r) * D + 16 * ks + 4 * g);
 #pragma unroll
-    for (int e = 0; e < kPerM<D>; ++e) {
-        const int idx = threadIdx.x + NT * e, row = idx / (D / 4), c4 = 4 * (idx % (D / 4));
-        *reinterpret_cast<floatx4 *>(dst + row * (D + 4) + c4) = m[e];
-    }
-}
-// the 16 columns col0.. of a [64][D] matrix: one floatx4 per thread
-template <int D> __device__ __forceinline__ floatx4 slice_load(const float *src, int col0) {
-    return *reinterpret_cast<const floatx4 *>(src + (threadIdx.x / 4) * D + col0 + 4 * (threadIdx.x % 4));
-}
-__device__ __forceinline__ void slice_store(floatx4 v, float *dst) {
-    *reinterpret_cast<floatx4 *>(dst + (threadIdx.x / 4) * 20 + 4 * (threadIdx.x % 4)) = v;
+    for (int j = 0; j < FwdOps<D>::NTW; ++j)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            o.kb[j][ks] = *reinterpret_cast<const floatx4 *>(rc + R::DKT + (16 * (w + 4 * j) + r) * C + 16 * ks + 4 * g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o.ut[i] = rc[R::UT + (16 * w + 4 * g + i) * D + 16 * vb + r];
+    o.gC = rc[R::G + 64];
 }
 
-// ---------------------------------------------------------------------------
-// The forward chain over chunks for value rows 16 vb .. 16 vb + 15 of one
-// head: stores each chunk's entry state, then U = U~ - W S^T (wave w: tokens
-// 16w..) and S <- gC S + U^T D K.
+// The forward chain for value rows 16 vb .. of one head: each chunk's entry
+// state goes to its record; U = U~ - W S^T (wave w: tokens 16 w ..), then
+// S <- gC S + U^T D K (wave w: key tiles w, w + 4, ...).
 template <int D>
 __global__ __launch_bounds__(NT) void bwd_state_kernel(Args a) {
     typedef Rec<D> R;
-    constexpr int LX = D + 4, LSL = 16 + 4, LS = D + 4, LU = 16 + 4;
-    extern __shared__ __align__(16) float lds[];
-    float *sW = lds, *sDK = sW + 64 * LX, *sUT = sDK + 64 * LX, *sS = sUT + 64 * LSL, *sU = sS + 16 * LS;
-    // one work item per (batch row, head, 16 value rows); the items of a head
-    // are neighbours in the list, so they share one XCD's L2
+    typedef FwdOps<D> O;
+    constexpr int LS = D + 4, LU = 16 + 4;
+    __shared__ __align__(16) float sS[16 * LS];
+    __shared__ __align__(16) float sU[C * LU];
     constexpr int NV = D / 16;
     int pos;
     if (!gdn::xcd_position(blockIdx.x, a.B * a.H * NV, gridDim.x, pos)) return;
     const int vb = pos % NV, h = (pos / NV) % a.H, b = pos / NV / a.H;
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, r = lane % 16, g = lane / 16;
+    float *rec0 = record<D>(a, b, h, 0);
     for (int idx = tid; idx < 16 * D; idx += NT) {
         const int row = idx / D, col = idx % D;
-        sS[row * LS + col] = a.S0 ? a.S0[(((size_t)b * a.H + h) * D + 16 * vb + row) * D + col] : 0.f;
-    }
-    floatx4 pw[kPerM<D>], pk[kPerM<D>], pu;
-    {
-        const float *r0 = record<D>(a, b, h, 0);
-        stage_load<D>(pw, r0 + R::W);
-        stage_load<D>(pk, r0 + R::DK);
-        pu = slice_load<D>(r0 + R::UT, 16 * vb);
-        stage_store<D>(pw, sW);
-        stage_store<D>(pk, sDK);
-        slice_store(pu, sUT);
+        const float v = a.S0 ? a.S0[(((size_t)b * a.H + h) * D + 16 * vb + row) * D + col] : 0.f;
+        sS[row * LS + col] = v;
+        rec0[R::SC + (16 * vb + row) * D + col] = v;
     }
     __syncthreads();
-    for (int c = 0; c < a.NC; ++c) {
-        float *rec = record<D>(a, b, h, c);
-        if (c + 1 < a.NC) {
-            const float *rn = record<D>(a, b, h, c + 1);
-            stage_load<D>(pw, rn + R::W);
-            stage_load<D>(pk, rn + R::DK);
-            pu = slice_load<D>(rn + R::UT, 16 * vb);
+
+    auto step = [&](const O &o, int c) {
+        // U = U~ - W S^T for tokens 16 w .. (B operand: S rows r, read k-contiguous)
+        floatx4 acc = z4();
+#pragma unroll
+        for (int ks = 0; ks < O::KS; ++ks) {
+            const floatx4 sv = *reinterpret_cast<const floatx4 *>(sS + r * LS + 16 * ks + 4 * g);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(o.wa[ks][j], sv[j], acc, 0, 0, 0);
         }
-        const float gC = rec[R::G + 64];
-        for (int idx = tid; idx < 16 * D; idx += NT) {
-            const int row = idx / D, col = idx % D;
-            rec[R::SC + (16 * vb + row) * D + col] = sS[row * LS + col];
-        }
-        {
-            const floatx4 acc = mm16<true, true, D>(z4(), sW, LX, 16 * w, sS, LS, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sU[(16 * w + 4 * g + i) * LU + r] = o.ut[i] - acc[i];
+        gdn::lds_barrier();
+        // S <- gC S + U^T D K on this wave's key tiles; the result is the next
+        // chunk's entry state (after the last chunk: the sink).  Loads and
+        // stores are unconditional so that the wait counts stay exact.
+        float *rn = c + 1 < a.NC ? record<D>(a, b, h, c + 1) + R::SC : a.sink + ((size_t)b * a.H + h) * D * D;
+#pragma unroll
+        for (int j = 0; j < O::NTW; ++j) {
+            const int nt = w + 4 * j;
+            floatx4 s4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s4[i] = o.gC * sS[(4 * g + i) * LS + 16 * nt + r];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    s4 = __builtin_amdgcn_mfma_f32_16x16x4f32(sU[(16 * ks + 4 * g + jj) * LU + r], o.kb[j][ks][jj], s4,
+                                                             0, 0, 0);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int tok = 16 * w + 4 * g + i;
-                sU[tok * LU + r] = sUT[tok * LSL + r] - acc[i];
+                sS[(4 * g + i) * LS + 16 * nt + r] = s4[i];
+                rn[(16 * vb + 4 * g + i) * D + 16 * nt + r] = s4[i];
             }
         }
         gdn::lds_barrier();
-        for (int nt = w; nt < D / 16; nt += 4) {
-            floatx4 acc;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = gC * sS[(4 * g + i) * LS + 16 * nt + r];
-            acc = mm16<false, false, C>(acc, sU, LU, 0, sDK, LX, 16 * nt);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sS[(4 * g + i) * LS + 16 * nt + r] = acc[i];
-        }
-        gdn::lds_barrier();
-        if (c + 1 < a.NC) {
-            stage_store<D>(pw, sW);
-            stage_store<D>(pk, sDK);
-            slice_store(pu, sUT);
-        }
-        gdn::lds_barrier();
+    };
+
+    O oa, ob;
+    fwd_ops_load<D>(oa, rec0, vb);
+    // (the scheduling barriers keep the next chunk's loads ahead of the step)
+    for (int c = 0; c < a.NC; c += 2) {
+        fwd_ops_load<D>(ob, record<D>(a, b, h, min(c + 1, a.NC - 1)), vb);
+        __builtin_amdgcn_sched_barrier(0);
+        step(oa, c);
+        if (c + 1 >= a.NC) break;
+        fwd_ops_load<D>(oa, record<D>(a, b, h, min(c + 2, a.NC - 1)), vb);
+        __builtin_amdgcn_sched_barrier(0);
+        step(ob, c + 1);
     }
 }
 
@@ -535,84 +553,115 @@ __global__ __launch_bounds__(NT) void bwd_out_kernel(Args a) {
 }
 
 // ---------------------------------------------------------------------------
+// Operands of one reverse-chain step, per wave (see FwdOps).
+template <int D> struct RevOps {
+    static constexpr int KS = D / 16, NTW = D / 64;
+    floatx4 ka[KS];         // D K rows 16 w + r (tokens), keys 16 ks + 4 g ..: B of dS (D K)^T
+    floatx4 wb[NTW][4];     // W^T rows 16 nt + r (keys), tokens 16 ks + 4 g ..: B of X W
+    floatx4 qb[NTW][4];     // Q'^T likewise: B of dO^T Q'
+    float oa[4][4];         // dO (token 16 ks + 4 g + jj, value 16 vb + r): A of dO^T Q'
+    float gC;
+};
+
+template <int D>
+__device__ __forceinline__ void rev_ops_load(RevOps<D> &o, const float *rc, int vb) {
+    typedef Rec<D> R;
+    const int w = threadIdx.x / 64, lane = threadIdx.x % 64, r = lane % 16, g = lane / 16;
+#pragma unroll
+    for (int ks = 0; ks < RevOps<D>::KS; ++ks)
+        o.ka[ks] = *reinterpret_cast<const floatx4 *>(rc + R::DK + (16 * w + r) * D + 16 * ks + 4 * g);
+#pragma unroll
+    for (int j = 0; j < RevOps<D>::NTW; ++j)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int off = (16 * (w + 4 * j) + r) * C + 16 * ks + 4 * g;
+            o.wb[j][ks] = *reinterpret_cast<const floatx4 *>(rc + R::WT + off);
+            o.qb[j][ks] = *reinterpret_cast<const floatx4 *>(rc + R::QPT + off);
+        }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) o.oa[ks][jj] = rc[R::DO + (16 * ks + 4 * g + jj) * D + 16 * vb + r];
+    o.gC = rc[R::G + 64];
+}
+
 // Entry-state gradients for value rows 16 vb .. of one head, last chunk
-// first: stores the exit-state gradient of each chunk, then
-// dS <- gC dS - (dS (D K)^T) W + dO^T Q'.
+// first.  Each chunk's exit-state gradient goes to its record; then
+// dS <- gC dS - (dS (D K)^T) W + dO^T Q' (X = dS (D K)^T: wave w tokens 16 w ..;
+// the update: wave w key tiles w, w + 4, ...).
 template <int D>
 __global__ __launch_bounds__(NT) void bwd_dstate_kernel(Args a) {
     typedef Rec<D> R;
-    constexpr int LX = D + 4, LSL = 16 + 4, LS = D + 4, LXX = C + 4;
-    extern __shared__ __align__(16) float lds[];
-    float *sDK = lds, *sW = sDK + 64 * LX, *sQP = sW + 64 * LX, *sDO = sQP + 64 * LX, *sD = sDO + 64 * LSL;
-    float *sX = sD + 16 * LS;
-    // one work item per (batch row, head, 16 value rows); the items of a head
-    // are neighbours in the list, so they share one XCD's L2
+    typedef RevOps<D> O;
+    constexpr int LS = D + 4, LXX = C + 4;
+    __shared__ __align__(16) float sD[16 * LS];
+    __shared__ __align__(16) float sX[16 * LXX];
     constexpr int NV = D / 16;
     int pos;
     if (!gdn::xcd_position(blockIdx.x, a.B * a.H * NV, gridDim.x, pos)) return;
     const int vb = pos % NV, h = (pos / NV) % a.H, b = pos / NV / a.H;
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, r = lane % 16, g = lane / 16;
+    float *recl = record<D>(a, b, h, a.NC - 1);
     for (int idx = tid; idx < 16 * D; idx += NT) {
         const int row = idx / D, col = idx % D;
-        sD[row * LS + col] = a.dS_T ? a.dS_T[(((size_t)b * a.H + h) * D + 16 * vb + row) * D + col] : 0.f;
-    }
-    floatx4 pk[kPerM<D>], pw[kPerM<D>], pq[kPerM<D>], po;
-    {
-        const float *r0 = record<D>(a, b, h, a.NC - 1);
-        stage_load<D>(pk, r0 + R::DK);
-        stage_load<D>(pw, r0 + R::W);
-        stage_load<D>(pq, r0 + R::QP);
-        po = slice_load<D>(r0 + R::DO, 16 * vb);
-        stage_store<D>(pk, sDK);
-        stage_store<D>(pw, sW);
-        stage_store<D>(pq, sQP);
-        slice_store(po, sDO);
+        const float v = a.dS_T ? a.dS_T[(((size_t)b * a.H + h) * D + 16 * vb + row) * D + col] : 0.f;
+        sD[row * LS + col] = v;
+        recl[R::DSN + (16 * vb + row) * D + col] = v;
     }
     __syncthreads();
-    for (int c = a.NC - 1; c >= 0; --c) {
-        float *rec = record<D>(a, b, h, c);
-        if (c > 0) {
-            const float *rn = record<D>(a, b, h, c - 1);
-            stage_load<D>(pk, rn + R::DK);
-            stage_load<D>(pw, rn + R::W);
-            stage_load<D>(pq, rn + R::QP);
-            po = slice_load<D>(rn + R::DO, 16 * vb);
-        }
-        const float gC = rec[R::G + 64];
-        for (int idx = tid; idx < 16 * D; idx += NT) {
-            const int row = idx / D, col = idx % D;
-            rec[R::DSN + (16 * vb + row) * D + col] = sD[row * LS + col];
-        }
-        {
-            // X = dS (D K)^T: 16 value rows x 64 tokens, wave w tokens 16w..
-            const floatx4 acc = mm16<true, true, D>(z4(), sD, LS, 0, sDK, LX, 16 * w);
+
+    auto step = [&](const O &o, int c) {
+        // X = dS (D K)^T: value rows x tokens 16 w .. (A operand: dS rows r, k-contiguous)
+        floatx4 acc = z4();
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sX[(4 * g + i) * LXX + 16 * w + r] = acc[i];
+        for (int ks = 0; ks < O::KS; ++ks) {
+            const floatx4 dv = *reinterpret_cast<const floatx4 *>(sD + r * LS + 16 * ks + 4 * g);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(dv[j], o.ka[ks][j], acc, 0, 0, 0);
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sX[(4 * g + i) * LXX + 16 * w + r] = acc[i];
         gdn::lds_barrier();
-        for (int nt = w; nt < D / 16; nt += 4) {
-            const floatx4 xw = mm16<true, false, C>(z4(), sX, LXX, 0, sW, LX, 16 * nt);
-            const floatx4 oq = mm16<false, false, C>(z4(), sDO, LSL, 0, sQP, LX, 16 * nt);
+        // the result: the previous chunk's exit-state gradient, or dS0 (the
+        // sink if dS0 is not wanted); unconditional stores keep the wait counts exact
+        float *dst = c > 0 ? record<D>(a, b, h, c - 1) + R::DSN
+                           : (a.dS0 ? a.dS0 : a.sink) + ((size_t)b * a.H + h) * D * D;
+#pragma unroll
+        for (int j = 0; j < O::NTW; ++j) {
+            const int nt = w + 4 * j;
+            floatx4 d4, xw = z4(), oq = z4();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) d4[i] = o.gC * sD[(4 * g + i) * LS + 16 * nt + r];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const floatx4 xv = *reinterpret_cast<const floatx4 *>(sX + r * LXX + 16 * ks + 4 * g);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    xw = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[jj], o.wb[j][ks][jj], xw, 0, 0, 0);
+                    oq = __builtin_amdgcn_mfma_f32_16x16x4f32(o.oa[ks][jj], o.qb[j][ks][jj], oq, 0, 0, 0);
+                }
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float *p = sD + (4 * g + i) * LS + 16 * nt + r;
-                *p = gC * *p - xw[i] + oq[i];
+                const float v = d4[i] - xw[i] + oq[i];
+                sD[(4 * g + i) * LS + 16 * nt + r] = v;
+                dst[(16 * vb + 4 * g + i) * D + 16 * nt + r] = v;
             }
         }
         gdn::lds_barrier();
-        if (c > 0) {
-            stage_store<D>(pk, sDK);
-            stage_store<D>(pw, sW);
-            stage_store<D>(pq, sQP);
-            slice_store(po, sDO);
-        }
-        gdn::lds_barrier();
+    };
+
+    O oa, ob;
+    rev_ops_load<D>(oa, recl, vb);
+    for (int c = a.NC - 1; c >= 0; c -= 2) {
+        rev_ops_load<D>(ob, record<D>(a, b, h, max(c - 1, 0)), vb);
+        __builtin_amdgcn_sched_barrier(0);
+        step(oa, c);
+        if (c - 1 < 0) break;
+        rev_ops_load<D>(oa, record<D>(a, b, h, max(c - 2, 0)), vb);
+        __builtin_amdgcn_sched_barrier(0);
+        step(ob, c - 1);
     }
-    if (a.dS0)
-        for (int idx = tid; idx < 16 * D; idx += NT) {
-            const int row = idx / D, col = idx % D;
-            a.dS0[(((size_t)b * a.H + h) * D + 16 * vb + row) * D + col] = sD[row * LS + col];
-        }
 }
 
 // ---------------------------------------------------------------------------

@@ -26,7 +26,7 @@ size_t elem_size(gdn_dtype d) { return d == GDN_BF16 ? 2 : 4; }
 size_t rec_floats(int D) { return D == 128 ? gdnb::Rec<128>::SIZE : gdnb::Rec<64>::SIZE; }
 
 struct Layout {
-    size_t rec, part_conv, part_norm, total;
+    size_t rec, part_conv, part_norm, sink, total;
 };
 
 Layout layout(const gdn_bwd_params *p) {
@@ -35,7 +35,8 @@ Layout layout(const gdn_bwd_params *p) {
     L.rec = 0;
     L.part_conv = round_up(B * H * NC * rec_floats(p->Dk) * sizeof(float));
     L.part_norm = L.part_conv + round_up(B * NC * H * 12 * D * sizeof(float));
-    L.total = L.part_norm + round_up(B * NC * H * D * sizeof(float));
+    L.sink = L.part_norm + round_up(B * NC * H * D * sizeof(float));
+    L.total = L.sink + round_up(B * H * D * D * sizeof(float));
     return L;
 }
 
@@ -100,8 +101,6 @@ gdn_status validate(const gdn_bwd_params *p) {
 }
 
 template <int D> size_t prep_lds() { return (3 * 64 * (D + 4) + 2 * 64 * 68 + 3 * 64 + 4 * 16 * 20) * sizeof(float); }
-template <int D> size_t state_lds() { return (2 * 64 * (D + 4) + 64 * 20 + 16 * (D + 4) + 64 * 20) * sizeof(float); }
-template <int D> size_t dstate_lds() { return (3 * 64 * (D + 4) + 64 * 20 + 16 * (D + 4) + 16 * 68) * sizeof(float); }
 template <int D> size_t prologue_lds() {
     typedef gdnb::PrologueCfg<D> P;
     return ((64 + 3) * P::LZ + P::RUNS * D * 4) * sizeof(float);
@@ -120,10 +119,6 @@ gdn_status set_attributes() {
             {reinterpret_cast<const void *>(&gdnb::bwd_prep_kernel<bf16, 64>), prep_lds<64>()},
             {reinterpret_cast<const void *>(&gdnb::bwd_prep_kernel<float, 128>), prep_lds<128>()},
             {reinterpret_cast<const void *>(&gdnb::bwd_prep_kernel<float, 64>), prep_lds<64>()},
-            {reinterpret_cast<const void *>(&gdnb::bwd_state_kernel<128>), state_lds<128>()},
-            {reinterpret_cast<const void *>(&gdnb::bwd_state_kernel<64>), state_lds<64>()},
-            {reinterpret_cast<const void *>(&gdnb::bwd_dstate_kernel<128>), dstate_lds<128>()},
-            {reinterpret_cast<const void *>(&gdnb::bwd_dstate_kernel<64>), dstate_lds<64>()},
             {reinterpret_cast<const void *>(&gdnb::bwd_prologue_kernel<bf16, 128>), prologue_lds<128>()},
             {reinterpret_cast<const void *>(&gdnb::bwd_prologue_kernel<bf16, 64>), prologue_lds<64>()},
             {reinterpret_cast<const void *>(&gdnb::bwd_prologue_kernel<float, 128>), prologue_lds<128>()},
@@ -157,6 +152,7 @@ gdn_status launch_all(const gdn_bwd_params *p, hipEvent_t *ev, hipStream_t s) {
     a.rec = reinterpret_cast<float *>(ws + L.rec);
     a.part_conv = reinterpret_cast<float *>(ws + L.part_conv);
     a.part_norm = reinterpret_cast<float *>(ws + L.part_norm);
+    a.sink = reinterpret_cast<float *>(ws + L.sink);
 
     // chains: 8 equal slices of the work list (whole heads each), one per XCD
     const int heads_per_xcd = (p->B * p->H + 7) / 8;
@@ -177,13 +173,13 @@ gdn_status launch_all(const gdn_bwd_params *p, hipEvent_t *ev, hipStream_t s) {
     bwd_prep_kernel<IO, D><<<chunks, NT, prep_lds<D>(), s>>>(a);
     if (!post()) return GDN_ERR_HIP;
     pre();
-    bwd_state_kernel<D><<<rows, NT, state_lds<D>(), s>>>(a);
+    bwd_state_kernel<D><<<rows, NT, 0, s>>>(a);
     if (!post()) return GDN_ERR_HIP;
     pre();
     bwd_out_kernel<IO, D><<<chunks, NT, 0, s>>>(a);
     if (!post()) return GDN_ERR_HIP;
     pre();
-    bwd_dstate_kernel<D><<<rows, NT, dstate_lds<D>(), s>>>(a);
+    bwd_dstate_kernel<D><<<rows, NT, 0, s>>>(a);
     if (!post()) return GDN_ERR_HIP;
     pre();
     bwd_grad_kernel<D><<<chunks, gdnb::GNT, grad_lds<D>(), s>>>(a);

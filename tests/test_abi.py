@@ -328,8 +328,9 @@ def fake_bwd(lib, B=2, T=300, H=3, D=128, io=gdn.GDN_BF16):
 def test_bwd_workspace_bytes(lib):
     p = fake_bwd(lib, B=1, T=32760, H=12, D=128)
     NC, D = 512, 128
-    per_chunk = (717 * D + 8320 + 2 * D * D) * 4
-    assert abs(p.workspace_bytes - 12 * NC * per_chunk) <= 3 * 256
+    per_chunk = (909 * D + 8320 + 2 * D * D) * 4
+    sink = 12 * D * D * 4  # the chains' stores past either end
+    assert abs(p.workspace_bytes - 12 * NC * per_chunk - sink) <= 4 * 256
     q = gdn.GdnBwdParams()
     q.B, q.T, q.H, q.Dk, q.Dv, q.io_dtype = 1, 100, 2, 96, 96, gdn.GDN_BF16
     assert lib.gdn_bwd_workspace_bytes(ctypes.byref(q)) == 0
