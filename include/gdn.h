@@ -320,7 +320,13 @@ int gdn_graph_cache_count(void);
  * Supported: Dk = Dv in {64, 128}, io_dtype GDN_BF16 or GDN_F32.  All
  * arithmetic is fp32 (fp32 MFMA); bf16 inputs are read exactly and bf16
  * outputs rounded to nearest even once.
- * Execution: the 7 kernels run in order on `stream`; nothing else is used.
+ * Execution: as for gdn_fwd, the call is ordered on `stream` like a single
+ * operation.  The two chains run over ranges of chunks on `stream`, and the
+ * kernels that follow each range run on one library stream per device
+ * (created on first use and kept, default priority), which waits for
+ * `stream` at the start of the call and which `stream` waits for at its end;
+ * enqueueing is serialised by a lock.  gdn_bwd_timed runs the 7 kernels once
+ * each, in order, on `stream` alone (same results, bit for bit).
  * The workspace (gdn_bwd_workspace_bytes(), 256-byte aligned) holds the
  * recomputed chunk quantities in fp32: about (909 D + 8320 + 2 D^2) * 4
  * bytes per (batch row, head, 64-token chunk), 3.6 GB at B = 1, T = 32760,

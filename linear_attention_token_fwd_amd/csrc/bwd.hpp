@@ -66,6 +66,7 @@ template <int D> struct Rec {
 
 struct Args {
     int B, T, H, NC;
+    int c0, c1;                                        // this launch's chunks: c0 .. c1 - 1
     const void *q, *k, *v, *gate, *dy;                 // [B, T, H, D], I/O dtype
     const float *log_a, *beta;                         // [B, T, H]
     const float *conv_q, *conv_k, *conv_v;             // [H D, 4]
@@ -171,7 +172,7 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(Args a) {
     extern __shared__ __align__(16) float lds[];
     float *sQ = lds, *sK = sQ + C * LX, *sV = sK + C * LX, *sT = sV + C * LX, *sM = sT + C * LC;
     float *sg = sM + C * LC, *sb = sg + C, *sgam = sb + C, *sTmp = sgam + C;
-    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t0 = c * C;
+    const int c = a.c0 + blockIdx.x, h = blockIdx.y, b = blockIdx.z, t0 = c * C;
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, r = lane % 16, g = lane / 16;
     float *rec = record<D>(a, b, h, c);
 
@@ -423,12 +424,19 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(Args a) {
     if (!gdn::xcd_position(blockIdx.x, a.B * a.H * NV, gridDim.x, pos)) return;
     const int vb = pos % NV, h = (pos / NV) % a.H, b = pos / NV / a.H;
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, r = lane % 16, g = lane / 16;
-    float *rec0 = record<D>(a, b, h, 0);
+    // the range's entry state: S0 for the first chunk, else what the previous
+    // range stored as this chunk's entry state
+    float *rec0 = record<D>(a, b, h, a.c0);
     for (int idx = tid; idx < 16 * D; idx += NT) {
         const int row = idx / D, col = idx % D;
-        const float v = a.S0 ? a.S0[(((size_t)b * a.H + h) * D + 16 * vb + row) * D + col] : 0.f;
-        sS[row * LS + col] = v;
-        rec0[R::SC + (16 * vb + row) * D + col] = v;
+        float *p = rec0 + R::SC + (16 * vb + row) * D + col;
+        if (a.c0 == 0) {
+            const float v = a.S0 ? a.S0[(((size_t)b * a.H + h) * D + 16 * vb + row) * D + col] : 0.f;
+            sS[row * LS + col] = v;
+            *p = v;
+        } else {
+            sS[row * LS + col] = *p;
+        }
     }
     __syncthreads();
 
@@ -472,12 +480,12 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(Args a) {
     O oa, ob;
     fwd_ops_load<D>(oa, rec0, vb);
     // (the scheduling barriers keep the next chunk's loads ahead of the step)
-    for (int c = 0; c < a.NC; c += 2) {
-        fwd_ops_load<D>(ob, record<D>(a, b, h, min(c + 1, a.NC - 1)), vb);
+    for (int c = a.c0; c < a.c1; c += 2) {
+        fwd_ops_load<D>(ob, record<D>(a, b, h, min(c + 1, a.c1 - 1)), vb);
         __builtin_amdgcn_sched_barrier(0);
         step(oa, c);
-        if (c + 1 >= a.NC) break;
-        fwd_ops_load<D>(oa, record<D>(a, b, h, min(c + 2, a.NC - 1)), vb);
+        if (c + 1 >= a.c1) break;
+        fwd_ops_load<D>(oa, record<D>(a, b, h, min(c + 2, a.c1 - 1)), vb);
         __builtin_amdgcn_sched_barrier(0);
         step(ob, c + 1);
     }
@@ -492,7 +500,7 @@ __global__ __launch_bounds__(NT) void bwd_out_kernel(Args a) {
     typedef Rec<D> R;
     constexpr int NTL = D / 16;
     __shared__ float sN[4][D];
-    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t0 = c * C;
+    const int c = a.c0 + blockIdx.x, h = blockIdx.y, b = blockIdx.z, t0 = c * C;
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, r = lane % 16, g = lane / 16;
     float *rec = record<D>(a, b, h, c);
     floatx4 o[NTL];
@@ -601,12 +609,19 @@ __global__ __launch_bounds__(NT) void bwd_dstate_kernel(Args a) {
     if (!gdn::xcd_position(blockIdx.x, a.B * a.H * NV, gridDim.x, pos)) return;
     const int vb = pos % NV, h = (pos / NV) % a.H, b = pos / NV / a.H;
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, r = lane % 16, g = lane / 16;
-    float *recl = record<D>(a, b, h, a.NC - 1);
+    // the range's last chunk's exit-state gradient: dS_T for the sequence's last
+    // chunk, else what the following range stored
+    float *recl = record<D>(a, b, h, a.c1 - 1);
     for (int idx = tid; idx < 16 * D; idx += NT) {
         const int row = idx / D, col = idx % D;
-        const float v = a.dS_T ? a.dS_T[(((size_t)b * a.H + h) * D + 16 * vb + row) * D + col] : 0.f;
-        sD[row * LS + col] = v;
-        recl[R::DSN + (16 * vb + row) * D + col] = v;
+        float *p = recl + R::DSN + (16 * vb + row) * D + col;
+        if (a.c1 == a.NC) {
+            const float v = a.dS_T ? a.dS_T[(((size_t)b * a.H + h) * D + 16 * vb + row) * D + col] : 0.f;
+            sD[row * LS + col] = v;
+            *p = v;
+        } else {
+            sD[row * LS + col] = *p;
+        }
     }
     __syncthreads();
 
@@ -653,12 +668,12 @@ __global__ __launch_bounds__(NT) void bwd_dstate_kernel(Args a) {
 
     O oa, ob;
     rev_ops_load<D>(oa, recl, vb);
-    for (int c = a.NC - 1; c >= 0; c -= 2) {
-        rev_ops_load<D>(ob, record<D>(a, b, h, max(c - 1, 0)), vb);
+    for (int c = a.c1 - 1; c >= a.c0; c -= 2) {
+        rev_ops_load<D>(ob, record<D>(a, b, h, max(c - 1, a.c0)), vb);
         __builtin_amdgcn_sched_barrier(0);
         step(oa, c);
-        if (c - 1 < 0) break;
-        rev_ops_load<D>(oa, record<D>(a, b, h, max(c - 2, 0)), vb);
+        if (c - 1 < a.c0) break;
+        rev_ops_load<D>(oa, record<D>(a, b, h, max(c - 2, a.c0)), vb);
         __builtin_amdgcn_sched_barrier(0);
         step(ob, c - 1);
     }
@@ -689,7 +704,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Args a) {
     float *La = L3 + C * LX, *Lb = La + C * LC, *Lc = Lb + C * LC;  // G; F; M
     float *vg = Lc + C * LC, *vb_ = vg + C, *vgam = vb_ + C, *vdl = vgam + C;
     float *vdgam = vdl + C, *vddl = vdgam + 2 * C, *vdb = vddl + 2 * C, *vred = vdb + 2 * C;
-    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t0 = c * C;
+    const int c = a.c0 + blockIdx.x, h = blockIdx.y, b = blockIdx.z, t0 = c * C;
     // wave w: row block rb (tokens 16 rb ..), column tiles hf, hf + 2, hf + 4, ...
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, r = lane % 16, g = lane / 16;
     const int rb = w % 4, hf = w / 4;
@@ -929,7 +944,7 @@ __global__ __launch_bounds__(NT) void bwd_prologue_kernel(Args a) {
     extern __shared__ __align__(16) float lds[];
     float *sZ = lds;                    // dz, rows 0..66 of the chunk
     float *sW = sZ + (C + 3) * LZ;      // conv-weight partial sums [RUNS][D * 4]
-    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t0 = c * C;
+    const int c = a.c0 + blockIdx.x, h = blockIdx.y, b = blockIdx.z, t0 = c * C;
     const int tid = threadIdx.x, cg = tid % G, run = tid / G, r0 = run * RUN;
     const IO *src[3] = {static_cast<const IO *>(a.q), static_cast<const IO *>(a.k), static_cast<const IO *>(a.v)};
     IO *dst[3] = {static_cast<IO *>(a.dq), static_cast<IO *>(a.dk), static_cast<IO *>(a.dv)};

@@ -2,8 +2,10 @@
 // workspace carve-up and the seven launches of the backward pass.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <map>
 #include <mutex>
 
 #include "../../include/gdn.h"
@@ -133,12 +135,35 @@ gdn_status set_attributes() {
     return result;
 }
 
-template <class IO, int D>
-gdn_status launch_all(const gdn_bwd_params *p, hipEvent_t *ev, hipStream_t s) {
-    using namespace gdnb;
+// Per device: one library stream (default priority, non-blocking) and the
+// events of the fork and joins, created on first use and kept.
+constexpr int kMaxRanges = 8;
+struct DeviceRes {
+    hipStream_t side = nullptr;
+    hipEvent_t ev[2 * kMaxRanges + 4] = {};
+};
+std::mutex g_mutex;
+std::map<int, DeviceRes> g_res;
+
+gdn_status device_res(DeviceRes *&out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GDN_ERR_HIP;
+    auto it = g_res.find(dev);
+    if (it == g_res.end()) {
+        DeviceRes r;
+        if (hipStreamCreateWithFlags(&r.side, hipStreamNonBlocking) != hipSuccess) return GDN_ERR_HIP;
+        for (hipEvent_t &e : r.ev)
+            if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return GDN_ERR_HIP;
+        it = g_res.emplace(dev, r).first;
+    }
+    out = &it->second;
+    return GDN_OK;
+}
+
+template <class IO, int D> gdnb::Args make_args(const gdn_bwd_params *p) {
     const Layout L = layout(p);
-    Args a;
-    a.B = p->B, a.T = p->T, a.H = p->H, a.NC = n_chunks(p->T);
+    gdnb::Args a;
+    a.B = p->B, a.T = p->T, a.H = p->H, a.NC = n_chunks(p->T), a.c0 = 0, a.c1 = a.NC;
     a.q = p->q, a.k = p->k, a.v = p->v, a.gate = p->gate, a.dy = p->dy;
     a.log_a = p->log_a, a.beta = p->beta;
     a.conv_q = p->conv_q, a.conv_k = p->conv_k, a.conv_v = p->conv_v, a.norm_w = p->norm_w;
@@ -153,43 +178,76 @@ gdn_status launch_all(const gdn_bwd_params *p, hipEvent_t *ev, hipStream_t s) {
     a.part_conv = reinterpret_cast<float *>(ws + L.part_conv);
     a.part_norm = reinterpret_cast<float *>(ws + L.part_norm);
     a.sink = reinterpret_cast<float *>(ws + L.sink);
+    return a;
+}
 
+// Launch i of the call on stream s over chunks [c0, c1) (per-chunk kernels
+// and chains; the last two kernels always cover everything).
+template <class IO, int D> bool launch(int i, gdnb::Args a, int c0, int c1, hipStream_t s) {
+    using namespace gdnb;
+    a.c0 = c0, a.c1 = c1;
+    const dim3 chunks(c1 - c0, a.H, a.B);
     // chains: 8 equal slices of the work list (whole heads each), one per XCD
-    const int heads_per_xcd = (p->B * p->H + 7) / 8;
-    const dim3 chunks(a.NC, p->H, p->B), rows(8 * heads_per_xcd * (D / 16));
-    const int nred = p->H * D * 13;
-    const dim3 red((nred + NT - 1) / NT);
-    int i = 0;
-    auto pre = [&] {
-        if (ev) (void)hipEventRecord(ev[2 * i], s);
+    const dim3 rows(8 * ((a.B * a.H + 7) / 8) * (D / 16));
+    switch (i) {
+    case 0: bwd_prep_kernel<IO, D><<<chunks, NT, prep_lds<D>(), s>>>(a); break;
+    case 1: bwd_state_kernel<D><<<rows, NT, 0, s>>>(a); break;
+    case 2: bwd_out_kernel<IO, D><<<chunks, NT, 0, s>>>(a); break;
+    case 3: bwd_dstate_kernel<D><<<rows, NT, 0, s>>>(a); break;
+    case 4: bwd_grad_kernel<D><<<chunks, GNT, grad_lds<D>(), s>>>(a); break;
+    case 5: bwd_prologue_kernel<IO, D><<<chunks, NT, prologue_lds<D>(), s>>>(a); break;
+    default: bwd_reduce_kernel<D><<<dim3((a.H * D * 13 + NT - 1) / NT), NT, 0, s>>>(a); break;
+    }
+    return hipGetLastError() == hipSuccess;
+}
+
+// Timed: every kernel once over all chunks on the caller's stream, events
+// around each.
+template <class IO, int D> gdn_status launch_timed(const gdn_bwd_params *p, hipEvent_t *ev, hipStream_t s) {
+    const gdnb::Args a = make_args<IO, D>(p);
+    for (int i = 0; i < kLaunches; ++i) {
+        (void)hipEventRecord(ev[2 * i], s);
+        if (!launch<IO, D>(i, a, 0, a.NC, s)) return GDN_ERR_HIP;
+        (void)hipEventRecord(ev[2 * i + 1], s);
+    }
+    return GDN_OK;
+}
+
+// The call: the two chains run over ranges of about 128 chunks on the
+// caller's stream; the output backward of a range follows its forward-chain
+// range, and the gradient kernel of a range its reverse-chain range, on the
+// library stream, so that both use the CUs the chains leave idle.
+template <class IO, int D> gdn_status launch_all(const gdn_bwd_params *p, hipStream_t s) {
+    const gdnb::Args a = make_args<IO, D>(p);
+    std::lock_guard<std::mutex> lock(g_mutex);
+    DeviceRes *res = nullptr;
+    gdn_status st = device_res(res);
+    if (st != GDN_OK) return st;
+    const int NC = a.NC, R = std::min(kMaxRanges, std::max(1, (NC + 127) / 128));
+    int bound[kMaxRanges + 1];
+    for (int r = 0; r <= R; ++r) bound[r] = (int)((long long)NC * r / R);
+    hipStream_t side = res->side;
+    hipEvent_t *ev = res->ev;
+    int e = 0;
+    auto fork = [&](hipStream_t from, hipStream_t to) {
+        hipEvent_t x = ev[e++];
+        return hipEventRecord(x, from) == hipSuccess && hipStreamWaitEvent(to, x, 0) == hipSuccess;
     };
-    auto post = [&]() -> bool {
-        if (hipGetLastError() != hipSuccess) return false;
-        if (ev) (void)hipEventRecord(ev[2 * i + 1], s);
-        ++i;
-        return true;
-    };
-    pre();
-    bwd_prep_kernel<IO, D><<<chunks, NT, prep_lds<D>(), s>>>(a);
-    if (!post()) return GDN_ERR_HIP;
-    pre();
-    bwd_state_kernel<D><<<rows, NT, 0, s>>>(a);
-    if (!post()) return GDN_ERR_HIP;
-    pre();
-    bwd_out_kernel<IO, D><<<chunks, NT, 0, s>>>(a);
-    if (!post()) return GDN_ERR_HIP;
-    pre();
-    bwd_dstate_kernel<D><<<rows, NT, 0, s>>>(a);
-    if (!post()) return GDN_ERR_HIP;
-    pre();
-    bwd_grad_kernel<D><<<chunks, gdnb::GNT, grad_lds<D>(), s>>>(a);
-    if (!post()) return GDN_ERR_HIP;
-    pre();
-    bwd_prologue_kernel<IO, D><<<chunks, NT, prologue_lds<D>(), s>>>(a);
-    if (!post()) return GDN_ERR_HIP;
-    pre();
-    bwd_reduce_kernel<D><<<red, NT, 0, s>>>(a);
-    if (!post()) return GDN_ERR_HIP;
+    if (!fork(s, side)) return GDN_ERR_HIP;
+    if (!launch<IO, D>(0, a, 0, NC, s)) return GDN_ERR_HIP;
+    for (int r = 0; r < R; ++r) {
+        if (!launch<IO, D>(1, a, bound[r], bound[r + 1], s) || !fork(s, side) ||
+            !launch<IO, D>(2, a, bound[r], bound[r + 1], side))
+            return GDN_ERR_HIP;
+    }
+    if (!fork(side, s)) return GDN_ERR_HIP;
+    for (int r = R - 1; r >= 0; --r) {
+        if (!launch<IO, D>(3, a, bound[r], bound[r + 1], s) || !fork(s, side) ||
+            !launch<IO, D>(4, a, bound[r], bound[r + 1], side))
+            return GDN_ERR_HIP;
+    }
+    if (!fork(side, s)) return GDN_ERR_HIP;
+    if (!launch<IO, D>(5, a, 0, NC, s) || !launch<IO, D>(6, a, 0, NC, s)) return GDN_ERR_HIP;
     return GDN_OK;
 }
 
@@ -199,9 +257,14 @@ gdn_status call(const gdn_bwd_params *p, hipEvent_t *ev, int n_ev, hipStream_t s
     if (ev && n_ev < 2 * kLaunches) return GDN_ERR_INVALID_ARG;
     st = set_attributes();
     if (st != GDN_OK) return st;
+    if (ev) {
+        if (p->io_dtype == GDN_BF16)
+            return p->Dk == 128 ? launch_timed<bf16, 128>(p, ev, s) : launch_timed<bf16, 64>(p, ev, s);
+        return p->Dk == 128 ? launch_timed<float, 128>(p, ev, s) : launch_timed<float, 64>(p, ev, s);
+    }
     if (p->io_dtype == GDN_BF16)
-        return p->Dk == 128 ? launch_all<bf16, 128>(p, ev, s) : launch_all<bf16, 64>(p, ev, s);
-    return p->Dk == 128 ? launch_all<float, 128>(p, ev, s) : launch_all<float, 64>(p, ev, s);
+        return p->Dk == 128 ? launch_all<bf16, 128>(p, s) : launch_all<bf16, 64>(p, s);
+    return p->Dk == 128 ? launch_all<float, 128>(p, s) : launch_all<float, 64>(p, s);
 }
 
 }  // namespace

@@ -115,3 +115,50 @@ def test_bwd_full_size_causal():
     ref = oracle_grads(short, g_short)
     head = {n: (got[n][:, :t1] if n in ("q", "k", "v", "gate", "log_a", "beta") else got[n]) for n in obwd.NAMES}
     compare(head, ref, "bf16", "full size, first 200 tokens")
+
+
+def test_bwd_ranges_match_single_pass():
+    """The call splits the chains into ranges (about 128 chunks each) on two
+    streams; the timed call runs every kernel once over all chunks on one
+    stream.  At the full size (512 chunks: 4 ranges), with dy and dS_T dense,
+    every gradient of the two must be identical, bit for bit."""
+    import ctypes
+    import linear_attention_token_fwd_amd as gdn
+    from bench import HipEvents
+    w = W[1]
+    inp = gdn_inputs.generate(w, seed=4321)
+    grads = gdn_inputs.generate_grads(w, seed=4322)
+    say("case: bwd ranges vs single pass, T=32760 H=12 d=128")
+    d = gdn.to_device(inp, dtype=torch.bfloat16)
+    dy = torch.from_numpy(grads["dy"]).to(torch.bfloat16).cuda()
+    dS = torch.from_numpy(grads["dS_T"]).cuda()
+    B, T, H, D = inp["q"].shape
+    lib = gdn.load()
+
+    def outputs():
+        o = {n: torch.full((B, T, H, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+             for n in ("q", "k", "v", "gate")}
+        o.update({n: torch.full((B, T, H), float("nan"), device="cuda") for n in ("log_a", "beta")})
+        o.update({n: torch.full((H * D, 4), float("nan"), device="cuda") for n in ("conv_q", "conv_k", "conv_v")})
+        o["norm_w"] = torch.full((H, D), float("nan"), device="cuda")
+        o["S0"] = torch.full((B, H, D, D), float("nan"), device="cuda")
+        return o
+
+    ws = torch.empty(gdn.gdn_bwd_workspace_bytes(B, T, H, D), dtype=torch.uint8, device="cuda")
+    args = (d["q"], d["k"], d["v"], d["log_a"], d["beta"], d["gate"], d["conv_q"], d["conv_k"], d["conv_v"],
+            d["norm_w"], d["S0"], dy, dS)
+    o1, o2 = outputs(), outputs()
+    stream = torch.cuda.current_stream().cuda_stream
+    p1 = gdn.bwd_params(*args, o1, ws)
+    assert lib.gdn_bwd(ctypes.byref(p1), ctypes.c_void_p(stream)) == gdn.GDN_OK
+    torch.cuda.synchronize()
+    ev = HipEvents()
+    n = 2 * lib.gdn_bwd_launch_count()
+    evs = ev.create(n)
+    p2 = gdn.bwd_params(*args, o2, ws)
+    assert lib.gdn_bwd_timed(ctypes.byref(p2), evs, n, ctypes.c_void_p(stream)) == gdn.GDN_OK
+    torch.cuda.synchronize()
+    for name in obwd.NAMES:
+        a, b = o1[name], o2[name]
+        assert torch.isfinite(a).all(), name
+        assert torch.equal(a, b), name
