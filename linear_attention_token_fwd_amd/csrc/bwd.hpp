@@ -20,7 +20,7 @@
 // Everything is fp32, on v_mfma_f32_16x16x4_f32.  The chunk quantities live
 // in the workspace as row-major fp32 arrays, one record per (batch row,
 // head, chunk).  Kernels, in launch order:
-//   bwd_prep_kernel      per chunk: recomputed q^, k^, v^; A, T, W, U~, P, Q', D K
+//   bwd_prep_kernel      per chunk (8 waves): recomputed q^, k^, v^; A, T, W, U~, P, Q', D K
 //   bwd_state_kernel     per 16 value rows: the forward chain, entry states
 //   bwd_out_kernel       per chunk: O, then the gated RMS norm's backward (dO, dgate)
 //   bwd_dstate_kernel    per 16 value rows: the entry-state gradients, last chunk first
@@ -39,6 +39,7 @@ using gdn::floatx4;
 
 constexpr int C = 64;     // tokens per chunk
 constexpr int NT = 256;   // threads per workgroup (4 waves)
+constexpr int GW = 8, GNT = 64 * GW;  // waves and threads of bwd_prep_kernel and bwd_grad_kernel
 
 // Offsets (in floats) inside one chunk record; all row-major.
 template <int D> struct Rec {
@@ -166,14 +167,16 @@ template <int D> __device__ __forceinline__ float *record(const Args &a, int b, 
 // the sequence's end are zero rows with b = 0 and log a = 0, which leave the
 // state and every gradient unchanged.
 template <class IO, int D>
-__global__ __launch_bounds__(NT) void bwd_prep_kernel(Args a) {
+__global__ __launch_bounds__(GNT) void bwd_prep_kernel(Args a) {
     typedef Rec<D> R;
     constexpr int LX = D + 4, LC = C + 4;
     extern __shared__ __align__(16) float lds[];
     float *sQ = lds, *sK = sQ + C * LX, *sV = sK + C * LX, *sT = sV + C * LX, *sM = sT + C * LC;
     float *sg = sM + C * LC, *sb = sg + C, *sgam = sb + C, *sTmp = sgam + C;
     const int c = a.c0 + blockIdx.x, h = blockIdx.y, b = blockIdx.z, t0 = c * C;
+    // 8 waves: wave w takes row block rb (16 tokens) and the column tiles hf, hf + 2, ...
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, r = lane % 16, g = lane / 16;
+    const int rb = w % 4, hf = w / 4;
     float *rec = record<D>(a, b, h, c);
 
     if (tid < 64) {
@@ -197,7 +200,7 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(Args a) {
     // consecutive tokens; its RUN + 3 input rows of q, k and v are all loaded
     // before any arithmetic.
     {
-        constexpr int G = D / 8, RUN = 64 / (NT / G), ROWS = RUN + 3;
+        constexpr int G = D / 8, RUN = 64 / (GNT / G), ROWS = RUN + 3;
         const int cg = tid % G, run = tid / G, s0 = t0 + run * RUN;
         const IO *src[3] = {static_cast<const IO *>(a.q), static_cast<const IO *>(a.k), static_cast<const IO *>(a.v)};
         const float *cw[3] = {a.conv_q, a.conv_k, a.conv_v};
@@ -237,9 +240,9 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(Args a) {
         }
     }
     __syncthreads();
-    // L2 norms of the q and k rows: wave w takes rows 16w..16w+15
-    for (int rr = 0; rr < 16; ++rr) {
-        const int row = 16 * w + rr;
+    // L2 norms of the q and k rows: wave w takes rows 8w..8w+7
+    for (int rr = 0; rr < 8; ++rr) {
+        const int row = 8 * w + rr;
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
             float *p = (x == 0 ? sQ : sK) + row * LX;
@@ -251,19 +254,20 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(Args a) {
         }
     }
     __syncthreads();
-    for (int idx = tid; idx < C * D / 4; idx += NT) {
+    for (int idx = tid; idx < C * D / 4; idx += GNT) {
         const int tl = idx / (D / 4), c4 = 4 * (idx % (D / 4));
         *reinterpret_cast<float4 *>(rec + R::XQ + tl * D + c4) = *reinterpret_cast<const float4 *>(sQ + tl * LX + c4);
         *reinterpret_cast<float4 *>(rec + R::XK + tl * D + c4) = *reinterpret_cast<const float4 *>(sK + tl * LX + c4);
         *reinterpret_cast<float4 *>(rec + R::XV + tl * D + c4) = *reinterpret_cast<const float4 *>(sV + tl * LX + c4);
     }
-    // A = strictly lower (b_i e^{g_i - g_j} k_i . k_j): wave w owns row block w
-    for (int nt = 0; nt < 4; ++nt) {
+    // A = strictly lower (b_i e^{g_i - g_j} k_i . k_j)
+    for (int j = 0; j < 2; ++j) {
+        const int nt = 2 * j + hf;
         floatx4 acc = z4();
-        if (nt <= w) acc = mm16<true, true, D>(acc, sK, LX, 16 * w, sK, LX, 16 * nt);
+        if (nt <= rb) acc = mm16<true, true, D>(acc, sK, LX, 16 * rb, sK, LX, 16 * nt);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = 16 * w + 4 * g + i, col = 16 * nt + r;
+            const int row = 16 * rb + 4 * g + i, col = 16 * nt + r;
             sM[row * LC + col] = col < row ? sb[row] * expf(sg[row] - sg[col]) * acc[i] : 0.f;
         }
     }
@@ -271,11 +275,12 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(Args a) {
     // T = (I + A)^-1 in 16 x 16 blocks.  Diagonal blocks: wave w inverts
     // (I + A_ww) by forward substitution, column n on lane n (lanes 0..15);
     // the blocks above the diagonal are zero.
-    for (int idx = lane; idx < 16 * 64; idx += 64) {
-        const int i = 16 * w + idx / 64, j = idx % 64;
-        if (j < 16 * w || j >= 16 * w + 16) sT[i * LC + j] = 0.f;
-    }
-    if (lane < 16) {
+    if (w < 4)
+        for (int idx = lane; idx < 16 * 64; idx += 64) {
+            const int i = 16 * w + idx / 64, j = idx % 64;
+            if (j < 16 * w || j >= 16 * w + 16) sT[i * LC + j] = 0.f;
+        }
+    if (w < 4 && lane < 16) {
         const int n = lane;
         const float *Aw = sM + 16 * w * LC + 16 * w;
         float x[16];
@@ -310,42 +315,45 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(Args a) {
         __syncthreads();
     }
     // T out; T' = T diag(b gam) into the A storage; diag(b) V in place
-    for (int idx = tid; idx < C * C; idx += NT) {
+    for (int idx = tid; idx < C * C; idx += GNT) {
         const int i = idx / C, j = idx % C;
         const float t = sT[i * LC + j];
         rec[R::TM + idx] = t;
         sM[i * LC + j] = t * sb[j] * sgam[j];
     }
-    for (int idx = tid; idx < C * D; idx += NT) {
+    for (int idx = tid; idx < C * D; idx += GNT) {
         const int tl = idx / D, ch = idx % D;
         sV[tl * LX + ch] *= sb[tl];
     }
     __syncthreads();
     // U~ = T diag(b) V
-    for (int nt = 0; nt < D / 16; ++nt) {
-        const floatx4 acc = mm16<true, false, C>(z4(), sT, LC, 16 * w, sV, LX, 16 * nt);
+    for (int j = 0; j < D / 32; ++j) {
+        const int nt = 2 * j + hf;
+        const floatx4 acc = mm16<true, false, C>(z4(), sT, LC, 16 * rb, sV, LX, 16 * nt);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rec[R::UT + (16 * w + 4 * g + i) * D + 16 * nt + r] = acc[i];
+        for (int i = 0; i < 4; ++i) rec[R::UT + (16 * rb + 4 * g + i) * D + 16 * nt + r] = acc[i];
     }
     __syncthreads();
     // W = T diag(b gam) K, out and into the V storage
-    for (int nt = 0; nt < D / 16; ++nt) {
-        const floatx4 acc = mm16<true, false, C>(z4(), sM, LC, 16 * w, sK, LX, 16 * nt);
+    for (int j = 0; j < D / 32; ++j) {
+        const int nt = 2 * j + hf;
+        const floatx4 acc = mm16<true, false, C>(z4(), sM, LC, 16 * rb, sK, LX, 16 * nt);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = 16 * w + 4 * g + i, col = 16 * nt + r;
+            const int row = 16 * rb + 4 * g + i, col = 16 * nt + r;
             rec[R::W + row * D + col] = acc[i];
             sV[row * LX + col] = acc[i];
         }
     }
     __syncthreads();
     // P = lower-inclusive (e^{g_i - g_j} q_i . k_j), out and into the A storage
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int j = 0; j < 2; ++j) {
+        const int nt = 2 * j + hf;
         floatx4 acc = z4();
-        if (nt <= w) acc = mm16<true, true, D>(acc, sQ, LX, 16 * w, sK, LX, 16 * nt);
+        if (nt <= rb) acc = mm16<true, true, D>(acc, sQ, LX, 16 * rb, sK, LX, 16 * nt);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = 16 * w + 4 * g + i, col = 16 * nt + r;
+            const int row = 16 * rb + 4 * g + i, col = 16 * nt + r;
             const float p = col <= row ? expf(sg[row] - sg[col]) * acc[i] : 0.f;
             sM[row * LC + col] = p;
             rec[R::P + row * C + col] = p;
@@ -353,24 +361,25 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(Args a) {
     }
     __syncthreads();
     // Q' = diag(gam) Q - P W;  D K = diag(e^{g_last - g}) K
-    for (int nt = 0; nt < D / 16; ++nt) {
-        const floatx4 acc = mm16<true, false, C>(z4(), sM, LC, 16 * w, sV, LX, 16 * nt);
+    for (int j = 0; j < D / 32; ++j) {
+        const int nt = 2 * j + hf;
+        const floatx4 acc = mm16<true, false, C>(z4(), sM, LC, 16 * rb, sV, LX, 16 * nt);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = 16 * w + 4 * g + i, col = 16 * nt + r;
+            const int row = 16 * rb + 4 * g + i, col = 16 * nt + r;
             const float qp = sgam[row] * sQ[row * LX + col] - acc[i];
             rec[R::QP + row * D + col] = qp;
             sQ[row * LX + col] = qp;
         }
     }
     const float glast = sg[63];
-    for (int idx = tid; idx < C * D; idx += NT) {
+    for (int idx = tid; idx < C * D; idx += GNT) {
         const int tl = idx / D, ch = idx % D;
         rec[R::DK + idx] = expf(glast - sg[tl]) * sK[tl * LX + ch];
     }
     __syncthreads();
     // key-major copies of W, D K and Q' (the chains read them as B operands)
-    for (int idx = tid; idx < C * D; idx += NT) {
+    for (int idx = tid; idx < C * D; idx += GNT) {
         const int key = idx / C, tl = idx % C;
         rec[R::WT + idx] = sV[tl * LX + key];
         rec[R::DKT + idx] = expf(glast - sg[tl]) * sK[tl * LX + key];
@@ -693,8 +702,6 @@ __global__ __launch_bounds__(NT) void bwd_dstate_kernel(Args a) {
 //   dg = gam d gam - dl d dl + rowsum(M) - colsum(M),  M = dP o P + dA o A,
 //        plus gC <dS', S> + sum(dl d dl) on the last token;
 //   d log a = the suffix sums of dg inside the chunk.
-constexpr int GW = 8, GNT = 64 * GW;  // waves and threads of bwd_grad_kernel
-
 template <int D>
 __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Args a) {
     typedef Rec<D> R;

@@ -190,7 +190,7 @@ template <class IO, int D> bool launch(int i, gdnb::Args a, int c0, int c1, hipS
     // chains: 8 equal slices of the work list (whole heads each), one per XCD
     const dim3 rows(8 * ((a.B * a.H + 7) / 8) * (D / 16));
     switch (i) {
-    case 0: bwd_prep_kernel<IO, D><<<chunks, NT, prep_lds<D>(), s>>>(a); break;
+    case 0: bwd_prep_kernel<IO, D><<<chunks, GNT, prep_lds<D>(), s>>>(a); break;
     case 1: bwd_state_kernel<D><<<rows, NT, 0, s>>>(a); break;
     case 2: bwd_out_kernel<IO, D><<<chunks, NT, 0, s>>>(a); break;
     case 3: bwd_dstate_kernel<D><<<rows, NT, 0, s>>>(a); break;
@@ -213,7 +213,7 @@ template <class IO, int D> gdn_status launch_timed(const gdn_bwd_params *p, hipE
     return GDN_OK;
 }
 
-// The call: the two chains run over ranges of about 128 chunks on the
+// The call: the two chains run over ranges of about 64 chunks on the
 // caller's stream; the output backward of a range follows its forward-chain
 // range, and the gradient kernel of a range its reverse-chain range, on the
 // library stream, so that both use the CUs the chains leave idle.
@@ -223,7 +223,7 @@ template <class IO, int D> gdn_status launch_all(const gdn_bwd_params *p, hipStr
     DeviceRes *res = nullptr;
     gdn_status st = device_res(res);
     if (st != GDN_OK) return st;
-    const int NC = a.NC, R = std::min(kMaxRanges, std::max(1, (NC + 127) / 128));
+    const int NC = a.NC, R = std::min(kMaxRanges, std::max(1, (NC + 63) / 64));
     int bound[kMaxRanges + 1];
     for (int r = 0; r <= R; ++r) bound[r] = (int)((long long)NC * r / R);
     hipStream_t side = res->side;

@@ -118,9 +118,9 @@ def test_bwd_full_size_causal():
 
 
 def test_bwd_ranges_match_single_pass():
-    """The call splits the chains into ranges (about 128 chunks each) on two
+    """The call splits the chains into ranges (about 64 chunks each) on two
     streams; the timed call runs every kernel once over all chunks on one
-    stream.  At the full size (512 chunks: 4 ranges), with dy and dS_T dense,
+    stream.  At the full size (512 chunks: 8 ranges), with dy and dS_T dense,
     every gradient of the two must be identical, bit for bit."""
     import ctypes
     import linear_attention_token_fwd_amd as gdn
