@@ -135,6 +135,44 @@ __device__ __forceinline__ floatx4 mm16(floatx4 acc, const float *A, int lda, in
 
 __device__ __forceinline__ floatx4 z4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
 
+// The A operand of mm16 held in registers, for a wave that multiplies the
+// same 16 rows by several column tiles: af[step][j] is what lane (r, g)
+// supplies to product j of 16-deep step `step`.
+template <bool KA, int K>
+__device__ __forceinline__ void load_a(float (&af)[K / 16][4], const float *A, int lda, int m0) {
+    const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int ks = 0; ks < K / 16; ++ks) {
+        if constexpr (KA) {
+            const floatx4 t = *reinterpret_cast<const floatx4 *>(A + (size_t)(m0 + r) * lda + 16 * ks + 4 * g);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) af[ks][j] = t[j];
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) af[ks][j] = A[(size_t)(16 * ks + 4 * g + j) * lda + m0 + r];
+        }
+    }
+}
+template <bool KB, int K>
+__device__ __forceinline__ floatx4 mm16a(floatx4 acc, const float (&af)[K / 16][4], const float *B, int ldb, int n0) {
+    const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int ks = 0; ks < K / 16; ++ks) {
+        float b[4];
+        if constexpr (KB) {
+            const floatx4 t = *reinterpret_cast<const floatx4 *>(B + (size_t)(n0 + r) * ldb + 16 * ks + 4 * g);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = t[j];
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = B[(size_t)(16 * ks + 4 * g + j) * ldb + n0 + r];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[ks][j], b[j], acc, 0, 0, 0);
+    }
+    return acc;
+}
+
 // 8 consecutive channels of one token row, loaded with one (bf16) or two
 // (fp32) 16-byte loads; a row outside the sequence reads as zeros.
 template <class IO> struct Row8;
@@ -737,15 +775,19 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Args a) {
         if (lane == 0) vred[w] = s;
     }
     // U = U~ - W S^T
+    {
+        float af[D / 16][4];
+        load_a<true, D>(af, rec + R::W, D, 16 * rb);
 #pragma unroll 1
     for (int j = 0; j < NTH; ++j) {
         const int nt = 2 * j + hf;
-        const floatx4 acc = mm16<true, true, D>(z4(), rec + R::W, D, 16 * rb, rec + R::SC, D, 16 * nt);
+        const floatx4 acc = mm16a<true, D>(z4(), af, rec + R::SC, D, 16 * nt);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * rb + 4 * g + i, col = 16 * nt + r;
             L1[row * LX + col] = rec[R::UT + row * D + col] - acc[i];
         }
+    }
     }
     __syncthreads();
 
@@ -760,11 +802,15 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Args a) {
         rbb[i] = vb_[row];
     }
     // dU = P^T dO + diag(dl) K dS'^T, d dl
+    {
+        float ak[D / 16][4], ap[C / 16][4];
+        load_a<true, D>(ak, rec + R::XK, D, 16 * rb);
+        load_a<false, C>(ap, rec + R::P, C, 16 * rb);
 #pragma unroll 1
     for (int j = 0; j < NTH; ++j) {
         const int nt = 2 * j + hf, col = 16 * nt + r;
-        const floatx4 kd = mm16<true, true, D>(z4(), rec + R::XK, D, 16 * rb, rec + R::DSN, D, 16 * nt);
-        const floatx4 pt = mm16<false, false, C>(z4(), rec + R::P, C, 16 * rb, rec + R::DO, D, 16 * nt);
+        const floatx4 kd = mm16a<true, D>(z4(), ak, rec + R::DSN, D, 16 * nt);
+        const floatx4 pt = mm16a<false, C>(z4(), ap, rec + R::DO, D, 16 * nt);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * rb + 4 * g + i;
@@ -772,11 +818,15 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Args a) {
             pdl[i] += kd[i] * L1[row * LX + col];
         }
     }
+    }
     // dq^ = diag(gam) dO S, d gam;  dk^ = diag(dl) U dS'
+    {
+        float ad[D / 16][4];
+        load_a<true, D>(ad, rec + R::DO, D, 16 * rb);
 #pragma unroll
     for (int j = 0; j < NTH; ++j) {
         const int nt = 2 * j + hf, col = 16 * nt + r;
-        const floatx4 dos = mm16<true, false, D>(z4(), rec + R::DO, D, 16 * rb, rec + R::SC, D, 16 * nt);
+        const floatx4 dos = mm16a<false, D>(z4(), ad, rec + R::SC, D, 16 * nt);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * rb + 4 * g + i;
@@ -784,6 +834,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Args a) {
             pgam[i] += dos[i] * rec[R::XQ + row * D + col];
         }
         __builtin_amdgcn_sched_barrier(0);
+    }
     }
 #pragma unroll
     for (int j = 0; j < NTH; ++j) {
@@ -817,11 +868,13 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Args a) {
         for (int i = 0; i < 4; ++i) L3[(16 * rb + 4 * g + i) * LX + 16 * nt + r] = -acc[i];
     }
     __syncthreads();
-    // dR_W = T^T dW (into the U storage)
+    // dR_W = T^T dW (into the U storage); T^T's rows are held for dR_U too
+    float at[C / 16][4];
+    load_a<false, C>(at, rec + R::TM, C, 16 * rb);
 #pragma unroll
     for (int j = 0; j < NTH; ++j) {
         const int nt = 2 * j + hf, col = 16 * nt + r;
-        const floatx4 acc = mm16<false, false, C>(z4(), rec + R::TM, C, 16 * rb, L3, LX, 16 * nt);
+        const floatx4 acc = mm16a<false, C>(z4(), at, L3, LX, 16 * nt);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * rb + 4 * g + i;
@@ -839,7 +892,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Args a) {
 #pragma unroll 1
     for (int j = 0; j < NTH; ++j) {
         const int nt = 2 * j + hf, col = 16 * nt + r;
-        const floatx4 acc = mm16<false, false, C>(z4(), rec + R::TM, C, 16 * rb, L2, LX, 16 * nt);
+        const floatx4 acc = mm16a<false, C>(z4(), at, L2, LX, 16 * nt);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * rb + 4 * g + i;
