@@ -1119,20 +1119,36 @@ __global__ __launch_bounds__(NT) void bwd_prologue_kernel(Args a) {
 // parts over batch rows and chunks, in a fixed order.
 template <int D>
 __global__ __launch_bounds__(NT) void bwd_reduce_kernel(Args a) {
-    const int idx = blockIdx.x * NT + threadIdx.x;
-    const int nconv = a.H * 3 * D * 4;
-    if (idx < nconv) {
-        const int h = idx / (3 * D * 4), rem = idx % (3 * D * 4), x = rem / (D * 4), e = rem % (D * 4);
-        float s = 0.f;
-        for (int bc = 0; bc < a.B * a.NC; ++bc) s += a.part_conv[((size_t)bc * a.H + h) * (3 * D * 4) + rem];
-        float *dst = x == 0 ? a.dconv_q : (x == 1 ? a.dconv_k : a.dconv_v);
-        dst[(size_t)h * D * 4 + e] = s;
-    } else if (idx < nconv + a.H * D && a.dnorm_w) {
-        const int j = idx - nconv;
-        const int h = j / D, ch = j % D;
-        float s = 0.f;
-        for (int bc = 0; bc < a.B * a.NC; ++bc) s += a.part_norm[((size_t)bc * a.H + h) * D + ch];
-        a.dnorm_w[j] = s;
+    // 64 outputs per workgroup; wave s sums slice s of the (batch row,
+    // chunk) parts, and the 4 slice sums are added in order
+    constexpr int SL = NT / 64;
+    __shared__ float sp[SL][64];
+    const int e = blockIdx.x * 64 + threadIdx.x % 64, sl = threadIdx.x / 64;
+    const int nconv = a.H * 3 * D * 4, ntot = nconv + a.H * D;
+    const int nbc = a.B * a.NC, per = (nbc + SL - 1) / SL, b0 = sl * per, b1 = min(nbc, b0 + per);
+    float s = 0.f;
+    if (e < nconv) {
+        const int h = e / (3 * D * 4), rem = e % (3 * D * 4);
+#pragma unroll 8
+        for (int bc = b0; bc < b1; ++bc) s += a.part_conv[((size_t)bc * a.H + h) * (3 * D * 4) + rem];
+    } else if (e < ntot) {
+        const int j = e - nconv, h = j / D, ch = j % D;
+#pragma unroll 8
+        for (int bc = b0; bc < b1; ++bc) s += a.part_norm[((size_t)bc * a.H + h) * D + ch];
+    }
+    sp[sl][threadIdx.x % 64] = s;
+    __syncthreads();
+    if (sl == 0 && e < ntot) {
+        float t = sp[0][threadIdx.x];
+#pragma unroll
+        for (int q = 1; q < SL; ++q) t += sp[q][threadIdx.x];
+        if (e < nconv) {
+            const int h = e / (3 * D * 4), rem = e % (3 * D * 4), x = rem / (D * 4), f = rem % (D * 4);
+            float *dst = x == 0 ? a.dconv_q : (x == 1 ? a.dconv_k : a.dconv_v);
+            dst[(size_t)h * D * 4 + f] = t;
+        } else if (a.dnorm_w) {
+            a.dnorm_w[e - nconv] = t;
+        }
     }
 }
 

@@ -196,7 +196,7 @@ template <class IO, int D> bool launch(int i, gdnb::Args a, int c0, int c1, hipS
     case 3: bwd_dstate_kernel<D><<<rows, NT, 0, s>>>(a); break;
     case 4: bwd_grad_kernel<D><<<chunks, GNT, grad_lds<D>(), s>>>(a); break;
     case 5: bwd_prologue_kernel<IO, D><<<chunks, NT, prologue_lds<D>(), s>>>(a); break;
-    default: bwd_reduce_kernel<D><<<dim3((a.H * D * 13 + NT - 1) / NT), NT, 0, s>>>(a); break;
+    default: bwd_reduce_kernel<D><<<dim3((a.H * D * 13 + 63) / 64), NT, 0, s>>>(a); break;
     }
     return hipGetLastError() == hipSuccess;
 }
