@@ -552,10 +552,13 @@ __global__ __launch_bounds__(NT) void bwd_out_kernel(Args a) {
     float *rec = record<D>(a, b, h, c);
     floatx4 o[NTL];
     float ss[4] = {0.f, 0.f, 0.f, 0.f};
+    float aq[D / 16][4], ap[C / 16][4];  // this wave's rows of Q' and P, used for every column tile
+    load_a<true, D>(aq, rec + R::QP, D, 16 * w);
+    load_a<true, C>(ap, rec + R::P, C, 16 * w);
 #pragma unroll
     for (int nt = 0; nt < NTL; ++nt) {
-        o[nt] = mm16<true, true, D>(z4(), rec + R::QP, D, 16 * w, rec + R::SC, D, 16 * nt);
-        o[nt] = mm16<true, false, C>(o[nt], rec + R::P, C, 16 * w, rec + R::UT, D, 16 * nt);
+        o[nt] = mm16a<true, D>(z4(), aq, rec + R::SC, D, 16 * nt);
+        o[nt] = mm16a<false, C>(o[nt], ap, rec + R::UT, D, 16 * nt);
 #pragma unroll
         for (int i = 0; i < 4; ++i) ss[i] += o[nt][i] * o[nt][i];
     }
