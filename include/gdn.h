@@ -300,8 +300,10 @@ gdn_status gdn_set_graph_cache_limit(int max_graphs);
 int gdn_graph_cache_count(void);
 
 /*
- * The layer's backward pass: the gradients of steps 1-5 (gdn_fwd with
- * reverse = 0) with respect to every input, for equal-length batch rows.
+ * The layer's backward pass: the gradients of steps 1-5 (gdn_fwd with the
+ * same reverse flag) with respect to every input, for equal-length batch
+ * rows.  The bidirectional variant's gradients are the sums of the calls with
+ * reverse = 0 and reverse = 1 (each with its own dS_T).
  * The pages train the converted GDN blocks (LinMorph project page,
  * "Abstract": progressive distillation and joint recovery), which needs
  * them; the Gated DeltaNet paper's chunkwise WY form (section 3.3) is the
@@ -332,7 +334,8 @@ int gdn_graph_cache_count(void);
  * bytes per (batch row, head, 64-token chunk), 3.6 GB at B = 1, T = 32760,
  * H = 12, D = 128.
  * Errors: as for gdn_fwd.  GDN_ERR_INVALID_ARG for a NULL required pointer,
- * bad sizes, eps < 0 or not finite, or an output that overlaps an input,
+ * bad sizes, eps < 0 or not finite, reverse not 0 or 1, or an output that
+ * overlaps an input,
  * another output or the workspace; GDN_ERR_ALIGNMENT for a tensor not
  * 16-byte aligned or a workspace not 256-byte aligned; GDN_ERR_UNSUPPORTED
  * for other D.
@@ -354,6 +357,7 @@ typedef struct gdn_bwd_params {
     float *dconv_q, *dconv_k, *dconv_v;
     float *dnorm_w;           /* or NULL */
     float *dS0;               /* or NULL */
+    int reverse;              /* 0 or 1, as for gdn_fwd */
     void *workspace;
     size_t workspace_bytes;
 } gdn_bwd_params;

@@ -82,7 +82,7 @@ class GdnBwdParams(ctypes.Structure):
         ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p), ("dgate", ctypes.c_void_p),
         ("dlog_a", ctypes.c_void_p), ("dbeta", ctypes.c_void_p),
         ("dconv_q", ctypes.c_void_p), ("dconv_k", ctypes.c_void_p), ("dconv_v", ctypes.c_void_p),
-        ("dnorm_w", ctypes.c_void_p), ("dS0", ctypes.c_void_p),
+        ("dnorm_w", ctypes.c_void_p), ("dS0", ctypes.c_void_p), ("reverse", ctypes.c_int),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
     ]
 
@@ -490,7 +490,7 @@ def gdn_bwd_launch_names() -> list:
 
 
 def bwd_params(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, dy, dS_T, grads: dict,
-               workspace, eps_l2=1e-6, eps_norm=1e-6) -> GdnBwdParams:
+               workspace, eps_l2=1e-6, eps_norm=1e-6, reverse=False) -> GdnBwdParams:
     """Fill the backward params struct from torch tensors; grads maps the
     names of BWD_GRADS to output tensors (norm_w and S0 may be None)."""
     import torch
@@ -508,6 +508,7 @@ def bwd_params(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, d
     p.dlog_a, p.dbeta = _ptr(grads.get("log_a")), _ptr(grads.get("beta"))
     p.dconv_q, p.dconv_k, p.dconv_v = (_ptr(grads.get(n)) for n in ("conv_q", "conv_k", "conv_v"))
     p.dnorm_w, p.dS0 = _ptr(grads.get("norm_w")), _ptr(grads.get("S0"))
+    p.reverse = 1 if reverse else 0
     p.workspace = _ptr(workspace)
     p.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return p
@@ -515,9 +516,9 @@ def bwd_params(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, d
 
 def gdn_bwd(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, dy, dS_T=None,
             eps_l2=1e-6, eps_norm=1e-6, want_norm_w=True, want_S0=True, out=None, workspace=None,
-            stream=None):
-    """Gradients of the layer forward (reverse = 0) given dy (and dS_T, the
-    final state's gradient, or None).  Returns a dict keyed by BWD_GRADS:
+            stream=None, reverse=False):
+    """Gradients of the layer forward (with the same reverse flag) given dy
+    (and dS_T, the final state's gradient, or None).  Returns a dict keyed by BWD_GRADS:
     dq, dk, dv, dgate in the I/O dtype, the rest float32 (norm_w / S0: None
     unless wanted).  out: an optional dict of preallocated output tensors
     under the same keys."""
@@ -544,7 +545,7 @@ def gdn_bwd(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, dy, 
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     p = bwd_params(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, dy, dS_T, g,
-                   workspace, eps_l2, eps_norm)
+                   workspace, eps_l2, eps_norm, reverse)
     s = (stream if stream is not None else torch.cuda.current_stream(dev)).cuda_stream
     st = lib.gdn_bwd(ctypes.byref(p), ctypes.c_void_p(s))
     if st != GDN_OK:

@@ -83,7 +83,11 @@ struct Args {
     float *part_conv;                                  // [B NC H][3][D][4]
     float *part_norm;                                  // [B NC H][D]
     float *sink;                                       // [B, H, D, D]: the chains' stores past either end
+    int reverse;                                       // 1: the layer on the time-reversed sequence
 };
+
+// Input / output row of scan position t (the records are in scan order).
+__device__ __forceinline__ int src_t(const Args &a, int t) { return a.reverse ? a.T - 1 - t : t; }
 
 __device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f(float x) { return x; }
@@ -220,8 +224,9 @@ __global__ __launch_bounds__(GNT) void bwd_prep_kernel(Args a) {
     if (tid < 64) {
         const int t = t0 + tid;
         const bool valid = t < a.T;
-        float la = valid ? a.log_a[((size_t)b * a.T + t) * a.H + h] : 0.f;
-        const float be = valid ? a.beta[((size_t)b * a.T + t) * a.H + h] : 0.f;
+        const int ts = valid ? src_t(a, t) : 0;
+        float la = valid ? a.log_a[((size_t)b * a.T + ts) * a.H + h] : 0.f;
+        const float be = valid ? a.beta[((size_t)b * a.T + ts) * a.H + h] : 0.f;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
             const float y = __shfl_up(la, o, 64);
@@ -248,7 +253,7 @@ __global__ __launch_bounds__(GNT) void bwd_prep_kernel(Args a) {
         for (int rr = 0; rr < ROWS; ++rr) {
             const int sp = s0 - 3 + rr;
             const bool ok = sp >= 0 && sp < a.T;
-            const size_t off = ((((size_t)b * a.T + (ok ? sp : 0)) * a.H + h) * D) + 8 * cg;
+            const size_t off = ((((size_t)b * a.T + (ok ? src_t(a, sp) : 0)) * a.H + h) * D) + 8 * cg;
 #pragma unroll
             for (int x = 0; x < 3; ++x) raw[x][rr].load(src[x] + off, ok);
         }
@@ -577,7 +582,7 @@ __global__ __launch_bounds__(NT) void bwd_out_kernel(Args a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = t0 + 16 * w + 4 * g + i;
-            const size_t off = (((size_t)b * a.T + t) * a.H + h) * D + col;
+            const size_t off = (((size_t)b * a.T + (t < a.T ? src_t(a, t) : 0)) * a.H + h) * D + col;
             gt[nt][i] = t < a.T ? to_f(gate[off]) : 0.f;
             dyv[nt][i] = t < a.T ? to_f(dy[off]) : 0.f;
             const float n = o[nt][i] * rr[i], sgt = silu(gt[nt][i]);
@@ -762,7 +767,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Args a) {
         const int t = t0 + tid;
         const float gg = rec[R::G + tid];
         vg[tid] = gg;
-        vb_[tid] = t < a.T ? a.beta[((size_t)b * a.T + t) * a.H + h] : 0.f;
+        vb_[tid] = t < a.T ? a.beta[((size_t)b * a.T + src_t(a, t)) * a.H + h] : 0.f;
         vgam[tid] = expf(gg);
         vdl[tid] = expf(rec[R::G + 63] - gg);
     }
@@ -981,8 +986,9 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Args a) {
         }
         const int tt = t0 + t;
         if (tt < a.T) {
-            a.dlog_a[((size_t)b * a.T + tt) * a.H + h] = dg;
-            a.dbeta[((size_t)b * a.T + tt) * a.H + h] = vdb[t] + vdb[C + t];
+            const int ts = src_t(a, tt);
+            a.dlog_a[((size_t)b * a.T + ts) * a.H + h] = dg;
+            a.dbeta[((size_t)b * a.T + ts) * a.H + h] = vdb[t] + vdb[C + t];
         }
     }
 }
@@ -1020,7 +1026,7 @@ __global__ __launch_bounds__(NT) void bwd_prologue_kernel(Args a) {
         for (int rr = 0; rr < ROWS; ++rr) {
             const int sp = t0 + r0 - 3 + rr;
             const bool ok = sp >= 0 && sp < a.T;
-            raw[rr].load(src[x] + ((((size_t)b * a.T + (ok ? sp : 0)) * a.H + h) * D) + 8 * cg, ok);
+            raw[rr].load(src[x] + ((((size_t)b * a.T + (ok ? src_t(a, sp) : 0)) * a.H + h) * D) + 8 * cg, ok);
         }
         floatx4 dxh[RUN][2];
 #pragma unroll
@@ -1102,7 +1108,7 @@ __global__ __launch_bounds__(NT) void bwd_prologue_kernel(Args a) {
                     for (int j = 0; j < 4; ++j) acc = fmaf(wt[i][j], sZ[(tl + 3 - j) * LZ + 8 * cg + i], acc);
                     dx[i] = acc;
                 }
-                IO *o = dst[x] + (((size_t)b * a.T + t) * a.H + h) * D + 8 * cg;
+                IO *o = dst[x] + (((size_t)b * a.T + src_t(a, t)) * a.H + h) * D + 8 * cg;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) o[i] = (IO)dx[i];
             }

@@ -70,6 +70,7 @@ gdn_status validate(const gdn_bwd_params *p) {
         return GDN_ERR_INVALID_ARG;
     if (!(p->eps_l2 >= 0.f) || !(p->eps_norm >= 0.f) || !std::isfinite(p->eps_l2) || !std::isfinite(p->eps_norm))
         return GDN_ERR_INVALID_ARG;
+    if (p->reverse != 0 && p->reverse != 1) return GDN_ERR_INVALID_ARG;
     const size_t B = p->B, T = p->T, H = p->H, D = p->Dk, es = elem_size(p->io_dtype);
     const size_t tok = B * T * H * D * es, gates = B * T * H * 4, conv = H * D * 16, st = B * H * D * D * 4;
     const Span in[] = {span(p->q, tok),      span(p->k, tok),      span(p->v, tok),
@@ -178,6 +179,7 @@ template <class IO, int D> gdnb::Args make_args(const gdn_bwd_params *p) {
     a.part_conv = reinterpret_cast<float *>(ws + L.part_conv);
     a.part_norm = reinterpret_cast<float *>(ws + L.part_norm);
     a.sink = reinterpret_cast<float *>(ws + L.sink);
+    a.reverse = p->reverse;
     return a;
 }
 

@@ -364,6 +364,7 @@ BWD_CASES = [
     ("dgate overlaps dq", lambda p: setattr(p, "dgate", p.dq + 512), gdn.GDN_ERR_INVALID_ARG),
     ("dS0 overlaps the workspace", lambda p: setattr(p, "dS0", p.workspace + 4096), gdn.GDN_ERR_INVALID_ARG),
     ("dnorm_w overlaps dS_T", lambda p: setattr(p, "dnorm_w", p.dS_T), gdn.GDN_ERR_INVALID_ARG),
+    ("reverse = 2", lambda p: setattr(p, "reverse", 2), gdn.GDN_ERR_INVALID_ARG),
 ]
 
 

@@ -23,7 +23,7 @@ def _workload(dtype, D):
     return gdn_inputs.Workload(91, f"{dtype} d{D}", 1, 1000, 2, D, dtype)
 
 
-def run_bwd(inp, grads, dtype):
+def run_bwd(inp, grads, dtype, reverse=False):
     """The library's gradients as float64 numpy arrays (keyed like the oracle)."""
     import linear_attention_token_fwd_amd as gdn
     d = gdn.to_device(inp, dtype=torch_dtype(dtype))
@@ -37,7 +37,7 @@ def run_bwd(inp, grads, dtype):
     out["norm_w"] = torch.full((H, D), float("nan"), device="cuda")
     out["S0"] = torch.full((B, H, D, D), float("nan"), device="cuda")
     g = gdn.gdn_bwd(d["q"], d["k"], d["v"], d["log_a"], d["beta"], d["gate"], d["conv_q"], d["conv_k"],
-                    d["conv_v"], d["norm_w"], d["S0"], dy, dS, out=out)
+                    d["conv_v"], d["norm_w"], d["S0"], dy, dS, out=out, reverse=reverse)
     torch.cuda.synchronize()
     return {n: g[n].double().cpu().numpy() for n in obwd.NAMES}
 
@@ -93,6 +93,32 @@ def test_bwd_matches_oracle(case):
     got = run_bwd(inp, grads, dtype)
     ref = oracle_grads(inp, grads)
     compare(got, ref, dtype, f"{dtype} D={D} T={T}")
+
+
+TOKEN_WISE = ("q", "k", "v", "gate", "log_a", "beta")
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
+def test_bwd_reverse_is_the_flipped_layer(dtype, D):
+    """reverse = 1 is the layer on the time-reversed sequence with its output
+    in input order, so its gradients are the oracle's on the flipped inputs
+    and dy, flipped back along time (the weights' and S0's as they are)."""
+    w = _workload(dtype, D)
+    T, H, B = 64 * 2 + 22, 2, 2
+    inp = gdn_inputs.generate(w, T=T, H=H, B=B, seed=900 + D)
+    rng = np.random.default_rng(901)
+    inp["S0"] = (0.1 * rng.standard_normal((B, H, D, D))).astype(np.float32)
+    inp["norm_w"] = (1 + 0.3 * rng.standard_normal((H, D))).astype(np.float32)
+    grads = gdn_inputs.generate_grads(w, seed=902, T=T, H=H, B=B)
+    say(f"case: bwd reverse {dtype} D={D} T={T}")
+    got = run_bwd(inp, grads, dtype, reverse=True)
+
+    def flip(a):
+        return np.ascontiguousarray(a[:, ::-1])
+    finp = {n: (flip(a) if n in TOKEN_WISE else a) for n, a in inp.items()}
+    ref = oracle_grads(finp, dict(dy=flip(grads["dy"]), dS_T=grads["dS_T"]))
+    ref = {n: (flip(a) if n in TOKEN_WISE else a) for n, a in ref.items()}
+    compare(got, ref, dtype, f"reverse {dtype} D={D} T={T}")
 
 
 def test_bwd_full_size_causal():
