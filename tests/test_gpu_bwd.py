@@ -188,3 +188,44 @@ def test_bwd_ranges_match_single_pass():
         a, b = o1[name], o2[name]
         assert torch.isfinite(a).all(), name
         assert torch.equal(a, b), name
+
+
+def test_bwd_graph_replays():
+    """The backward captured in a HIP graph (torch.cuda.graph on a side
+    stream; the call's fork onto the library stream and the join back are
+    captured with it) at 131 chunks (3 ranges).  Every replay, with eager
+    backward calls and synchronisations in between, must equal the eager
+    call bit for bit."""
+    import linear_attention_token_fwd_amd as gdn
+    w = _workload("bf16", 64)
+    T, H, B, D = 64 * 130 + 7, 2, 1, 64
+    inp = gdn_inputs.generate(w, T=T, H=H, B=B, seed=71)
+    grads = gdn_inputs.generate_grads(w, seed=72, T=T, H=H, B=B)
+    d = gdn.to_device(inp, dtype=torch.bfloat16)
+    dy = torch.from_numpy(grads["dy"]).to(torch.bfloat16).cuda()
+    dS = torch.from_numpy(grads["dS_T"]).cuda()
+    args = (d["q"], d["k"], d["v"], d["log_a"], d["beta"], d["gate"], d["conv_q"], d["conv_k"], d["conv_v"],
+            d["norm_w"], d["S0"], dy, dS)
+    ws = torch.empty(gdn.gdn_bwd_workspace_bytes(B, T, H, D), dtype=torch.uint8, device="cuda")
+    eager = {n: t.clone() for n, t in gdn.gdn_bwd(*args, workspace=ws).items() if t is not None}
+    torch.cuda.synchronize()
+    out = {n: torch.empty_like(t) for n, t in eager.items()}
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        gdn.gdn_bwd(*args, out=out, workspace=ws, stream=side)  # warm-up on the side stream
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=side):
+        gdn.gdn_bwd(*args, out=out, workspace=ws, stream=side)
+    for rep in range(3):
+        for t in out.values():
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        same = all(torch.equal(out[n], eager[n]) for n in eager)
+        say(f"  replay {rep}: every gradient equal {same}")
+        assert same, f"replay {rep} differs from the eager call"
+        gdn.gdn_bwd(*args, workspace=ws)  # eager work between the replays
+        torch.cuda.synchronize()
