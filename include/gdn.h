@@ -335,10 +335,10 @@ int gdn_graph_cache_count(void);
  * H = 12, D = 128.
  * Errors: as for gdn_fwd.  GDN_ERR_INVALID_ARG for a NULL required pointer,
  * bad sizes, eps < 0 or not finite, reverse not 0 or 1, or an output that
- * overlaps an input,
- * another output or the workspace; GDN_ERR_ALIGNMENT for a tensor not
- * 16-byte aligned or a workspace not 256-byte aligned; GDN_ERR_UNSUPPORTED
- * for other D.
+ * overlaps an input, another output or the workspace; GDN_ERR_ALIGNMENT for
+ * q, k, v or a conv weight not 16-byte aligned, another tensor not aligned
+ * to its element size, or a workspace not 256-byte aligned;
+ * GDN_ERR_UNSUPPORTED for other D.
  */
 typedef struct gdn_bwd_params {
     int B, T, H, Dk, Dv;
@@ -370,6 +370,18 @@ gdn_status gdn_bwd(const gdn_bwd_params *p, struct ihipStream_t *stream);
  * around kernel i (n_events >= 2 * gdn_bwd_launch_count()). */
 gdn_status gdn_bwd_timed(const gdn_bwd_params *p, struct ihipEvent_t **events, int n_events,
                          struct ihipStream_t *stream);
+/*
+ * The backward of gdn_fwd_varlen: p->B sequences packed along the token axis
+ * (cu_seqlens: a HOST array of p->B + 1 ints, as for gdn_fwd_varlen; p->T is
+ * ignored).  q, k, v, gate, dy and dq, dk, dv, dgate are [total, H, D];
+ * log_a, beta, dlog_a, dbeta [total, H]; S0, dS_T, dS0 [p->B, H, D, D]; the
+ * weight gradients are sums over all sequences.  The table is copied into the
+ * workspace (gdn_bwd_varlen_workspace_bytes(p, cu_seqlens) bytes; 0 for an
+ * invalid table) on `stream`.  Each sequence's per-token and per-sequence
+ * gradients equal gdn_bwd on that sequence alone.
+ */
+size_t gdn_bwd_varlen_workspace_bytes(const gdn_bwd_params *p, const int *cu_seqlens);
+gdn_status gdn_bwd_varlen(const gdn_bwd_params *p, const int *cu_seqlens, struct ihipStream_t *stream);
 /* The number of kernels of a gdn_bwd call, and the name of kernel i
  * (NULL out of range). */
 int gdn_bwd_launch_count(void);

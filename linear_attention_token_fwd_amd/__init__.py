@@ -22,7 +22,7 @@ EXPORTS = ("gdn_fwd", "gdn_fwd_bidir", "gdn_fwd_workspace_bytes", "gdn_fwd_bidir
            "gdn_in_proj", "gdn_out_proj", "gdn_mixer_workspace_bytes", "gdn_mixer_fwd", "gdn_mixer_fwd_timed",
            "gdn_fwd_varlen", "gdn_fwd_varlen_workspace_bytes", "gdn_set_graph_cache_limit",
            "gdn_graph_cache_count", "gdn_bwd", "gdn_bwd_workspace_bytes", "gdn_bwd_timed",
-           "gdn_bwd_launch_count", "gdn_bwd_launch_name")
+           "gdn_bwd_launch_count", "gdn_bwd_launch_name", "gdn_bwd_varlen", "gdn_bwd_varlen_workspace_bytes")
 
 
 class GdnFwdParams(ctypes.Structure):
@@ -144,6 +144,10 @@ def load(path: str | None = None):
     lib.gdn_bwd.restype = ctypes.c_int
     lib.gdn_bwd_timed.argtypes = [PB, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_void_p]
     lib.gdn_bwd_timed.restype = ctypes.c_int
+    lib.gdn_bwd_varlen.argtypes = [PB, IP, ctypes.c_void_p]
+    lib.gdn_bwd_varlen.restype = ctypes.c_int
+    lib.gdn_bwd_varlen_workspace_bytes.argtypes = [PB, IP]
+    lib.gdn_bwd_varlen_workspace_bytes.restype = ctypes.c_size_t
     lib.gdn_bwd_launch_count.argtypes = []
     lib.gdn_bwd_launch_count.restype = ctypes.c_int
     lib.gdn_bwd_launch_name.argtypes = [ctypes.c_int]
@@ -551,3 +555,44 @@ def gdn_bwd(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, dy, 
     if st != GDN_OK:
         raise GdnError(st, "gdn_bwd")
     return g
+
+
+def gdn_bwd_varlen(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, dy, dS_T, cu_seqlens,
+                   eps_l2=1e-6, eps_norm=1e-6, want_norm_w=True, want_S0=True, reverse=False, stream=None):
+    """The backward of gdn_fwd_varlen: q, k, v, gate, dy [total, H, D] (a
+    leading batch dimension of 1 is accepted), log_a, beta [total, H];
+    cu_seqlens a host sequence of B + 1 ints; S0, dS_T [B, H, D, D] or None.
+    Returns a dict keyed by BWD_GRADS (per-token gradients shaped like their
+    inputs)."""
+    import torch
+    lib = load()
+    tok = tuple(q.shape[-3:])
+    total, H, D = tok
+    cu = (ctypes.c_int * len(cu_seqlens))(*[int(x) for x in cu_seqlens])
+    B = len(cu_seqlens) - 1
+    dev, io, f32 = q.device, q.dtype, torch.float32
+    g = {n: torch.empty(q.shape, dtype=io, device=dev) for n in ("q", "k", "v", "gate")}
+    g["log_a"] = torch.empty(log_a.shape, dtype=f32, device=dev)
+    g["beta"] = torch.empty(beta.shape, dtype=f32, device=dev)
+    for n in ("conv_q", "conv_k", "conv_v"):
+        g[n] = torch.empty((H * D, 4), dtype=f32, device=dev)
+    g["norm_w"] = torch.empty((H, D), dtype=f32, device=dev) if want_norm_w else None
+    g["S0"] = torch.empty((B, H, D, D), dtype=f32, device=dev) if want_S0 else None
+    p = GdnBwdParams()
+    p.B, p.T, p.H, p.Dk, p.Dv = B, 0, H, D, D
+    p.io_dtype = GDN_BF16 if io == torch.bfloat16 else GDN_F32
+    need = lib.gdn_bwd_varlen_workspace_bytes(ctypes.byref(p), cu)
+    if need == 0:
+        raise GdnError(GDN_ERR_INVALID_ARG, "gdn_bwd_varlen_workspace_bytes")
+    workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    def as4(t):
+        return t.reshape(1, total, H, D)
+    p = bwd_params(as4(q), as4(k), as4(v), log_a, beta, as4(gate), conv_q, conv_k, conv_v, norm_w, S0, as4(dy),
+                   dS_T, g, workspace, eps_l2, eps_norm, reverse)
+    p.B, p.T = B, 0
+    s = (stream if stream is not None else torch.cuda.current_stream(dev)).cuda_stream
+    st = lib.gdn_bwd_varlen(ctypes.byref(p), cu, ctypes.c_void_p(s))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_bwd_varlen")
+    return g
+

@@ -84,10 +84,23 @@ struct Args {
     float *part_norm;                                  // [B NC H][D]
     float *sink;                                       // [B, H, D, D]: the chains' stores past either end
     int reverse;                                       // 1: the layer on the time-reversed sequence
+    const int *cu;                                     // variable lengths: B + 1 row offsets, or null
 };
 
-// Input / output row of scan position t (the records are in scan order).
-__device__ __forceinline__ int src_t(const Args &a, int t) { return a.reverse ? a.T - 1 - t : t; }
+// Sequence b: its first token row and its length.  Without a table, row b of
+// a [B, T] batch; with one, rows cu[b] .. cu[b+1] - 1 of the packed tokens
+// (T is then the longest length, and every sequence has NC chunk records).
+struct Seq {
+    long long off;
+    int len;
+};
+__device__ __forceinline__ Seq seq_of(const Args &a, int b) {
+    if (a.cu) return Seq{a.cu[b], a.cu[b + 1] - a.cu[b]};
+    return Seq{(long long)b * a.T, a.T};
+}
+// Input / output row (within the sequence) of scan position t; the records
+// are in scan order.
+__device__ __forceinline__ int src_t(const Args &a, const Seq &q, int t) { return a.reverse ? q.len - 1 - t : t; }
 
 __device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f(float x) { return x; }
@@ -220,13 +233,14 @@ __global__ __launch_bounds__(GNT) void bwd_prep_kernel(Args a) {
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, r = lane % 16, g = lane / 16;
     const int rb = w % 4, hf = w / 4;
     float *rec = record<D>(a, b, h, c);
+    const Seq sq = seq_of(a, b);
 
     if (tid < 64) {
         const int t = t0 + tid;
-        const bool valid = t < a.T;
-        const int ts = valid ? src_t(a, t) : 0;
-        float la = valid ? a.log_a[((size_t)b * a.T + ts) * a.H + h] : 0.f;
-        const float be = valid ? a.beta[((size_t)b * a.T + ts) * a.H + h] : 0.f;
+        const bool valid = t < sq.len;
+        const int ts = valid ? src_t(a, sq, t) : 0;
+        float la = valid ? a.log_a[((size_t)sq.off + ts) * a.H + h] : 0.f;
+        const float be = valid ? a.beta[((size_t)sq.off + ts) * a.H + h] : 0.f;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
             const float y = __shfl_up(la, o, 64);
@@ -252,8 +266,8 @@ __global__ __launch_bounds__(GNT) void bwd_prep_kernel(Args a) {
 #pragma unroll
         for (int rr = 0; rr < ROWS; ++rr) {
             const int sp = s0 - 3 + rr;
-            const bool ok = sp >= 0 && sp < a.T;
-            const size_t off = ((((size_t)b * a.T + (ok ? src_t(a, sp) : 0)) * a.H + h) * D) + 8 * cg;
+            const bool ok = sp >= 0 && sp < sq.len;
+            const size_t off = ((((size_t)sq.off + (ok ? src_t(a, sq, sp) : 0)) * a.H + h) * D) + 8 * cg;
 #pragma unroll
             for (int x = 0; x < 3; ++x) raw[x][rr].load(src[x] + off, ok);
         }
@@ -267,7 +281,7 @@ __global__ __launch_bounds__(GNT) void bwd_prep_kernel(Args a) {
             }
 #pragma unroll
             for (int rt = 0; rt < RUN; ++rt) {
-                const bool valid = s0 + rt < a.T;
+                const bool valid = s0 + rt < sq.len;
                 float out[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
@@ -555,6 +569,7 @@ __global__ __launch_bounds__(NT) void bwd_out_kernel(Args a) {
     const int c = a.c0 + blockIdx.x, h = blockIdx.y, b = blockIdx.z, t0 = c * C;
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, r = lane % 16, g = lane / 16;
     float *rec = record<D>(a, b, h, c);
+    const Seq sq = seq_of(a, b);
     floatx4 o[NTL];
     float ss[4] = {0.f, 0.f, 0.f, 0.f};
     float aq[D / 16][4], ap[C / 16][4];  // this wave's rows of Q' and P, used for every column tile
@@ -582,13 +597,13 @@ __global__ __launch_bounds__(NT) void bwd_out_kernel(Args a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = t0 + 16 * w + 4 * g + i;
-            const size_t off = (((size_t)b * a.T + (t < a.T ? src_t(a, t) : 0)) * a.H + h) * D + col;
-            gt[nt][i] = t < a.T ? to_f(gate[off]) : 0.f;
-            dyv[nt][i] = t < a.T ? to_f(dy[off]) : 0.f;
+            const size_t off = (((size_t)sq.off + (t < sq.len ? src_t(a, sq, t) : 0)) * a.H + h) * D + col;
+            gt[nt][i] = t < sq.len ? to_f(gate[off]) : 0.f;
+            dyv[nt][i] = t < sq.len ? to_f(dy[off]) : 0.f;
             const float n = o[nt][i] * rr[i], sgt = silu(gt[nt][i]);
             dot[i] += dyv[nt][i] * wn * sgt * n;
             cs[nt] += dyv[nt][i] * n * sgt;
-            if (t < a.T) dgate[off] = (IO)(dyv[nt][i] * n * wn * dsilu(gt[nt][i]));
+            if (t < sq.len) dgate[off] = (IO)(dyv[nt][i] * n * wn * dsilu(gt[nt][i]));
         }
     }
 #pragma unroll
@@ -762,12 +777,13 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Args a) {
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, r = lane % 16, g = lane / 16;
     const int rb = w % 4, hf = w / 4;
     const float *rec = record<D>(a, b, h, c);
+    const Seq sq = seq_of(a, b);
 
     if (tid < 64) {
         const int t = t0 + tid;
         const float gg = rec[R::G + tid];
         vg[tid] = gg;
-        vb_[tid] = t < a.T ? a.beta[((size_t)b * a.T + src_t(a, t)) * a.H + h] : 0.f;
+        vb_[tid] = t < sq.len ? a.beta[((size_t)sq.off + src_t(a, sq, t)) * a.H + h] : 0.f;
         vgam[tid] = expf(gg);
         vdl[tid] = expf(rec[R::G + 63] - gg);
     }
@@ -985,10 +1001,10 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Args a) {
             if (t + o < 64) dg += y;
         }
         const int tt = t0 + t;
-        if (tt < a.T) {
-            const int ts = src_t(a, tt);
-            a.dlog_a[((size_t)b * a.T + ts) * a.H + h] = dg;
-            a.dbeta[((size_t)b * a.T + ts) * a.H + h] = vdb[t] + vdb[C + t];
+        if (tt < sq.len) {
+            const size_t row = (size_t)sq.off + src_t(a, sq, tt);
+            a.dlog_a[row * a.H + h] = dg;
+            a.dbeta[row * a.H + h] = vdb[t] + vdb[C + t];
         }
     }
 }
@@ -1015,6 +1031,7 @@ __global__ __launch_bounds__(NT) void bwd_prologue_kernel(Args a) {
     float *sW = sZ + (C + 3) * LZ;      // conv-weight partial sums [RUNS][D * 4]
     const int c = a.c0 + blockIdx.x, h = blockIdx.y, b = blockIdx.z, t0 = c * C;
     const int tid = threadIdx.x, cg = tid % G, run = tid / G, r0 = run * RUN;
+    const Seq sq = seq_of(a, b);
     const IO *src[3] = {static_cast<const IO *>(a.q), static_cast<const IO *>(a.k), static_cast<const IO *>(a.v)};
     IO *dst[3] = {static_cast<IO *>(a.dq), static_cast<IO *>(a.dk), static_cast<IO *>(a.dv)};
     const float *cw[3] = {a.conv_q, a.conv_k, a.conv_v};
@@ -1025,14 +1042,14 @@ __global__ __launch_bounds__(NT) void bwd_prologue_kernel(Args a) {
 #pragma unroll
         for (int rr = 0; rr < ROWS; ++rr) {
             const int sp = t0 + r0 - 3 + rr;
-            const bool ok = sp >= 0 && sp < a.T;
-            raw[rr].load(src[x] + ((((size_t)b * a.T + (ok ? src_t(a, sp) : 0)) * a.H + h) * D) + 8 * cg, ok);
+            const bool ok = sp >= 0 && sp < sq.len;
+            raw[rr].load(src[x] + ((((size_t)sq.off + (ok ? src_t(a, sq, sp) : 0)) * a.H + h) * D) + 8 * cg, ok);
         }
         floatx4 dxh[RUN][2];
 #pragma unroll
         for (int rt = 0; rt < RUN; ++rt) {
             const int t = t0 + r0 + rt;
-            const bool ok = t < a.T && r0 + rt < C + 3;
+            const bool ok = t < sq.len && r0 + rt < C + 3;
             const float *pr = ok ? record<D>(a, b, h, t / C) + dxo[x] + (t % C) * D + 8 * cg : nullptr;
             dxh[rt][0] = ok ? *reinterpret_cast<const floatx4 *>(pr) : z4();
             dxh[rt][1] = ok ? *reinterpret_cast<const floatx4 *>(pr + 4) : z4();
@@ -1074,7 +1091,7 @@ __global__ __launch_bounds__(NT) void bwd_prologue_kernel(Args a) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) dv[i] = rho * (dv[i] - sv[i] * rho * dot);
             }
-            const bool valid = t < a.T;
+            const bool valid = t < sq.len;
             float dz[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) dz[i] = valid ? dv[i] * dsilu(z[i]) : 0.f;
@@ -1099,7 +1116,7 @@ __global__ __launch_bounds__(NT) void bwd_prologue_kernel(Args a) {
 #pragma unroll
         for (int rt = 0; rt < RUN; ++rt) {
             const int tl = r0 + rt, t = t0 + tl;
-            if (tl < C && t < a.T) {
+            if (tl < C && t < sq.len) {
                 float dx[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
@@ -1108,7 +1125,7 @@ __global__ __launch_bounds__(NT) void bwd_prologue_kernel(Args a) {
                     for (int j = 0; j < 4; ++j) acc = fmaf(wt[i][j], sZ[(tl + 3 - j) * LZ + 8 * cg + i], acc);
                     dx[i] = acc;
                 }
-                IO *o = dst[x] + (((size_t)b * a.T + src_t(a, t)) * a.H + h) * D + 8 * cg;
+                IO *o = dst[x] + (((size_t)sq.off + src_t(a, sq, t)) * a.H + h) * D + 8 * cg;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) o[i] = (IO)dx[i];
             }

@@ -28,17 +28,19 @@ size_t elem_size(gdn_dtype d) { return d == GDN_BF16 ? 2 : 4; }
 size_t rec_floats(int D) { return D == 128 ? gdnb::Rec<128>::SIZE : gdnb::Rec<64>::SIZE; }
 
 struct Layout {
-    size_t rec, part_conv, part_norm, sink, total;
+    size_t rec, part_conv, part_norm, sink, seq, total;
 };
 
-Layout layout(const gdn_bwd_params *p) {
+// varlen: room for the device copy of a sequence table of B + 1 ints
+Layout layout(const gdn_bwd_params *p, bool varlen = false) {
     const size_t B = p->B, H = p->H, D = p->Dk, NC = n_chunks(p->T);
     Layout L;
     L.rec = 0;
     L.part_conv = round_up(B * H * NC * rec_floats(p->Dk) * sizeof(float));
     L.part_norm = L.part_conv + round_up(B * NC * H * 12 * D * sizeof(float));
     L.sink = L.part_norm + round_up(B * NC * H * D * sizeof(float));
-    L.total = L.sink + round_up(B * H * D * D * sizeof(float));
+    L.seq = L.sink + round_up(B * H * D * D * sizeof(float));
+    L.total = L.seq + (varlen ? round_up((B + 1) * sizeof(int)) : 0);
     return L;
 }
 
@@ -60,7 +62,8 @@ Span span(const void *ptr, size_t bytes) { return Span{(uintptr_t)ptr, (uintptr_
 bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
 bool aligned(const void *ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
 
-gdn_status validate(const gdn_bwd_params *p) {
+// rows: token rows of the per-token tensors (B T, or the packed total)
+gdn_status validate(const gdn_bwd_params *p, size_t rows, bool varlen) {
     if (!sizes_ok(p)) return GDN_ERR_INVALID_ARG;
     if (p->Dk != p->Dv) return GDN_ERR_UNSUPPORTED;
     if (p->Dk != 64 && p->Dk != 128) return GDN_ERR_UNSUPPORTED;
@@ -71,8 +74,8 @@ gdn_status validate(const gdn_bwd_params *p) {
     if (!(p->eps_l2 >= 0.f) || !(p->eps_norm >= 0.f) || !std::isfinite(p->eps_l2) || !std::isfinite(p->eps_norm))
         return GDN_ERR_INVALID_ARG;
     if (p->reverse != 0 && p->reverse != 1) return GDN_ERR_INVALID_ARG;
-    const size_t B = p->B, T = p->T, H = p->H, D = p->Dk, es = elem_size(p->io_dtype);
-    const size_t tok = B * T * H * D * es, gates = B * T * H * 4, conv = H * D * 16, st = B * H * D * D * 4;
+    const size_t B = p->B, H = p->H, D = p->Dk, es = elem_size(p->io_dtype);
+    const size_t tok = rows * H * D * es, gates = rows * H * 4, conv = H * D * 16, st = B * H * D * D * 4;
     const Span in[] = {span(p->q, tok),      span(p->k, tok),      span(p->v, tok),
                        span(p->gate, tok),   span(p->dy, tok),     span(p->log_a, gates),
                        span(p->beta, gates), span(p->conv_q, conv), span(p->conv_k, conv),
@@ -90,15 +93,19 @@ gdn_status validate(const gdn_bwd_params *p) {
         for (int j = i + 1; j < nout; ++j)
             if (overlap(out[i], out[j])) return GDN_ERR_INVALID_ARG;
     }
-    // 16-byte vector loads of q, k, v and the conv weights; every tensor is
-    // held to the same rule
-    const void *all[] = {p->q,      p->k,      p->v,       p->gate,    p->dy,      p->dq,    p->dk,
-                         p->dv,     p->dgate,  p->log_a,   p->beta,    p->conv_q,  p->conv_k, p->conv_v,
-                         p->norm_w, p->S0,     p->dS_T,    p->dlog_a,  p->dbeta,   p->dconv_q, p->dconv_k,
-                         p->dconv_v, p->dnorm_w, p->dS0};
-    for (const void *ptr : all)
-        if (ptr && !aligned(ptr, 16)) return GDN_ERR_ALIGNMENT;
-    if (!p->workspace || p->workspace_bytes < layout(p).total) return GDN_ERR_WORKSPACE;
+    // q, k, v and the conv weights are read with 16-byte loads; every other
+    // tensor is accessed element by element
+    const void *vec[] = {p->q, p->k, p->v, p->conv_q, p->conv_k, p->conv_v};
+    for (const void *ptr : vec)
+        if (!aligned(ptr, 16)) return GDN_ERR_ALIGNMENT;
+    const void *io[] = {p->gate, p->dy, p->dq, p->dk, p->dv, p->dgate};
+    for (const void *ptr : io)
+        if (!aligned(ptr, es)) return GDN_ERR_ALIGNMENT;
+    const void *f32[] = {p->log_a, p->beta, p->norm_w, p->S0, p->dS_T, p->dlog_a, p->dbeta, p->dconv_q,
+                         p->dconv_k, p->dconv_v, p->dnorm_w, p->dS0};
+    for (const void *ptr : f32)
+        if (ptr && !aligned(ptr, 4)) return GDN_ERR_ALIGNMENT;
+    if (!p->workspace || p->workspace_bytes < layout(p, varlen).total) return GDN_ERR_WORKSPACE;
     if (!aligned(p->workspace, kAlign)) return GDN_ERR_ALIGNMENT;
     return GDN_OK;
 }
@@ -161,8 +168,8 @@ gdn_status device_res(DeviceRes *&out) {
     return GDN_OK;
 }
 
-template <class IO, int D> gdnb::Args make_args(const gdn_bwd_params *p) {
-    const Layout L = layout(p);
+template <class IO, int D> gdnb::Args make_args(const gdn_bwd_params *p, const int *cu_dev) {
+    const Layout L = layout(p, cu_dev != nullptr);
     gdnb::Args a;
     a.B = p->B, a.T = p->T, a.H = p->H, a.NC = n_chunks(p->T), a.c0 = 0, a.c1 = a.NC;
     a.q = p->q, a.k = p->k, a.v = p->v, a.gate = p->gate, a.dy = p->dy;
@@ -180,6 +187,7 @@ template <class IO, int D> gdnb::Args make_args(const gdn_bwd_params *p) {
     a.part_norm = reinterpret_cast<float *>(ws + L.part_norm);
     a.sink = reinterpret_cast<float *>(ws + L.sink);
     a.reverse = p->reverse;
+    a.cu = cu_dev;
     return a;
 }
 
@@ -206,7 +214,7 @@ template <class IO, int D> bool launch(int i, gdnb::Args a, int c0, int c1, hipS
 // Timed: every kernel once over all chunks on the caller's stream, events
 // around each.
 template <class IO, int D> gdn_status launch_timed(const gdn_bwd_params *p, hipEvent_t *ev, hipStream_t s) {
-    const gdnb::Args a = make_args<IO, D>(p);
+    const gdnb::Args a = make_args<IO, D>(p, nullptr);
     for (int i = 0; i < kLaunches; ++i) {
         (void)hipEventRecord(ev[2 * i], s);
         if (!launch<IO, D>(i, a, 0, a.NC, s)) return GDN_ERR_HIP;
@@ -219,8 +227,8 @@ template <class IO, int D> gdn_status launch_timed(const gdn_bwd_params *p, hipE
 // caller's stream; the output backward of a range follows its forward-chain
 // range, and the gradient kernel of a range its reverse-chain range, on the
 // library stream, so that both use the CUs the chains leave idle.
-template <class IO, int D> gdn_status launch_all(const gdn_bwd_params *p, hipStream_t s) {
-    const gdnb::Args a = make_args<IO, D>(p);
+template <class IO, int D> gdn_status launch_all(const gdn_bwd_params *p, const int *cu_dev, hipStream_t s) {
+    const gdnb::Args a = make_args<IO, D>(p, cu_dev);
     std::lock_guard<std::mutex> lock(g_mutex);
     DeviceRes *res = nullptr;
     gdn_status st = device_res(res);
@@ -254,7 +262,8 @@ template <class IO, int D> gdn_status launch_all(const gdn_bwd_params *p, hipStr
 }
 
 gdn_status call(const gdn_bwd_params *p, hipEvent_t *ev, int n_ev, hipStream_t s) {
-    gdn_status st = validate(p);
+    if (!sizes_ok(p)) return GDN_ERR_INVALID_ARG;
+    gdn_status st = validate(p, (size_t)p->B * p->T, false);
     if (st != GDN_OK) return st;
     if (ev && n_ev < 2 * kLaunches) return GDN_ERR_INVALID_ARG;
     st = set_attributes();
@@ -265,8 +274,42 @@ gdn_status call(const gdn_bwd_params *p, hipEvent_t *ev, int n_ev, hipStream_t s
         return p->Dk == 128 ? launch_timed<float, 128>(p, ev, s) : launch_timed<float, 64>(p, ev, s);
     }
     if (p->io_dtype == GDN_BF16)
-        return p->Dk == 128 ? launch_all<bf16, 128>(p, s) : launch_all<bf16, 64>(p, s);
-    return p->Dk == 128 ? launch_all<float, 128>(p, s) : launch_all<float, 64>(p, s);
+        return p->Dk == 128 ? launch_all<bf16, 128>(p, nullptr, s) : launch_all<bf16, 64>(p, nullptr, s);
+    return p->Dk == 128 ? launch_all<float, 128>(p, nullptr, s) : launch_all<float, 64>(p, nullptr, s);
+}
+
+// Variable-length batch: the params with T = the longest length, or an error
+// for a malformed table (cu[0] = 0, every length >= 1).
+gdn_status varlen_params(const gdn_bwd_params *p, const int *cu, gdn_bwd_params &q) {
+    if (!p || !cu || p->B < 1) return GDN_ERR_INVALID_ARG;
+    if (cu[0] != 0) return GDN_ERR_INVALID_ARG;
+    int longest = 0;
+    for (int b = 0; b < p->B; ++b) {
+        const long long len = (long long)cu[b + 1] - cu[b];
+        if (len < 1) return GDN_ERR_INVALID_ARG;
+        if (len > longest) longest = (int)len;
+    }
+    q = *p;
+    q.T = longest;
+    return GDN_OK;
+}
+
+gdn_status varlen_call(const gdn_bwd_params *p, const int *cu, hipStream_t s) {
+    gdn_bwd_params q;
+    gdn_status st = varlen_params(p, cu, q);
+    if (st != GDN_OK) return st;
+    if (!sizes_ok(&q)) return GDN_ERR_INVALID_ARG;
+    st = validate(&q, (size_t)cu[q.B], true);
+    if (st != GDN_OK) return st;
+    st = set_attributes();
+    if (st != GDN_OK) return st;
+    int *cu_dev = reinterpret_cast<int *>(static_cast<char *>(q.workspace) + layout(&q, true).seq);
+    // the table goes to the workspace first, on the caller's stream
+    if (hipMemcpyAsync(cu_dev, cu, sizeof(int) * (q.B + 1), hipMemcpyHostToDevice, s) != hipSuccess)
+        return GDN_ERR_HIP;
+    if (q.io_dtype == GDN_BF16)
+        return q.Dk == 128 ? launch_all<bf16, 128>(&q, cu_dev, s) : launch_all<bf16, 64>(&q, cu_dev, s);
+    return q.Dk == 128 ? launch_all<float, 128>(&q, cu_dev, s) : launch_all<float, 64>(&q, cu_dev, s);
 }
 
 }  // namespace
@@ -291,6 +334,21 @@ gdn_status gdn_bwd_timed(const gdn_bwd_params *p, struct ihipEvent_t **events, i
     if (!events) return GDN_ERR_INVALID_ARG;
     try {
         return call(p, events, n_events, stream);
+    } catch (...) {
+        return GDN_ERR_HIP;
+    }
+}
+
+size_t gdn_bwd_varlen_workspace_bytes(const gdn_bwd_params *p, const int *cu_seqlens) {
+    gdn_bwd_params q;
+    if (varlen_params(p, cu_seqlens, q) != GDN_OK) return 0;
+    if (!sizes_ok(&q) || q.Dk != q.Dv || (q.Dk != 64 && q.Dk != 128)) return 0;
+    return layout(&q, true).total;
+}
+
+gdn_status gdn_bwd_varlen(const gdn_bwd_params *p, const int *cu_seqlens, struct ihipStream_t *stream) {
+    try {
+        return varlen_call(p, cu_seqlens, stream);
     } catch (...) {
         return GDN_ERR_HIP;
     }

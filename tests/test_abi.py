@@ -34,7 +34,7 @@ def lib():
 
 def test_every_declared_function_is_exported_and_bound(lib):
     decl = declared_functions()
-    assert len(decl) == 22, decl
+    assert len(decl) == 24, decl
     assert set(decl) == set(gdn.EXPORTS)
     for name in decl:
         fn = getattr(lib, name)  # AttributeError if the library does not export it
@@ -357,6 +357,8 @@ BWD_CASES = [
     ("D = 32", lambda p: (setattr(p, "Dk", 32), setattr(p, "Dv", 32)), gdn.GDN_ERR_UNSUPPORTED),
     ("dq misaligned", lambda p: setattr(p, "dq", p.dq + 1), gdn.GDN_ERR_ALIGNMENT),
     ("dlog_a misaligned", lambda p: setattr(p, "dlog_a", p.dlog_a + 2), gdn.GDN_ERR_ALIGNMENT),
+    ("k not 16-byte aligned", lambda p: setattr(p, "k", p.k + 8), gdn.GDN_ERR_ALIGNMENT),
+    ("conv_v not 16-byte aligned", lambda p: setattr(p, "conv_v", p.conv_v + 4), gdn.GDN_ERR_ALIGNMENT),
     ("workspace NULL", lambda p: setattr(p, "workspace", None), gdn.GDN_ERR_WORKSPACE),
     ("workspace too small", lambda p: setattr(p, "workspace_bytes", p.workspace_bytes - 1), gdn.GDN_ERR_WORKSPACE),
     ("workspace misaligned", lambda p: setattr(p, "workspace", p.workspace + 16), gdn.GDN_ERR_ALIGNMENT),
@@ -389,3 +391,19 @@ def test_bwd_timed_needs_events(lib):
     events = (ctypes.c_void_p * (n - 1))()
     assert lib.gdn_bwd_timed(ctypes.byref(p), events, n - 1, None) == gdn.GDN_ERR_INVALID_ARG
     assert lib.gdn_bwd_timed(ctypes.byref(p), None, n, None) == gdn.GDN_ERR_INVALID_ARG
+
+
+def test_bwd_varlen_table_checks(lib):
+    p = fake_bwd(lib, B=3, T=150)
+    p.T = 0  # ignored by the varlen calls
+    IP = ctypes.c_int * 4
+    assert lib.gdn_bwd_varlen_workspace_bytes(ctypes.byref(p), IP(0, 100, 250, 300)) > 0
+    assert lib.gdn_bwd_varlen_workspace_bytes(ctypes.byref(p), IP(1, 100, 250, 300)) == 0   # not from 0
+    assert lib.gdn_bwd_varlen_workspace_bytes(ctypes.byref(p), IP(0, 100, 100, 300)) == 0   # an empty sequence
+    # the longest sequence (150 tokens) sets the chunk records: the same bytes as a B = 3, T = 150 batch,
+    # plus the table
+    q = fake_bwd(lib, B=3, T=150)
+    assert lib.gdn_bwd_varlen_workspace_bytes(ctypes.byref(p), IP(0, 100, 250, 300)) == q.workspace_bytes + 256
+    assert lib.gdn_bwd_varlen(ctypes.byref(p), IP(0, 100, 90, 300), None) == gdn.GDN_ERR_INVALID_ARG
+    assert lib.gdn_bwd_varlen(ctypes.byref(p), None, None) == gdn.GDN_ERR_INVALID_ARG
+

@@ -229,3 +229,46 @@ def test_bwd_graph_replays():
         assert same, f"replay {rep} differs from the eager call"
         gdn.gdn_bwd(*args, workspace=ws)  # eager work between the replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_bwd_varlen_equals_each_sequence(reverse):
+    """Three sequences of different lengths packed along the token axis: each
+    one's per-token gradients and dS0 equal gdn_bwd on that sequence alone,
+    bit for bit (its chunks past the end are identity steps of both chains);
+    the weight gradients equal the sums of the single calls' to rounding."""
+    import linear_attention_token_fwd_amd as gdn
+    w = _workload("bf16", 64)
+    lens = (150, 64 * 3 + 5, 70)
+    H, D = 2, 64
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(int)
+    total = int(cu[-1])
+    inp = gdn_inputs.generate(w, T=total, H=H, B=1, seed=81)
+    rng = np.random.default_rng(82)
+    S0 = (0.1 * rng.standard_normal((len(lens), H, D, D))).astype(np.float32)
+    grads = gdn_inputs.generate_grads(w, seed=83, T=total, H=H, B=1)
+    dS_T = rng.standard_normal((len(lens), H, D, D)).astype(np.float32)
+    say(f"case: bwd varlen lengths {lens} reverse={reverse}")
+    d = gdn.to_device(inp, dtype=torch.bfloat16)
+    dy = torch.from_numpy(grads["dy"]).to(torch.bfloat16).cuda()
+    S0_d, dS_d = torch.from_numpy(S0).cuda(), torch.from_numpy(dS_T).cuda()
+    tok = ("q", "k", "v", "gate", "log_a", "beta")
+    got = gdn.gdn_bwd_varlen(d["q"][0], d["k"][0], d["v"][0], d["log_a"][0], d["beta"][0], d["gate"][0],
+                             d["conv_q"], d["conv_k"], d["conv_v"], d["norm_w"], S0_d, dy[0], dS_d, list(cu),
+                             reverse=reverse)
+    torch.cuda.synchronize()
+    wsum = {n: 0.0 for n in ("conv_q", "conv_k", "conv_v", "norm_w")}
+    for b, n_b in enumerate(lens):
+        sl = slice(int(cu[b]), int(cu[b + 1]))
+        one = gdn.gdn_bwd(*[d[n][:, sl].contiguous() if n in tok else d[n]
+                            for n in ("q", "k", "v", "log_a", "beta", "gate", "conv_q", "conv_k", "conv_v", "norm_w")],
+                          S0_d[b:b + 1].contiguous(), dy[:, sl].contiguous(), dS_d[b:b + 1].contiguous(),
+                          reverse=reverse)
+        torch.cuda.synchronize()
+        for n in tok:
+            assert torch.equal(got[n][sl], one[n][0]), (b, n)
+        assert torch.equal(got["S0"][b], one["S0"][0]), (b, "S0")
+        for n in wsum:
+            wsum[n] = wsum[n] + one[n].double()
+    for n, ref in wsum.items():
+        assert rel_l2(got[n].double().cpu().numpy(), ref.cpu().numpy()) < 1e-5, n
