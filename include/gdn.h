@@ -306,8 +306,8 @@ int gdn_graph_cache_count(void);
  * reverse = 0 and reverse = 1 (each with its own dS_T).
  * The pages train the converted GDN blocks (LinMorph project page,
  * "Abstract": progressive distillation and joint recovery), which needs
- * them; the Gated DeltaNet paper's chunkwise WY form (section 3.3) is the
- * forward they differentiate.  Given dy = dL/dy and dS_T = dL/dS_T, one call
+ * them; they are taken through the forward's chunked form (the delta rule
+ * unrolled inside 64-token chunks).  Given dy = dL/dy and dS_T = dL/dS_T, one call
  * writes
  *   dq, dk, dv, dgate   [B, T, H, D]   io_dtype
  *   dlog_a, dbeta       [B, T, H]      float32

@@ -3,9 +3,11 @@
 // delta rule in 64-token chunks, the gated RMS normalisation) with respect to
 // every input.
 //
-// The backward follows the forward's chunking (Gated DeltaNet paper, section
-// 3.3, the chunkwise WY form; the LinMorph project page trains the converted
-// GDN blocks, which needs these gradients).  For chunk c with entry state S
+// The backward follows the forward's chunking: the chunked WY form, which
+// comes from unrolling the gated delta rule inside a 64-token chunk.  (The
+// LinMorph project page, "Abstract", trains the converted GDN blocks by
+// progressive distillation and joint recovery, which needs these gradients.)
+// For chunk c with entry state S
 // (value rows, key columns), tokens as rows, g the cumulative log decay
 // inside the chunk, gam = e^g, gC = e^{g_last}, dl = e^{g_last - g}:
 //   A = strictly lower (b_i e^{g_i - g_j} k_i . k_j),  T = (I + A)^-1
