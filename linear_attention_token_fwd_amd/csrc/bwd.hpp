@@ -845,23 +845,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Args a) {
         }
     }
     }
-    // dq^ = diag(gam) dO S, d gam;  dk^ = diag(dl) U dS'
-    {
-        float ad[D / 16][4];
-        load_a<true, D>(ad, rec + R::DO, D, 16 * rb);
-#pragma unroll
-    for (int j = 0; j < NTH; ++j) {
-        const int nt = 2 * j + hf, col = 16 * nt + r;
-        const floatx4 dos = mm16a<false, D>(z4(), ad, rec + R::SC, D, 16 * nt);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 16 * rb + 4 * g + i;
-            dQ[j][i] = rgam[i] * dos[i];
-            pgam[i] += dos[i] * rec[R::XQ + row * D + col];
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    }
+    // dk^ = diag(dl) U dS'
 #pragma unroll
     for (int j = 0; j < NTH; ++j) {
         const int nt = 2 * j + hf;
@@ -885,13 +869,38 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Args a) {
         }
     }
     __syncthreads();
-    // dW = -dU S
-#pragma unroll 1
-    for (int j = 0; j < NTH; ++j) {
-        const int nt = 2 * j + hf;
-        const floatx4 acc = mm16<true, false, D>(z4(), L2, LX, 16 * rb, rec + R::SC, D, 16 * nt);
+    // dq^ = diag(gam) dO S, d gam, and dW = -dU S: each 16-key column block
+    // of S is loaded once, for both products
+    {
+        float ad[D / 16][4];
+        load_a<true, D>(ad, rec + R::DO, D, 16 * rb);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) L3[(16 * rb + 4 * g + i) * LX + 16 * nt + r] = -acc[i];
+        for (int j = 0; j < NTH; ++j) {
+            const int nt = 2 * j + hf, col = 16 * nt + r;
+            float sb[D / 16][4];
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) sb[ks][jj] = rec[R::SC + (16 * ks + 4 * g + jj) * D + col];
+            floatx4 dos = z4(), dw = z4();
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks) {
+                const floatx4 u = *reinterpret_cast<const floatx4 *>(L2 + (16 * rb + r) * LX + 16 * ks + 4 * g);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    dos = __builtin_amdgcn_mfma_f32_16x16x4f32(ad[ks][jj], sb[ks][jj], dos, 0, 0, 0);
+                    dw = __builtin_amdgcn_mfma_f32_16x16x4f32(u[jj], sb[ks][jj], dw, 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * rb + 4 * g + i;
+                dQ[j][i] = rgam[i] * dos[i];
+                pgam[i] += dos[i] * rec[R::XQ + row * D + col];
+                L3[row * LX + col] = -dw[i];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
     __syncthreads();
     // dR_W = T^T dW (into the U storage); T^T's rows are held for dR_U too
