@@ -961,15 +961,35 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Args a) {
         }
     }
     __syncthreads();
-    // dk^ += F K + F^T K + G^T Q;  dq^ += G K
+    // dk^ += F K + F^T K + G^T Q;  dq^ += G K.  The A operands (rows and
+    // columns 16 rb .. of F and G) are held for all column tiles, and each
+    // column block of K serves three products.
     float *dxq = const_cast<float *>(rec) + R::DXQ, *dxk = const_cast<float *>(rec) + R::DXK;
+    float fa[C / 16][4], fta[C / 16][4], ga[C / 16][4], gta[C / 16][4];
+    load_a<true, C>(fa, Lb, LC, 16 * rb);
+    load_a<false, C>(fta, Lb, LC, 16 * rb);
+    load_a<true, C>(ga, La, LC, 16 * rb);
+    load_a<false, C>(gta, La, LC, 16 * rb);
 #pragma unroll
     for (int j = 0; j < NTH; ++j) {
         const int nt = 2 * j + hf;
-        dK[j] = mm16<true, false, C>(dK[j], Lb, LC, 16 * rb, rec + R::XK, D, 16 * nt);
-        dK[j] = mm16<false, false, C>(dK[j], Lb, LC, 16 * rb, rec + R::XK, D, 16 * nt);
-        dK[j] = mm16<false, false, C>(dK[j], La, LC, 16 * rb, rec + R::XQ, D, 16 * nt);
-        dQ[j] = mm16<true, false, C>(dQ[j], La, LC, 16 * rb, rec + R::XK, D, 16 * nt);
+        float kb[C / 16][4], qb[C / 16][4];
+#pragma unroll
+        for (int ks = 0; ks < C / 16; ++ks)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                kb[ks][jj] = rec[R::XK + (16 * ks + 4 * g + jj) * D + 16 * nt + r];
+                qb[ks][jj] = rec[R::XQ + (16 * ks + 4 * g + jj) * D + 16 * nt + r];
+            }
+#pragma unroll
+        for (int ks = 0; ks < C / 16; ++ks)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                dK[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[ks][jj], kb[ks][jj], dK[j], 0, 0, 0);
+                dK[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fta[ks][jj], kb[ks][jj], dK[j], 0, 0, 0);
+                dK[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(gta[ks][jj], qb[ks][jj], dK[j], 0, 0, 0);
+                dQ[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ga[ks][jj], kb[ks][jj], dQ[j], 0, 0, 0);
+            }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * rb + 4 * g + i, col = 16 * nt + r;
