@@ -255,7 +255,7 @@ __global__ __launch_bounds__(GNT) void bwd_prep_kernel(Args a) {
         if (tid == 63) rec[R::G + 64] = expf(la);
     }
     // short conv + SiLU of q, k, v (tap j multiplies x_{t-3+j}; zeros before the
-    // start).  Thread: 8 channels (one 16- or 32-byte load per row) of RUN
+    // start), L2 norms of q and k.  Thread: 8 channels (one 16- or 32-byte load per row) of RUN
     // consecutive tokens; its RUN + 3 input rows of q, k and v are all loaded
     // before any arithmetic.
     {
@@ -292,24 +292,20 @@ __global__ __launch_bounds__(GNT) void bwd_prep_kernel(Args a) {
                     for (int j = 0; j < 4; ++j) z = fmaf(wt[i][j], raw[x][rt + j].get(i), z);
                     out[i] = valid ? silu(z) : 0.f;
                 }
+                if (x < 2) {
+                    // L2 norm of the token's row: its D channels sit on the G
+                    // neighbouring lanes of this run
+                    float ss = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) ss += out[i] * out[i];
+                    const float rho = 1.0f / sqrtf(gdn::group_sum<G>(ss) + a.eps_l2);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) out[i] *= rho;
+                }
                 float *row = dst[x] + (run * RUN + rt) * LX + 8 * cg;
                 *reinterpret_cast<float4 *>(row) = make_float4(out[0], out[1], out[2], out[3]);
                 *reinterpret_cast<float4 *>(row + 4) = make_float4(out[4], out[5], out[6], out[7]);
             }
-        }
-    }
-    __syncthreads();
-    // L2 norms of the q and k rows: wave w takes rows 8w..8w+7
-    for (int rr = 0; rr < 8; ++rr) {
-        const int row = 8 * w + rr;
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-            float *p = (x == 0 ? sQ : sK) + row * LX;
-            float ss = 0.f;
-            for (int ch = lane; ch < D; ch += 64) ss += p[ch] * p[ch];
-            ss = wave_sum(ss);
-            const float rho = 1.0f / sqrtf(ss + a.eps_l2);
-            for (int ch = lane; ch < D; ch += 64) p[ch] *= rho;
         }
     }
     __syncthreads();
