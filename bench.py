@@ -489,12 +489,12 @@ def bwd_flops_per_chunk_head(D: int) -> dict:
       dstate: dS (D K)^T, X W, dO^T Q'
       grad : W S^T, K dS'^T, dO S, U dS', dW = dU S (64 D^2 each); P^T dO,
              T^T dW, T^T dU, F K, F^T K, G^T Q, G K (64 64 D each);
-             dO U^T, dR_W W^T, dR_U U~^T, K K^T (tri)."""
+             dO U^T, dR_W W^T, dR_U U~^T (tri; E o K K^T comes from prep)."""
     t, tri = 64 * 64 * D, 64 * 64 * D * 10 / 16
     sq = 64 * D * D
     return {"bwd_prep_kernel": 2 * (2 * tri + 3 * t), "bwd_state_kernel": 2 * (2 * sq),
             "bwd_out_kernel": 2 * (sq + t), "bwd_dstate_kernel": 2 * (3 * sq),
-            "bwd_grad_kernel": 2 * (5 * sq + 7 * t + 4 * tri)}
+            "bwd_grad_kernel": 2 * (5 * sq + 7 * t + 3 * tri)}
 
 
 def run_bwd(args) -> int:

@@ -330,8 +330,8 @@ int gdn_graph_cache_count(void);
  * enqueueing is serialised by a lock.  gdn_bwd_timed runs the 7 kernels once
  * each, in order, on `stream` alone (same results, bit for bit).
  * The workspace (gdn_bwd_workspace_bytes(), 256-byte aligned) holds the
- * recomputed chunk quantities in fp32: about (909 D + 8320 + 2 D^2) * 4
- * bytes per (batch row, head, 64-token chunk), 3.6 GB at B = 1, T = 32760,
+ * recomputed chunk quantities in fp32: about (909 D + 12416 + 2 D^2) * 4
+ * bytes per (batch row, head, 64-token chunk), 4.0 GB at B = 1, T = 32760,
  * H = 12, D = 128.
  * Errors: as for gdn_fwd.  GDN_ERR_INVALID_ARG for a NULL required pointer,
  * bad sizes, eps < 0 or not finite, reverse not 0 or 1, or an output that

@@ -64,7 +64,8 @@ template <int D> struct Rec {
     static constexpr int WT = DSN + D * D;   // W, key-major [D][64]
     static constexpr int DKT = WT + 64 * D;  // D K, key-major
     static constexpr int QPT = DKT + 64 * D; // Q', key-major
-    static constexpr int SIZE = QPT + 64 * D;
+    static constexpr int EKK = QPT + 64 * D; // strictly lower e^{g_i - g_j} k_i . k_j [64][64]
+    static constexpr int SIZE = EKK + 64 * 64;
 };
 
 struct Args {
@@ -323,7 +324,9 @@ __global__ __launch_bounds__(GNT) void bwd_prep_kernel(Args a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * rb + 4 * g + i, col = 16 * nt + r;
-            sM[row * LC + col] = col < row ? sb[row] * expf(sg[row] - sg[col]) * acc[i] : 0.f;
+            const float ekk = col < row ? expf(sg[row] - sg[col]) * acc[i] : 0.f;
+            sM[row * LC + col] = sb[row] * ekk;
+            rec[R::EKK + row * C + col] = ekk;
         }
     }
     __syncthreads();
@@ -757,6 +760,7 @@ __global__ __launch_bounds__(NT) void bwd_dstate_kernel(Args a) {
 //   dW = -dU S,  dR_W = T^T dW,  dR_U = T^T dU,  dv^ = diag(b) dR_U
 //   db = gam rowdot(dR_W, K) + rowdot(dR_U, V) + rowsum(dA o E o K K^T)
 //   dA = -(dR_W W^T + dR_U U~^T) (strictly lower),  F = diag(b) (E o dA)
+//   (E o K K^T, strictly lower, comes from the prep's record)
 //   dP = dO U^T (lower-inclusive),  G = E o dP     (E_ij = e^{g_i - g_j})
 //   dg = gam d gam - dl d dl + rowsum(M) - colsum(M),  M = dP o P + dA o A,
 //        plus gC <dS', S> + sum(dl d dl) on the last token;
@@ -937,21 +941,21 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Args a) {
 #pragma unroll 1
     for (int j = 0; j < 2; ++j) {
         const int nt = 2 * j + hf;
-        floatx4 acc = z4(), kk = z4();
+        floatx4 acc = z4();
         if (nt <= rb) {
             acc = mm16<true, true, D>(acc, L1, LX, 16 * rb, rec + R::W, D, 16 * nt);
             acc = mm16<true, true, D>(acc, L3, LX, 16 * rb, rec + R::UT, D, 16 * nt);
-            kk = mm16<true, true, D>(kk, rec + R::XK, D, 16 * rb, rec + R::XK, D, 16 * nt);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * rb + 4 * g + i, col = 16 * nt + r;
             float f = 0.f;
             if (col < row) {
-                const float e = expf(vg[row] - vg[col]), da = -acc[i];
+                // E o K K^T from the prep (so A = diag(b) of it)
+                const float e = expf(vg[row] - vg[col]), da = -acc[i], ekk = rec[R::EKK + row * C + col];
                 f = rbb[i] * e * da;
-                pdb[i] += e * da * kk[i];
-                Lc[row * LC + col] += f * kk[i];
+                pdb[i] += da * ekk;
+                Lc[row * LC + col] += rbb[i] * da * ekk;
             }
             Lb[row * LC + col] = f;
         }
