@@ -12,7 +12,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgdn.so")
+# the in-tree build, or another build of the same sources named by GDN_LIBRARY
+# (the host-sanitizer test loads an instrumented build this way)
+LIB_PATH = os.environ.get("GDN_LIBRARY") or os.path.join(_HERE, "libgdn.so")
 
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_ALIGNMENT, GDN_ERR_WORKSPACE, GDN_ERR_HIP = range(6)
 GDN_F32, GDN_BF16 = 0, 1
@@ -198,6 +200,44 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _stream(stream, device):
+    """The stream a call runs on: the given one, else the device's current stream."""
+    import torch
+    return stream if stream is not None else torch.cuda.current_stream(device)
+
+
+def _alloc(shape, dtype, device, stream):
+    """A tensor allocated on the pool of the stream the call runs on, so that
+    the caching allocator reuses its memory only after that stream's work."""
+    import torch
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
+def _workspace(nbytes, device, stream):
+    """The call's own workspace when the caller passes none: allocated on the
+    call's stream (see _alloc), so freeing it on return is safe even when the
+    call runs on a stream other than the current one."""
+    import torch
+    return _alloc((max(int(nbytes), 1),), torch.uint8, device, stream)
+
+
+def _checked_table(cu_seqlens, total: int):
+    """The sequence offsets as ints, after the checks the C layer cannot make
+    (it does not see tensor sizes): offsets from 0, every length >= 1, and the
+    last offset equal to the packed row count of the tensors."""
+    vals = [int(x) for x in cu_seqlens]
+    if len(vals) < 2:
+        raise ValueError("cu_seqlens needs at least two offsets (one sequence)")
+    if vals[0] != 0:
+        raise ValueError("cu_seqlens must start at 0")
+    if any(b <= a for a, b in zip(vals, vals[1:])):
+        raise ValueError("cu_seqlens must increase: every sequence holds at least one token")
+    if vals[-1] != int(total):
+        raise ValueError(f"cu_seqlens ends at {vals[-1]}, but the tensors hold {total} token rows")
+    return vals
+
+
 def make_params(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, out, S_T,
                 workspace, eps_l2=1e-6, eps_norm=1e-6, reverse=False) -> GdnFwdParams:
     """Fill the params struct from torch tensors (no checks beyond shape
@@ -219,37 +259,47 @@ def make_params(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, 
     return p
 
 
-def _check(t, name, dtype, shape):
+def _check_all(specs):
+    """_check over (tensor, name, dtype, shape) entries: dtype, shape and
+    layout of every tensor first, then that each lives on the device."""
+    for t, name, dt, shp in specs:
+        _check(t, name, dt, shp, device=False)
+    for t, name, dt, shp in specs:
+        _check(t, name, dt, shp)
+
+
+def _check(t, name, dtype, shape, device=True):
     import torch
     if t is None:
         return
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
-        raise TypeError(f"{name} must be a device tensor")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if device and not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
 
 
-def _prepare(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, out, S_T):
+def _prepare(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, out, S_T, stream=None):
     import torch
     B, T, H, D = q.shape
     io = q.dtype
     if io not in (torch.bfloat16, torch.float32):
         raise TypeError("q, k, v, gate must be bfloat16 or float32")
     f32 = torch.float32
-    for t, name, dt, shp in ((q, "q", io, (B, T, H, D)), (k, "k", io, (B, T, H, D)),
+    _check_all(((q, "q", io, (B, T, H, D)), (k, "k", io, (B, T, H, D)),
                              (v, "v", io, (B, T, H, D)), (gate, "gate", io, (B, T, H, D)),
                              (log_a, "log_a", f32, (B, T, H)), (beta, "beta", f32, (B, T, H)),
                              (conv_q, "conv_q", f32, (H * D, 4)), (conv_k, "conv_k", f32, (H * D, 4)),
                              (conv_v, "conv_v", f32, (H * D, 4)), (norm_w, "norm_w", f32, (H, D)),
                              (S0, "S0", f32, (B, H, D, D)), (out, "out", io, (B, T, H, D)),
-                             (S_T, "S_T", f32, (B, H, D, D))):
-        _check(t, name, dt, shp)
+                             (S_T, "S_T", f32, (B, H, D, D))))
     if out is None:
-        out = torch.empty((B, T, H, D), dtype=io, device=q.device)
+        out = _alloc((B, T, H, D), io, q.device, _stream(stream, q.device))
     return out
 
 
@@ -259,17 +309,17 @@ def gdn_fwd(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w=None, S0=
     """One GDN layer forward on device tensors.  Returns (out, S_T)."""
     import torch
     lib = load()
-    out = _prepare(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, out, S_T)
+    strm = _stream(stream, q.device)
+    out = _prepare(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, out, S_T, strm)
     B, T, H, D = q.shape
     if S_T is None and want_state:
-        S_T = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+        S_T = _alloc((B, H, D, D), torch.float32, q.device, strm)
     need = gdn_fwd_workspace_bytes(B, T, H, D, GDN_BF16 if q.dtype == torch.bfloat16 else GDN_F32)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = _workspace(need, q.device, strm)
     p = make_params(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, out, S_T,
                     workspace, eps_l2, eps_norm, reverse)
-    s = (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
-    st = lib.gdn_fwd(ctypes.byref(p), ctypes.c_void_p(s))
+    st = lib.gdn_fwd(ctypes.byref(p), ctypes.c_void_p(strm.cuda_stream))
     if st != GDN_OK:
         raise GdnError(st, "gdn_fwd")
     return out, S_T
@@ -281,21 +331,21 @@ def gdn_fwd_bidir(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w=Non
     """Forward and time-reversed scans, outputs added.  Returns (out, S_T, S_T_rev)."""
     import torch
     lib = load()
-    out = _prepare(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, out, S_T)
+    strm = _stream(stream, q.device)
+    out = _prepare(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, out, S_T, strm)
     B, T, H, D = q.shape
     _check(S_T_rev, "S_T_rev", torch.float32, (B, H, D, D))
     if want_state:
         if S_T is None:
-            S_T = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+            S_T = _alloc((B, H, D, D), torch.float32, q.device, strm)
         if S_T_rev is None:
-            S_T_rev = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+            S_T_rev = _alloc((B, H, D, D), torch.float32, q.device, strm)
     need = gdn_fwd_bidir_workspace_bytes(B, T, H, D, GDN_BF16 if q.dtype == torch.bfloat16 else GDN_F32)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = _workspace(need, q.device, strm)
     p = make_params(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, out, S_T,
                     workspace, eps_l2, eps_norm, False)
-    s = (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
-    st = lib.gdn_fwd_bidir(ctypes.byref(p), ctypes.c_void_p(_ptr(S_T_rev)), ctypes.c_void_p(s))
+    st = lib.gdn_fwd_bidir(ctypes.byref(p), ctypes.c_void_p(_ptr(S_T_rev)), ctypes.c_void_p(strm.cuda_stream))
     if st != GDN_OK:
         raise GdnError(st, "gdn_fwd_bidir")
     return out, S_T, S_T_rev
@@ -341,12 +391,12 @@ def gdn_in_proj(x, w_in, A_log, H, D, b_in=None, stream=None):
     _check(b_in, "b_in", torch.float32, (N,))
     _check(A_log, "A_log", torch.float32, (H,))
     dev = x.device
-    q, k, v, gate = (torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev) for _ in range(4))
-    beta = torch.empty((B, T, H), dtype=torch.float32, device=dev)
-    log_a = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    strm = _stream(stream, dev)
+    q, k, v, gate = (_alloc((B, T, H, D), torch.bfloat16, dev, strm) for _ in range(4))
+    beta = _alloc((B, T, H), torch.float32, dev, strm)
+    log_a = _alloc((B, T, H), torch.float32, dev, strm)
     p = in_proj_params(x, w_in, b_in, A_log, H, D, q, k, v, gate, beta, log_a)
-    s = (stream if stream is not None else torch.cuda.current_stream(dev)).cuda_stream
-    st = load().gdn_in_proj(ctypes.byref(p), ctypes.c_void_p(s))
+    st = load().gdn_in_proj(ctypes.byref(p), ctypes.c_void_p(strm.cuda_stream))
     if st != GDN_OK:
         raise GdnError(st, "gdn_in_proj")
     return q, k, v, gate, beta, log_a
@@ -370,11 +420,11 @@ def gdn_out_proj(y, w_out, b_out=None, out=None, stream=None):
     _check(w_out, "w_out", torch.bfloat16, (C, H * D))
     _check(b_out, "b_out", torch.float32, (C,))
     _check(out, "out", torch.bfloat16, (B, T, C))
+    strm = _stream(stream, y.device)
     if out is None:
-        out = torch.empty((B, T, C), dtype=torch.bfloat16, device=y.device)
+        out = _alloc((B, T, C), torch.bfloat16, y.device, strm)
     p = out_proj_params(y, w_out, b_out, out)
-    s = (stream if stream is not None else torch.cuda.current_stream(y.device)).cuda_stream
-    st = load().gdn_out_proj(ctypes.byref(p), ctypes.c_void_p(s))
+    st = load().gdn_out_proj(ctypes.byref(p), ctypes.c_void_p(strm.cuda_stream))
     if st != GDN_OK:
         raise GdnError(st, "gdn_out_proj")
     return out
@@ -410,25 +460,23 @@ def gdn_mixer_fwd(x, w_in, A_log, conv_q, conv_k, conv_v, w_out, H, D, b_in=None
     B, T, C = x.shape
     N = 4 * H * D + 2 * H
     f32 = torch.float32
-    for t, name, dt, shp in ((x, "x", torch.bfloat16, (B, T, C)), (w_in, "w_in", torch.bfloat16, (N, C)),
+    _check_all(((x, "x", torch.bfloat16, (B, T, C)), (w_in, "w_in", torch.bfloat16, (N, C)),
                              (b_in, "b_in", f32, (N,)), (A_log, "A_log", f32, (H,)),
                              (conv_q, "conv_q", f32, (H * D, 4)), (conv_k, "conv_k", f32, (H * D, 4)),
                              (conv_v, "conv_v", f32, (H * D, 4)), (norm_w, "norm_w", f32, (H, D)),
                              (S0, "S0", f32, (B, H, D, D)), (w_out, "w_out", torch.bfloat16, (C, H * D)),
                              (b_out, "b_out", f32, (C,)), (out, "out", torch.bfloat16, (B, T, C)),
-                             (S_T, "S_T", f32, (B, H, D, D))):
-        _check(t, name, dt, shp)
+                             (S_T, "S_T", f32, (B, H, D, D))))
+    strm = _stream(stream, x.device)
     if out is None:
-        out = torch.empty((B, T, C), dtype=torch.bfloat16, device=x.device)
+        out = _alloc((B, T, C), torch.bfloat16, x.device, strm)
     if S_T is None and want_state:
-        S_T = torch.empty((B, H, D, D), dtype=f32, device=x.device)
+        S_T = _alloc((B, H, D, D), f32, x.device, strm)
     if workspace is None:
-        workspace = torch.empty(max(gdn_mixer_workspace_bytes(B, T, H, D, C), 1), dtype=torch.uint8,
-                                device=x.device)
+        workspace = _workspace(gdn_mixer_workspace_bytes(B, T, H, D, C), x.device, strm)
     p = mixer_params(x, w_in, b_in, A_log, conv_q, conv_k, conv_v, norm_w, S0, w_out, b_out, out, S_T,
                      workspace, H, D, eps_l2, eps_norm)
-    s = (stream if stream is not None else torch.cuda.current_stream(x.device)).cuda_stream
-    st = load().gdn_mixer_fwd(ctypes.byref(p), ctypes.c_void_p(s))
+    st = load().gdn_mixer_fwd(ctypes.byref(p), ctypes.c_void_p(strm.cuda_stream))
     if st != GDN_OK:
         raise GdnError(st, "gdn_mixer_fwd")
     return out, S_T
@@ -453,25 +501,25 @@ def gdn_fwd_varlen(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, cu_seqlen
     (a host sequence of ints), S0 / S_T [N, H, D, D].  Returns (out, S_T)."""
     import torch
     lib = load()
-    cu = seq_table(cu_seqlens)
-    N = len(cu) - 1
-    out = _prepare(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, None, out, None)
-    _, total, H, D = q.shape
-    if q.shape[0] != 1:
+    if not isinstance(q, torch.Tensor) or q.dim() != 4 or q.shape[0] != 1:
         raise ValueError("q must be [1, total, H, D] (sequences packed along the token axis)")
+    cu = seq_table(_checked_table(cu_seqlens, q.shape[1]))
+    N = len(cu) - 1
+    strm = _stream(stream, q.device)
+    out = _prepare(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, None, out, None, strm)
+    _, total, H, D = q.shape
     _check(S0, "S0", torch.float32, (N, H, D, D))
     _check(S_T, "S_T", torch.float32, (N, H, D, D))
     if S_T is None and want_state:
-        S_T = torch.empty((N, H, D, D), dtype=torch.float32, device=q.device)
+        S_T = _alloc((N, H, D, D), torch.float32, q.device, strm)
     io = GDN_BF16 if q.dtype == torch.bfloat16 else GDN_F32
     if workspace is None:
         need = lib.gdn_fwd_varlen_workspace_bytes(ctypes.byref(_sizes(N, 0, H, D, io)), cu)
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = _workspace(need, q.device, strm)
     p = make_params(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, out, S_T, workspace,
                     eps_l2, eps_norm, reverse)
     p.B = N
-    s = (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
-    st = lib.gdn_fwd_varlen(ctypes.byref(p), cu, ctypes.c_void_p(s))
+    st = lib.gdn_fwd_varlen(ctypes.byref(p), cu, ctypes.c_void_p(strm.cuda_stream))
     if st != GDN_OK:
         raise GdnError(st, "gdn_fwd_varlen")
     return out, S_T
@@ -533,13 +581,14 @@ def gdn_bwd(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, dy, 
     _check(dy, "dy", q.dtype, (B, T, H, D))
     _check(dS_T, "dS_T", torch.float32, (B, H, D, D))
     dev, io, f32 = q.device, q.dtype, torch.float32
-    g = {n: torch.empty((B, T, H, D), dtype=io, device=dev) for n in ("q", "k", "v", "gate")}
-    g["log_a"] = torch.empty((B, T, H), dtype=f32, device=dev)
-    g["beta"] = torch.empty((B, T, H), dtype=f32, device=dev)
+    strm = _stream(stream, dev)
+    g = {n: _alloc((B, T, H, D), io, dev, strm) for n in ("q", "k", "v", "gate")}
+    g["log_a"] = _alloc((B, T, H), f32, dev, strm)
+    g["beta"] = _alloc((B, T, H), f32, dev, strm)
     for n in ("conv_q", "conv_k", "conv_v"):
-        g[n] = torch.empty((H * D, 4), dtype=f32, device=dev)
-    g["norm_w"] = torch.empty((H, D), dtype=f32, device=dev) if want_norm_w else None
-    g["S0"] = torch.empty((B, H, D, D), dtype=f32, device=dev) if want_S0 else None
+        g[n] = _alloc((H * D, 4), f32, dev, strm)
+    g["norm_w"] = _alloc((H, D), f32, dev, strm) if want_norm_w else None
+    g["S0"] = _alloc((B, H, D, D), f32, dev, strm) if want_S0 else None
     if out is not None:
         for n, t in out.items():
             if g.get(n) is not None:
@@ -547,11 +596,10 @@ def gdn_bwd(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, dy, 
             g[n] = t
     need = gdn_bwd_workspace_bytes(B, T, H, D, GDN_BF16 if io == torch.bfloat16 else GDN_F32)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        workspace = _workspace(need, dev, strm)
     p = bwd_params(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, dy, dS_T, g,
                    workspace, eps_l2, eps_norm, reverse)
-    s = (stream if stream is not None else torch.cuda.current_stream(dev)).cuda_stream
-    st = lib.gdn_bwd(ctypes.byref(p), ctypes.c_void_p(s))
+    st = lib.gdn_bwd(ctypes.byref(p), ctypes.c_void_p(strm.cuda_stream))
     if st != GDN_OK:
         raise GdnError(st, "gdn_bwd")
     return g
@@ -560,39 +608,54 @@ def gdn_bwd(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, dy, 
 def gdn_bwd_varlen(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, dy, dS_T, cu_seqlens,
                    eps_l2=1e-6, eps_norm=1e-6, want_norm_w=True, want_S0=True, reverse=False, stream=None):
     """The backward of gdn_fwd_varlen: q, k, v, gate, dy [total, H, D] (a
-    leading batch dimension of 1 is accepted), log_a, beta [total, H];
-    cu_seqlens a host sequence of B + 1 ints; S0, dS_T [B, H, D, D] or None.
-    Returns a dict keyed by BWD_GRADS (per-token gradients shaped like their
-    inputs)."""
+    leading batch dimension of 1 is accepted), log_a, beta [total, H] (or
+    [1, total, H]); cu_seqlens a host sequence of B + 1 ints; S0, dS_T
+    [B, H, D, D] or None.  Returns a dict keyed by BWD_GRADS (per-token
+    gradients shaped like their inputs).  Every tensor is checked (device,
+    dtype, shape, contiguity) and the table against the packed row count
+    before anything is launched."""
     import torch
     lib = load()
-    tok = tuple(q.shape[-3:])
-    total, H, D = tok
-    cu = (ctypes.c_int * len(cu_seqlens))(*[int(x) for x in cu_seqlens])
-    B = len(cu_seqlens) - 1
+    if not isinstance(q, torch.Tensor) or q.dim() not in (3, 4) or (q.dim() == 4 and q.shape[0] != 1):
+        raise ValueError("q must be [total, H, D] or [1, total, H, D]")
+    total, H, D = tuple(q.shape[-3:])
+    vals = _checked_table(cu_seqlens, total)
+    cu = seq_table(vals)
+    B = len(vals) - 1
     dev, io, f32 = q.device, q.dtype, torch.float32
-    g = {n: torch.empty(q.shape, dtype=io, device=dev) for n in ("q", "k", "v", "gate")}
-    g["log_a"] = torch.empty(log_a.shape, dtype=f32, device=dev)
-    g["beta"] = torch.empty(beta.shape, dtype=f32, device=dev)
+    if io not in (torch.bfloat16, torch.float32):
+        raise TypeError("q, k, v, gate, dy must be bfloat16 or float32")
+    tok_shape = tuple(q.shape)
+    gate_shape = tuple(log_a.shape) if isinstance(log_a, torch.Tensor) else None
+    if gate_shape not in ((total, H), (1, total, H)):
+        raise ValueError(f"log_a must be [total, H] or [1, total, H], got {gate_shape}")
+    _check_all(((q, "q", io, tok_shape), (k, "k", io, tok_shape), (v, "v", io, tok_shape),
+                             (gate, "gate", io, tok_shape), (dy, "dy", io, tok_shape),
+                             (log_a, "log_a", f32, gate_shape), (beta, "beta", f32, gate_shape),
+                             (conv_q, "conv_q", f32, (H * D, 4)), (conv_k, "conv_k", f32, (H * D, 4)),
+                             (conv_v, "conv_v", f32, (H * D, 4)), (norm_w, "norm_w", f32, (H, D)),
+                             (S0, "S0", f32, (B, H, D, D)), (dS_T, "dS_T", f32, (B, H, D, D))))
+    strm = _stream(stream, dev)
+    g = {n: _alloc(tok_shape, io, dev, strm) for n in ("q", "k", "v", "gate")}
+    g["log_a"] = _alloc(gate_shape, f32, dev, strm)
+    g["beta"] = _alloc(gate_shape, f32, dev, strm)
     for n in ("conv_q", "conv_k", "conv_v"):
-        g[n] = torch.empty((H * D, 4), dtype=f32, device=dev)
-    g["norm_w"] = torch.empty((H, D), dtype=f32, device=dev) if want_norm_w else None
-    g["S0"] = torch.empty((B, H, D, D), dtype=f32, device=dev) if want_S0 else None
+        g[n] = _alloc((H * D, 4), f32, dev, strm)
+    g["norm_w"] = _alloc((H, D), f32, dev, strm) if want_norm_w else None
+    g["S0"] = _alloc((B, H, D, D), f32, dev, strm) if want_S0 else None
     p = GdnBwdParams()
     p.B, p.T, p.H, p.Dk, p.Dv = B, 0, H, D, D
     p.io_dtype = GDN_BF16 if io == torch.bfloat16 else GDN_F32
     need = lib.gdn_bwd_varlen_workspace_bytes(ctypes.byref(p), cu)
     if need == 0:
         raise GdnError(GDN_ERR_INVALID_ARG, "gdn_bwd_varlen_workspace_bytes")
-    workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    workspace = _workspace(need, dev, strm)
     def as4(t):
         return t.reshape(1, total, H, D)
     p = bwd_params(as4(q), as4(k), as4(v), log_a, beta, as4(gate), conv_q, conv_k, conv_v, norm_w, S0, as4(dy),
                    dS_T, g, workspace, eps_l2, eps_norm, reverse)
     p.B, p.T = B, 0
-    s = (stream if stream is not None else torch.cuda.current_stream(dev)).cuda_stream
-    st = lib.gdn_bwd_varlen(ctypes.byref(p), cu, ctypes.c_void_p(s))
+    st = lib.gdn_bwd_varlen(ctypes.byref(p), cu, ctypes.c_void_p(strm.cuda_stream))
     if st != GDN_OK:
         raise GdnError(st, "gdn_bwd_varlen")
     return g
-

@@ -57,7 +57,8 @@ Layout layout(const gdn_fwd_params *p, int scans, bool varlen = false) {
 bool sizes_ok(const gdn_fwd_params *p) {
     if (!p) return false;
     if (p->B < 1 || p->T < 1 || p->H < 1 || p->Dk < 1 || p->Dv < 1) return false;
-    if (p->io_dtype != GDN_F32 && p->io_dtype != GDN_BF16) return false;
+    const int dt = gdn_internal::dtype_code(p->io_dtype);
+    if (dt != GDN_F32 && dt != GDN_BF16) return false;
     // element counts must fit the 32-bit grid and the index arithmetic below
     const double elems = (double)p->B * p->T * p->H * (double)(p->Dk > p->Dv ? p->Dk : p->Dv);
     if (elems > 4.0e12) return false;
@@ -357,14 +358,14 @@ struct ScanBufs {
 };
 
 ScanBufs scan_bufs(const gdn_fwd_params *p, const Layout &L, int scan) {
-    char *base = static_cast<char *>(p->workspace) + (size_t)scan * L.per_scan;
+    char *base = gdn_internal::at_offset(p->workspace, (size_t)scan * L.per_scan);
     ScanBufs b;
-    b.rec = base + L.rec;
-    b.sc = base + L.sc;
-    b.gC = reinterpret_cast<float *>(base + L.gC);
+    b.rec = gdn_internal::at_offset(base, L.rec);
+    b.sc = gdn_internal::at_offset(base, L.sc);
+    b.gC = gdn_internal::at_offset<float>(base, L.gC);
     const size_t sbytes = round_up((size_t)p->B * p->H * p->Dk * p->Dk * sizeof(float));
-    b.smid[0] = reinterpret_cast<float *>(base + L.smid);
-    b.smid[1] = reinterpret_cast<float *>(base + L.smid + sbytes);
+    b.smid[0] = gdn_internal::at_offset<float>(base, L.smid);
+    b.smid[1] = gdn_internal::at_offset<float>(base, L.smid + sbytes);
     return b;
 }
 
@@ -460,7 +461,7 @@ gdn_status plan_fwd(Plan &plan, const gdn_fwd_params *p, float *S_T_rev, bool bi
         // reversed chain on stream 3, all preps on stream 1; the outputs run
         // on stream 2, the reversed scan's after all of the forward scan's
         // (they add into its fp32 sum)
-        float *acc = reinterpret_cast<float *>(static_cast<char *>(p->workspace) + L.acc);
+        float *acc = gdn_internal::at_offset<float>(p->workspace, L.acc);
         plan_scan<T, D>(plan, p, 0, scan_bufs(p, L, 0), p->S_T, 1, 0, 2, 1, acc, cu);
         plan_scan<T, D>(plan, p, 1, scan_bufs(p, L, 1), S_T_rev, 1, 3, 2, 2, acc, cu);
     }
@@ -549,7 +550,7 @@ gdn_status varlen_call(const gdn_fwd_params *p, const int *cu, hipStream_t s) {
     st = validate(&q, nullptr, 1, (size_t)cu[q.B], true);
     if (st != GDN_OK) return st;
     const Layout L = layout(&q, 1, true);
-    int *cu_dev = reinterpret_cast<int *>(static_cast<char *>(q.workspace) + L.seq);
+    int *cu_dev = gdn_internal::at_offset<int>(q.workspace, L.seq);
     Plan plan;
     st = make_plan(plan, &q, nullptr, false, cu_dev);
     if (st != GDN_OK) return st;
@@ -652,7 +653,13 @@ const char *gdn_fwd_launch_name(const gdn_fwd_params *p, int bidirectional, int 
 }
 
 const char *gdn_status_string(gdn_status s) {
-    switch (s) {
+    // A C caller may pass any int here.  In C++ an enum object holding a
+    // value outside the enumeration's range is undefined behaviour, so the
+    // code is read as the int it is (host UBSan flags the switch otherwise).
+    static_assert(sizeof(gdn_status) == sizeof(int), "gdn_status is passed as an int");
+    int code;
+    memcpy(&code, &s, sizeof code);
+    switch (code) {
     case GDN_OK: return "ok";
     case GDN_ERR_INVALID_ARG: return "invalid argument";
     case GDN_ERR_UNSUPPORTED: return "unsupported size or dtype";

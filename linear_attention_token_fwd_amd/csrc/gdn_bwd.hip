@@ -10,6 +10,7 @@
 
 #include "../../include/gdn.h"
 #include "bwd.hpp"
+#include "internal.hpp"
 
 namespace {
 
@@ -47,7 +48,8 @@ Layout layout(const gdn_bwd_params *p, bool varlen = false) {
 bool sizes_ok(const gdn_bwd_params *p) {
     if (!p) return false;
     if (p->B < 1 || p->T < 1 || p->H < 1 || p->Dk < 1 || p->Dv < 1) return false;
-    if (p->io_dtype != GDN_F32 && p->io_dtype != GDN_BF16) return false;
+    const int dt = gdn_internal::dtype_code(p->io_dtype);
+    if (dt != GDN_F32 && dt != GDN_BF16) return false;
     if (p->H > 65535 || p->B > 65535) return false;
     // element counts inside one launch's index arithmetic, and the chunk grid
     if ((double)p->B * p->T * p->H * (double)p->Dk > 4.0e12) return false;
@@ -181,11 +183,10 @@ template <class IO, int D> gdnb::Args make_args(const gdn_bwd_params *p, const i
     a.dlog_a = p->dlog_a, a.dbeta = p->dbeta;
     a.dconv_q = p->dconv_q, a.dconv_k = p->dconv_k, a.dconv_v = p->dconv_v;
     a.dnorm_w = p->dnorm_w, a.dS0 = p->dS0;
-    char *ws = static_cast<char *>(p->workspace);
-    a.rec = reinterpret_cast<float *>(ws + L.rec);
-    a.part_conv = reinterpret_cast<float *>(ws + L.part_conv);
-    a.part_norm = reinterpret_cast<float *>(ws + L.part_norm);
-    a.sink = reinterpret_cast<float *>(ws + L.sink);
+    a.rec = gdn_internal::at_offset<float>(p->workspace, L.rec);
+    a.part_conv = gdn_internal::at_offset<float>(p->workspace, L.part_conv);
+    a.part_norm = gdn_internal::at_offset<float>(p->workspace, L.part_norm);
+    a.sink = gdn_internal::at_offset<float>(p->workspace, L.sink);
     a.reverse = p->reverse;
     a.cu = cu_dev;
     return a;
@@ -303,7 +304,7 @@ gdn_status varlen_call(const gdn_bwd_params *p, const int *cu, hipStream_t s) {
     if (st != GDN_OK) return st;
     st = set_attributes();
     if (st != GDN_OK) return st;
-    int *cu_dev = reinterpret_cast<int *>(static_cast<char *>(q.workspace) + layout(&q, true).seq);
+    int *cu_dev = gdn_internal::at_offset<int>(q.workspace, layout(&q, true).seq);
     // the table goes to the workspace first, on the caller's stream
     if (hipMemcpyAsync(cu_dev, cu, sizeof(int) * (q.B + 1), hipMemcpyHostToDevice, s) != hipSuccess)
         return GDN_ERR_HIP;

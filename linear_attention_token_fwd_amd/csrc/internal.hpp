@@ -2,12 +2,33 @@
 // (hidden: not part of the C ABI).
 #pragma once
 #include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
 
 #include "../../include/gdn.h"
 
 namespace gdn_internal {
 
 #define GDN_HIDDEN __attribute__((visibility("hidden")))
+
+// The I/O dtype as the int a C caller stored.  A C struct may hold any int in
+// an enum field, but in C++ loading an enum object whose value lies outside
+// the enumeration's range is undefined behaviour, so the checks read the
+// field's bytes as an int; once a value has passed them, the field is read
+// as the enum.
+// base + off bytes, computed on the address's integer value: the plan
+// builders also run for sizes only (launch counts and names), with a NULL
+// workspace, where pointer arithmetic would be undefined.
+template <class T = char> inline T *at_offset(const void *base, size_t off) {
+    return reinterpret_cast<T *>(reinterpret_cast<uintptr_t>(base) + off);
+}
+
+inline int dtype_code(const gdn_dtype &d) {
+    static_assert(sizeof(gdn_dtype) == sizeof(int), "gdn_dtype is stored as an int");
+    int v;
+    __builtin_memcpy(&v, &d, sizeof v);
+    return v;
+}
 
 // Every check gdn_fwd makes, without launching anything.
 GDN_HIDDEN gdn_status fwd_check(const gdn_fwd_params *p);

@@ -272,3 +272,90 @@ def test_bwd_varlen_equals_each_sequence(reverse):
             wsum[n] = wsum[n] + one[n].double()
     for n, ref in wsum.items():
         assert rel_l2(got[n].double().cpu().numpy(), ref.cpu().numpy()) < 1e-5, n
+
+
+def _varlen_bwd_case(lens, H, D, dtype, seed):
+    w = _workload(dtype, D)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(int)
+    total = int(cu[-1])
+    inp = gdn_inputs.generate(w, T=total, H=H, B=1, seed=seed)
+    rng = np.random.default_rng(seed + 1)
+    S0 = (0.1 * rng.standard_normal((len(lens), H, D, D))).astype(np.float32)
+    grads = gdn_inputs.generate_grads(w, seed=seed + 2, T=total, H=H, B=1)
+    dS_T = rng.standard_normal((len(lens), H, D, D)).astype(np.float32)
+    return inp, S0, grads, dS_T, cu
+
+
+def _run_varlen_bwd(inp, S0, grads, dS_T, cu, dtype, reverse):
+    import linear_attention_token_fwd_amd as gdn
+    d = gdn.to_device(inp, dtype=torch_dtype(dtype))
+    dy = torch.from_numpy(grads["dy"]).to(torch_dtype(dtype)).cuda()
+    S0_d, dS_d = torch.from_numpy(S0).cuda(), torch.from_numpy(dS_T).cuda()
+    got = gdn.gdn_bwd_varlen(d["q"][0], d["k"][0], d["v"][0], d["log_a"][0], d["beta"][0], d["gate"][0],
+                             d["conv_q"], d["conv_k"], d["conv_v"], d["norm_w"], S0_d, dy[0], dS_d, list(cu),
+                             reverse=reverse)
+    torch.cuda.synchronize()
+    return d, dy, S0_d, dS_d, got
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_bwd_varlen_multi_range_equals_each_sequence(reverse):
+    """The backward of a variable-length batch at the model's shape (H = 12,
+    d = 128, bf16) whose longest sequence spans several chain ranges (about
+    64 chunks each) while the others end inside the first and the third:
+    lengths 20000, 37, 9000, 64.  Each sequence's per-token gradients and dS0
+    equal gdn_bwd on that sequence alone, bit for bit; the weight gradients
+    equal the sums of the single calls' to rounding."""
+    import linear_attention_token_fwd_amd as gdn
+    lens = (20000, 37, 9000, 64)
+    inp, S0, grads, dS_T, cu = _varlen_bwd_case(lens, 12, 128, "bf16", 1201)
+    say(f"case: bwd varlen multi-range lengths {lens} H=12 d=128 bf16 reverse={reverse}")
+    d, dy, S0_d, dS_d, got = _run_varlen_bwd(inp, S0, grads, dS_T, cu, "bf16", reverse)
+    tok = ("q", "k", "v", "gate", "log_a", "beta")
+    wsum = {n: 0.0 for n in ("conv_q", "conv_k", "conv_v", "norm_w")}
+    for b in range(len(lens)):
+        sl = slice(int(cu[b]), int(cu[b + 1]))
+        one = gdn.gdn_bwd(*[d[n][:, sl].contiguous() if n in tok else d[n]
+                            for n in ("q", "k", "v", "log_a", "beta", "gate", "conv_q", "conv_k", "conv_v", "norm_w")],
+                          S0_d[b:b + 1].contiguous(), dy[:, sl].contiguous(), dS_d[b:b + 1].contiguous(),
+                          reverse=reverse)
+        torch.cuda.synchronize()
+        for n in tok:
+            assert torch.isfinite(got[n][sl]).all(), (b, n)
+            assert torch.equal(got[n][sl], one[n][0]), (b, n)
+        assert torch.equal(got["S0"][b], one["S0"][0]), (b, "S0")
+        for n in wsum:
+            wsum[n] = wsum[n] + one[n].double()
+        del one
+    for n, ref in wsum.items():
+        assert rel_l2(got[n].double().cpu().numpy(), ref.cpu().numpy()) < 1e-5, n
+
+
+def test_bwd_varlen_multi_range_matches_oracle():
+    """The same structure at d = 64, one head, against the fp64 autograd
+    oracle on each sequence alone: lengths 9000 (141 chunks, three chain
+    ranges), 37, 5000 (ends inside the second range) and 64."""
+    lens = (9000, 37, 5000, 64)
+    H, D = 1, 64
+    inp, S0, grads, dS_T, cu = _varlen_bwd_case(lens, H, D, "bf16", 1301)
+    say(f"case: bwd varlen multi-range lengths {lens} H={H} d={D} bf16 vs oracle")
+    _, _, _, _, got = _run_varlen_bwd(inp, S0, grads, dS_T, cu, "bf16", False)
+    tok = ("q", "k", "v", "gate", "log_a", "beta")
+    wsum = {n: 0.0 for n in ("conv_q", "conv_k", "conv_v", "norm_w")}
+    for b in range(len(lens)):
+        sl = slice(int(cu[b]), int(cu[b + 1]))
+        seq = {n: (inp[n][:, sl] if n in tok else inp[n]) for n in obwd.NAMES if n != "S0"}
+        seq["S0"] = S0[b:b + 1]
+        ref = oracle_grads(seq, {"dy": grads["dy"][:, sl], "dS_T": dS_T[b:b + 1]})
+        for n in tok:
+            e = rel_l2(got[n][sl].double().cpu().numpy(), ref[n][0])
+            say(f"  seq {b} (T={lens[b]}) d{n} rel-L2 {e:.2e}")
+            assert e <= TOL["bf16"], (b, n, e)
+        e = rel_l2(got["S0"][b].double().cpu().numpy(), ref["S0"][0])
+        assert e <= TOL["bf16"], (b, "S0", e)
+        for n in wsum:
+            wsum[n] = wsum[n] + ref[n]
+    for n, ref in wsum.items():
+        e = rel_l2(got[n].double().cpu().numpy(), ref)
+        say(f"  d{n} (sum over sequences) rel-L2 {e:.2e}")
+        assert e <= TOL["bf16"], (n, e)

@@ -194,3 +194,51 @@ def test_varlen_long_and_short():
         ry, rs, _ = oracle.inputs_for(seq)
         check(f"y[{i}]", y[:, cu[i]:cu[i + 1]], ry, "bf16")
         check(f"S_T[{i}]", s[i:i + 1], rs, "bf16")
+
+
+MULTI_RANGE_LENGTHS = [20000, 37, 9000, 64]
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_varlen_multi_range(reverse):
+    """A variable-length batch whose longest sequence spans several chunk
+    ranges of the launch plan while the others end inside the first and the
+    second range: lengths 20000, 37, 9000 and 64 at the model's shape
+    (H = 12, d = 128, bf16), as in a batch of two videos of different lengths
+    with two short prompts.  Each sequence against the oracle on that
+    sequence alone, and bit-identical to gdn_fwd on it alone (the final state
+    of a sequence that ends early is written by the range it ends in)."""
+    import linear_attention_token_fwd_amd as gdn
+    w = W[1]
+    lengths = MULTI_RANGE_LENGTHS
+    H = 12
+    rng = np.random.default_rng(9090)
+    seqs = []
+    base = gdn_inputs.generate(w, T=64, H=H, seed=9091)
+    for i, L in enumerate(lengths):
+        d = gdn_inputs.generate(w, T=L, H=H, seed=9100 + i)
+        for key in ("conv_q", "conv_k", "conv_v", "norm_w"):
+            d[key] = base[key]
+        d["S0"] = (0.05 * rng.standard_normal((1, H, w.D, w.D))).astype(np.float32)
+        seqs.append(d)
+    packed = {key: np.concatenate([d[key] for d in seqs], axis=1) for key in ("q", "k", "v", "gate", "log_a", "beta")}
+    for key in ("conv_q", "conv_k", "conv_v", "norm_w"):
+        packed[key] = base[key]
+    packed["S0"] = np.concatenate([d["S0"] for d in seqs], axis=0)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).tolist()
+    say(f"case: varlen multi-range lengths {lengths} H={H} d=128 bf16 reverse={reverse}")
+    d = gdn.to_device(packed, dtype=torch.bfloat16)
+    out = torch.full((1, cu[-1], H, w.D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    S_T = torch.full((len(lengths), H, w.D, w.D), float("nan"), dtype=torch.float32, device="cuda")
+    gdn.gdn_fwd_varlen(d["q"], d["k"], d["v"], d["log_a"], d["beta"], d["gate"], d["conv_q"], d["conv_k"],
+                       d["conv_v"], cu, norm_w=d["norm_w"], S0=d["S0"], reverse=reverse, out=out, S_T=S_T)
+    torch.cuda.synchronize()
+    y = out.double().cpu().numpy()
+    s = S_T.double().cpu().numpy()
+    for i, seq in enumerate(seqs):
+        ys = y[:, cu[i]:cu[i + 1]]
+        ry, rs, _ = oracle.inputs_for(seq, reverse=reverse)
+        check(f"y[{i}] (T={lengths[i]})", ys, ry, "bf16")
+        check(f"S_T[{i}]", s[i:i + 1], rs, "bf16")
+        y1, s1 = run_gpu(seq, "bf16", reverse=reverse)
+        assert np.array_equal(ys, y1) and np.array_equal(s[i:i + 1], s1), f"sequence {i} differs from gdn_fwd alone"
