@@ -126,10 +126,10 @@ size_t gdn_fwd_workspace_bytes(const gdn_fwd_params *p);
 
 /*
  * One GDN layer forward (steps 1-5 above), in scan order given by p->reverse.
- * Supported: io_dtype GDN_BF16 with Dk = Dv in {64, 128}, and GDN_F32 with
- * Dk = Dv = 64; other combinations return GDN_ERR_UNSUPPORTED.  With bf16
- * I/O the matrix products take bf16 operands with fp32 accumulation and an
- * fp32 master state; with fp32 I/O they run in fp32 throughout.
+ * Supported: io_dtype GDN_BF16 or GDN_F32 with Dk = Dv in {64, 128}; other
+ * sizes return GDN_ERR_UNSUPPORTED.  With bf16 I/O the matrix products take
+ * bf16 operands with fp32 accumulation and an fp32 master state; with fp32
+ * I/O they run in fp32 throughout.
  */
 gdn_status gdn_fwd(const gdn_fwd_params *p, struct ihipStream_t *stream);
 

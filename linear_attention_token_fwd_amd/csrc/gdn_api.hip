@@ -67,9 +67,7 @@ bool sizes_ok(const gdn_fwd_params *p) {
 }
 
 bool supported(const gdn_fwd_params *p) {
-    if (p->Dk != p->Dv) return false;
-    if (p->io_dtype == GDN_BF16) return p->Dk == 64 || p->Dk == 128;
-    return p->Dk == 64;
+    return p->Dk == p->Dv && (p->Dk == 64 || p->Dk == 128);
 }
 
 struct Range {
@@ -472,6 +470,7 @@ gdn_status plan_fwd(Plan &plan, const gdn_fwd_params *p, float *S_T_rev, bool bi
 gdn_status make_plan(Plan &plan, const gdn_fwd_params *p, float *S_T_rev, bool bidir, const int *cu = nullptr) {
     if (p->io_dtype == GDN_BF16 && p->Dk == 128) return plan_fwd<bf16, 128>(plan, p, S_T_rev, bidir, cu);
     if (p->io_dtype == GDN_BF16 && p->Dk == 64) return plan_fwd<bf16, 64>(plan, p, S_T_rev, bidir, cu);
+    if (p->io_dtype == GDN_F32 && p->Dk == 128) return plan_fwd<float, 128>(plan, p, S_T_rev, bidir, cu);
     if (p->io_dtype == GDN_F32 && p->Dk == 64) return plan_fwd<float, 64>(plan, p, S_T_rev, bidir, cu);
     return GDN_ERR_UNSUPPORTED;
 }
@@ -487,12 +486,15 @@ gdn_status set_attributes() {
         } attrs[] = {
             {reinterpret_cast<const void *>(&gdn::gdn_prep_kernel<bf16, 128>), sizeof(gdn::PrepSmem<bf16, 128>)},
             {reinterpret_cast<const void *>(&gdn::gdn_prep_kernel<bf16, 64>), sizeof(gdn::PrepSmem<bf16, 64>)},
+            {reinterpret_cast<const void *>(&gdn::gdn_prep_kernel<float, 128>), sizeof(gdn::PrepSmem<float, 128>)},
             {reinterpret_cast<const void *>(&gdn::gdn_prep_kernel<float, 64>), sizeof(gdn::PrepSmem<float, 64>)},
             {reinterpret_cast<const void *>(&gdn::gdn_state_kernel<bf16, 128>), state_lds<bf16, 128>()},
             {reinterpret_cast<const void *>(&gdn::gdn_state_kernel<bf16, 64>), state_lds<bf16, 64>()},
+            {reinterpret_cast<const void *>(&gdn::gdn_state_kernel<float, 128>), state_lds<float, 128>()},
             {reinterpret_cast<const void *>(&gdn::gdn_state_kernel<float, 64>), state_lds<float, 64>()},
             {reinterpret_cast<const void *>(&gdn::gdn_out_kernel<bf16, 128>), sizeof(gdn::OutSmem<bf16, 128>)},
             {reinterpret_cast<const void *>(&gdn::gdn_out_kernel<bf16, 64>), sizeof(gdn::OutSmem<bf16, 64>)},
+            {reinterpret_cast<const void *>(&gdn::gdn_out_kernel<float, 128>), sizeof(gdn::OutSmem<float, 128>)},
             {reinterpret_cast<const void *>(&gdn::gdn_out_kernel<float, 64>), sizeof(gdn::OutSmem<float, 64>)},
         };
         for (const A &a : attrs)

@@ -90,8 +90,12 @@ def test_launch_plan(lib):
     assert lib.gdn_fwd_launch_count(ctypes.byref(p), 1) == 2 * n
     short = gdn._sizes(1, 100, 2, 64, gdn.GDN_F32)
     assert lib.gdn_fwd_launch_count(ctypes.byref(short), 0) == 3
-    for unsupported in ((1, 64, 2, 96, gdn.GDN_BF16), (1, 64, 2, 128, gdn.GDN_F32)):
+    for unsupported in ((1, 64, 2, 96, gdn.GDN_BF16), (1, 64, 2, 32, gdn.GDN_F32)):
         assert lib.gdn_fwd_launch_count(ctypes.byref(gdn._sizes(*unsupported)), 0) == -1
+    # every I/O dtype with D = 64 and D = 128
+    for io in (gdn.GDN_BF16, gdn.GDN_F32):
+        for D in (64, 128):
+            assert lib.gdn_fwd_launch_count(ctypes.byref(gdn._sizes(1, 100, 2, D, io)), 0) == 3
 
 
 def fake_params(lib, B=1, T=200, H=2, D=64, io=gdn.GDN_BF16, bidir=False):
@@ -124,7 +128,7 @@ CASES = [
     ("T = 0", lambda p: setattr(p, "T", 0), gdn.GDN_ERR_INVALID_ARG),
     ("Dk != Dv", lambda p: setattr(p, "Dv", 128), gdn.GDN_ERR_UNSUPPORTED),
     ("D = 96", lambda p: (setattr(p, "Dk", 96), setattr(p, "Dv", 96)), gdn.GDN_ERR_UNSUPPORTED),
-    ("fp32 D = 128", lambda p: (setattr(p, "io_dtype", gdn.GDN_F32), setattr(p, "Dk", 128), setattr(p, "Dv", 128)),
+    ("fp32 D = 64, Dv = 128", lambda p: (setattr(p, "io_dtype", gdn.GDN_F32), setattr(p, "Dv", 128)),
      gdn.GDN_ERR_UNSUPPORTED),
     ("q misaligned", lambda p: setattr(p, "q", p.q + 8), gdn.GDN_ERR_ALIGNMENT),
     ("log_a misaligned", lambda p: setattr(p, "log_a", p.log_a + 2), gdn.GDN_ERR_ALIGNMENT),
@@ -406,4 +410,5 @@ def test_bwd_varlen_table_checks(lib):
     assert lib.gdn_bwd_varlen_workspace_bytes(ctypes.byref(p), IP(0, 100, 250, 300)) == q.workspace_bytes + 256
     assert lib.gdn_bwd_varlen(ctypes.byref(p), IP(0, 100, 90, 300), None) == gdn.GDN_ERR_INVALID_ARG
     assert lib.gdn_bwd_varlen(ctypes.byref(p), None, None) == gdn.GDN_ERR_INVALID_ARG
+
 

@@ -57,6 +57,21 @@ def test_bf16_d64():
     compare_workload(w)
 
 
+F32_D128 = gdn_inputs.Workload(92, "fp32 d128", 1, 32760, 12, 128, "f32")
+
+
+@pytest.mark.parametrize("T,H,reverse", [(64 * 5 + 37, 2, False), (64 * 5 + 37, 2, True), (1, 3, False)])
+def test_f32_d128(T, H, reverse):
+    """fp32 I/O with d = 128 (the fp32 MFMA path at the model's head size),
+    to the fp32 bar."""
+    compare_workload(F32_D128, T=T, H=H, reverse=reverse)
+
+
+def test_f32_d128_full_length():
+    """fp32 I/O, d = 128, at the full 480x832 length: T = 32760, H = 12."""
+    compare_workload(F32_D128)
+
+
 @pytest.mark.parametrize("wid", [0, 1])
 def test_reverse_scan(wid):
     compare_workload(W[wid], T=64 * 3 + 5, H=2, reverse=True)
