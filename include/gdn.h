@@ -133,6 +133,23 @@ size_t gdn_fwd_workspace_bytes(const gdn_fwd_params *p);
  */
 gdn_status gdn_fwd(const gdn_fwd_params *p, struct ihipStream_t *stream);
 
+/*
+ * gdn_fwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same operation, results equal to gdn_fwd's bit for bit, but p->workspace
+ * and p->workspace_bytes are ignored.  The workspace is instead a 64 MiB
+ * array the library holds in device memory (one per GPU, for the life of the
+ * process).  The call allocates nothing and creates nothing (no memory,
+ * streams, events or graphs): its kernels run one after another on
+ * `stream`.  Sizes whose workspace (gdn_fwd_workspace_bytes) exceeds 64 MiB
+ * return GDN_ERR_WORKSPACE before any device call; for example B = 1,
+ * H = 8, D = 128 bf16 fits up to T = 4544.  All calls on one GPU share the
+ * array: calls that may overlap on that GPU (on different streams, or from
+ * different threads without ordering) race and must not be issued.  Every
+ * other rule is gdn_fwd's.
+ */
+gdn_status gdn_fwd_noalloc(const gdn_fwd_params *p, struct ihipStream_t *stream);
+
 /* Workspace for gdn_fwd_bidir (two scans' partial results at once). */
 size_t gdn_fwd_bidir_workspace_bytes(const gdn_fwd_params *p);
 

@@ -24,7 +24,8 @@ EXPORTS = ("gdn_fwd", "gdn_fwd_bidir", "gdn_fwd_workspace_bytes", "gdn_fwd_bidir
            "gdn_in_proj", "gdn_out_proj", "gdn_mixer_workspace_bytes", "gdn_mixer_fwd", "gdn_mixer_fwd_timed",
            "gdn_fwd_varlen", "gdn_fwd_varlen_workspace_bytes", "gdn_set_graph_cache_limit",
            "gdn_graph_cache_count", "gdn_bwd", "gdn_bwd_workspace_bytes", "gdn_bwd_timed",
-           "gdn_bwd_launch_count", "gdn_bwd_launch_name", "gdn_bwd_varlen", "gdn_bwd_varlen_workspace_bytes")
+           "gdn_bwd_launch_count", "gdn_bwd_launch_name", "gdn_bwd_varlen", "gdn_bwd_varlen_workspace_bytes",
+           "gdn_fwd_noalloc")
 
 
 class GdnFwdParams(ctypes.Structure):
@@ -110,6 +111,8 @@ def load(path: str | None = None):
     P = ctypes.POINTER(GdnFwdParams)
     lib.gdn_fwd.argtypes = [P, ctypes.c_void_p]
     lib.gdn_fwd.restype = ctypes.c_int
+    lib.gdn_fwd_noalloc.argtypes = [P, ctypes.c_void_p]
+    lib.gdn_fwd_noalloc.restype = ctypes.c_int
     lib.gdn_fwd_bidir.argtypes = [P, ctypes.c_void_p, ctypes.c_void_p]
     lib.gdn_fwd_bidir.restype = ctypes.c_int
     lib.gdn_fwd_workspace_bytes.argtypes = [P]
@@ -322,6 +325,24 @@ def gdn_fwd(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w=None, S0=
     st = lib.gdn_fwd(ctypes.byref(p), ctypes.c_void_p(strm.cuda_stream))
     if st != GDN_OK:
         raise GdnError(st, "gdn_fwd")
+    return out, S_T
+
+
+def gdn_fwd_noalloc(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, out, S_T=None, norm_w=None, S0=None,
+                    eps_l2=1e-6, eps_norm=1e-6, reverse=False, stream=None):
+    """gdn_fwd into caller-given outputs (out, and S_T or None) with the
+    library's own 64 MiB device workspace: nothing is allocated, by the
+    binding or by the library.  Returns (out, S_T)."""
+    lib = load()
+    strm = _stream(stream, q.device)
+    _prepare(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, out, S_T, strm)
+    if out is None:
+        raise ValueError("gdn_fwd_noalloc writes into a caller-given out tensor")
+    p = make_params(q, k, v, log_a, beta, gate, conv_q, conv_k, conv_v, norm_w, S0, out, S_T, None,
+                    eps_l2, eps_norm, reverse)
+    st = lib.gdn_fwd_noalloc(ctypes.byref(p), ctypes.c_void_p(strm.cuda_stream))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_fwd_noalloc")
     return out, S_T
 
 

@@ -564,6 +564,67 @@ gdn_status varlen_call(const gdn_fwd_params *p, const int *cu, hipStream_t s) {
     return run_plan(plan, s, nullptr, true);
 }
 
+// ---- the entry point that allocates nothing (gdn_fwd_noalloc)
+//
+// Its workspace is this file-scope device array: every GPU the library runs
+// on holds its own copy, for the life of the process.  In host code the
+// array's name only stands for it; the address of a device's copy is taken
+// once per device with hipGetSymbolAddress (with that device current) and
+// kept below, and only that address reaches the kernels.  The workspace
+// needs no clearing: every byte a call reads was written earlier in the same
+// call.  Calls that overlap on one GPU share the array and race.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mutex;
+std::map<int, void *> g_scratch;  // device -> address of its copy of `scratch`
+
+gdn_status scratch_address(void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GDN_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    auto it = g_scratch.find(dev);
+    if (it == g_scratch.end()) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return GDN_ERR_HIP;
+        it = g_scratch.emplace(dev, ptr).first;
+    }
+    *out = it->second;
+    return GDN_OK;
+}
+
+// gdn_fwd's launches in plan order, all on the caller's stream (no library
+// streams, events or graphs: nothing is created), with `scratch` as the
+// workspace.
+gdn_status noalloc_call(const gdn_fwd_params *p, hipStream_t s) {
+    if (!sizes_ok(p)) return GDN_ERR_INVALID_ARG;
+    gdn_fwd_params q = *p;
+    const size_t need = layout(&q, 1).total;
+    if (need > kScratchBytes) return GDN_ERR_WORKSPACE;  // beyond the array: refused before any device call
+    void *ws = nullptr;
+    gdn_status st = scratch_address(&ws);
+    if (st != GDN_OK) return st;
+    q.workspace = ws;
+    q.workspace_bytes = kScratchBytes;
+    st = validate(&q, nullptr, 1, (size_t)q.B * q.T, false);
+    if (st != GDN_OK) return st;
+    Plan plan;
+    st = make_plan(plan, &q, nullptr, false);
+    if (st != GDN_OK) return st;
+    st = set_attributes();
+    if (st != GDN_OK) return st;
+    // every launch waits for the ones before it on the one stream, which
+    // covers each cross-stream dependency of the plan (all preps come before
+    // every state launch, and those before every output launch)
+    for (const Op &op : plan.ops) {
+        if (op.kind != Op::LAUNCH) continue;
+        const Launch &L = plan.launches[op.event];
+        void *kargs[] = {const_cast<unsigned char *>(L.args)};
+        if (hipLaunchKernel(L.fn, L.grid, L.block, kargs, L.smem, s) != hipSuccess) return GDN_ERR_HIP;
+    }
+    return GDN_OK;
+}
+
 }  // namespace
 
 gdn_status gdn_internal::fwd_check(const gdn_fwd_params *p) {
@@ -585,6 +646,14 @@ size_t gdn_fwd_workspace_bytes(const gdn_fwd_params *p) {
 size_t gdn_fwd_bidir_workspace_bytes(const gdn_fwd_params *p) {
     if (!sizes_ok(p)) return 0;
     return layout(p, 2).total;
+}
+
+gdn_status gdn_fwd_noalloc(const gdn_fwd_params *p, struct ihipStream_t *stream) {
+    try {
+        return noalloc_call(p, stream);
+    } catch (...) {
+        return GDN_ERR_HIP;
+    }
 }
 
 gdn_status gdn_fwd(const gdn_fwd_params *p, struct ihipStream_t *stream) {

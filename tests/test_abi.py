@@ -34,7 +34,7 @@ def lib():
 
 def test_every_declared_function_is_exported_and_bound(lib):
     decl = declared_functions()
-    assert len(decl) == 24, decl
+    assert len(decl) == 25, decl
     assert set(decl) == set(gdn.EXPORTS)
     for name in decl:
         fn = getattr(lib, name)  # AttributeError if the library does not export it
@@ -412,3 +412,12 @@ def test_bwd_varlen_table_checks(lib):
     assert lib.gdn_bwd_varlen(ctypes.byref(p), None, None) == gdn.GDN_ERR_INVALID_ARG
 
 
+
+def test_noalloc_refuses_sizes_beyond_its_array(lib):
+    """gdn_fwd_noalloc's workspace is a fixed 64 MiB device array: larger
+    sizes are refused before any device call (so this runs without a GPU)."""
+    p = fake_params(lib, B=1, T=32760, H=12, D=128)
+    assert lib.gdn_fwd_workspace_bytes(ctypes.byref(p)) > (64 << 20)
+    assert lib.gdn_fwd_noalloc(ctypes.byref(p), None) == gdn.GDN_ERR_WORKSPACE
+    p.T = 0
+    assert lib.gdn_fwd_noalloc(ctypes.byref(p), None) == gdn.GDN_ERR_INVALID_ARG
