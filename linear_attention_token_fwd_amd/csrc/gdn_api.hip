@@ -2,6 +2,7 @@
 // argument validation, workspace carve-up and the launch sequence.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -398,12 +399,12 @@ gdn::StateArgs state_args(const gdn_fwd_params *p, const ScanBufs &sb, int c0, i
 
 template <class T, int D>
 gdn::OutArgs out_args(const gdn_fwd_params *p, int reverse, const ScanBufs &sb, int c0, int mode, float *acc,
-                      const int *cu) {
+                      const int *cu, int t_mid = 0) {
     gdn::OutArgs oa;
     memset(&oa, 0, sizeof(oa));  // padding too: the argument bytes key the graph cache
     oa.B = p->B; oa.T = p->T; oa.H = p->H; oa.NC = n_chunks(p->T); oa.reverse = reverse;
     oa.cu = cu;
-    oa.c_begin = c0; oa.mode = mode;
+    oa.c_begin = c0; oa.mode = mode; oa.t_mid = t_mid;
     oa.rec = sb.rec; oa.sc = sb.sc;
     oa.gate = p->gate; oa.norm_w = p->norm_w; oa.eps = p->eps_norm;
     oa.out = p->o; oa.acc = acc;
@@ -447,6 +448,86 @@ void plan_scan(Plan &plan, const gdn_fwd_params *p, int reverse, const ScanBufs 
     }
 }
 
+// The bidirectional variant: both scans co-scheduled.  The preps of the two
+// directions alternate on one stream (forward range 0, reversed range 0,
+// forward range 1, ...), so both chains start at once and advance together
+// on streams of their own.  The outputs are summed in fp32 and stored once:
+// with t_mid the forward scan's chunk boundary nearest the middle, each scan
+// is the first to reach one half of the tokens (forward: t < t_mid,
+// reversed: t >= t_mid) and writes its normalised output there to the fp32
+// accumulator; on the other half it adds the accumulator and stores y.  The
+// output launches run on one stream in an order that puts every writer of a
+// token after the first writer of that token:
+//   1. forward ranges before the middle, interleaved with the reversed ranges
+//      whose tokens all lie at or after t_mid;
+//   2. the reversed range (if any) that straddles t_mid;
+//   3. forward ranges from the middle on, interleaved with the remaining
+//      reversed ranges.
+// Each also waits for its own chain range.
+template <class T, int D>
+void plan_bidir(Plan &plan, const gdn_fwd_params *p, float *S_T_rev, const Layout &L) {
+    const int NC = n_chunks(p->T), R = n_ranges(NC), Tn = p->T;
+    const ScanBufs sb[2] = {scan_bufs(p, L, 0), scan_bufs(p, L, 1)};
+    float *S_T[2] = {p->S_T, S_T_rev};
+    float *acc = gdn_internal::at_offset<float>(p->workspace, L.acc);
+    const int chain_stream[2] = {0, 3}, prep_stream = 1, out_stream = 2;
+    const int i_mid = R / 2;
+    const int t_mid = std::min(Tn, range_begin(NC, R, i_mid) * gdn::kChunk);
+    const void *prep = reinterpret_cast<const void *>(&gdn::gdn_prep_kernel<T, D>);
+    const void *state = reinterpret_cast<const void *>(&gdn::gdn_state_kernel<T, D>);
+    const void *out = reinterpret_cast<const void *>(&gdn::gdn_out_kernel<T, D>);
+    std::vector<int> prep_done[2], state_done[2];
+    for (int d = 0; d < 2; ++d) {
+        prep_done[d].resize(R);
+        state_done[d].resize(R);
+    }
+    for (int i = 0; i < R; ++i) {
+        const int c0 = range_begin(NC, R, i), c1 = range_begin(NC, R, i + 1);
+        for (int d = 0; d < 2; ++d) {
+            plan.launch(prep_stream, "gdn_prep_kernel", prep, dim3(c1 - c0, p->H, p->B), dim3(gdn::kThreads),
+                        sizeof(gdn::PrepSmem<T, D>), prep_args<T, D>(p, d, sb[d], c0, nullptr));
+            prep_done[d][i] = plan.record(prep_stream);
+        }
+    }
+    const int used = p->B * p->H * (D / 16);
+    for (int d = 0; d < 2; ++d) {
+        for (int i = 0; i < R; ++i) {
+            const int c0 = range_begin(NC, R, i), c1 = range_begin(NC, R, i + 1);
+            const float *S_in = i == 0 ? p->S0 : sb[d].smid[(i - 1) & 1];
+            float *S_out = i == R - 1 ? nullptr : sb[d].smid[i & 1];
+            plan.wait(chain_stream[d], prep_done[d][i]);
+            plan.launch(chain_stream[d], "gdn_state_kernel", state, dim3((used + 7) / 8 * 8),
+                        dim3(gdn::StateCfg<T, D>::THREADS), state_lds<T, D>(),
+                        state_args<T, D>(p, sb[d], c0, c1, S_in, S_out, S_T[d], nullptr));
+            state_done[d][i] = plan.record(chain_stream[d]);
+        }
+    }
+    auto out_launch = [&](int d, int i) {
+        const int c0 = range_begin(NC, R, i), c1 = range_begin(NC, R, i + 1);
+        plan.wait(out_stream, state_done[d][i]);
+        plan.launch(out_stream, "gdn_out_kernel", out, dim3(c1 - c0, p->H, p->B), dim3(gdn::kThreads),
+                    sizeof(gdn::OutSmem<T, D>), out_args<T, D>(p, d, sb[d], c0, 1, acc, nullptr, t_mid));
+    };
+    // reversed range j covers sequence positions [T - 64 c1, T - 64 c0)
+    std::vector<int> rev_first, rev_mixed, rev_second;
+    for (int j = 0; j < R; ++j) {
+        const long long lo = (long long)Tn - (long long)gdn::kChunk * range_begin(NC, R, j + 1);
+        const long long hi = (long long)Tn - (long long)gdn::kChunk * range_begin(NC, R, j);
+        if (lo >= t_mid) rev_first.push_back(j);
+        else if (hi <= t_mid) rev_second.push_back(j);
+        else rev_mixed.push_back(j);
+    }
+    for (size_t k = 0; k < (size_t)std::max(i_mid, (int)rev_first.size()); ++k) {
+        if ((int)k < i_mid) out_launch(0, (int)k);
+        if (k < rev_first.size()) out_launch(1, rev_first[k]);
+    }
+    for (int j : rev_mixed) out_launch(1, j);
+    for (size_t k = 0; k < (size_t)std::max(R - i_mid, (int)rev_second.size()); ++k) {
+        if (i_mid + (int)k < R) out_launch(0, i_mid + (int)k);
+        if (k < rev_second.size()) out_launch(1, rev_second[k]);
+    }
+}
+
 template <class T, int D>
 gdn_status plan_fwd(Plan &plan, const gdn_fwd_params *p, float *S_T_rev, bool bidir, const int *cu) {
     const Layout L = layout(p, bidir ? 2 : 1, cu != nullptr);
@@ -455,13 +536,7 @@ gdn_status plan_fwd(Plan &plan, const gdn_fwd_params *p, float *S_T_rev, bool bi
     if (!bidir) {
         plan_scan<T, D>(plan, p, p->reverse, scan_bufs(p, L, 0), p->S_T, 1, 0, 2, 0, nullptr, cu);
     } else {
-        // the two directions are independent: forward chain on stream 0,
-        // reversed chain on stream 3, all preps on stream 1; the outputs run
-        // on stream 2, the reversed scan's after all of the forward scan's
-        // (they add into its fp32 sum)
-        float *acc = gdn_internal::at_offset<float>(p->workspace, L.acc);
-        plan_scan<T, D>(plan, p, 0, scan_bufs(p, L, 0), p->S_T, 1, 0, 2, 1, acc, cu);
-        plan_scan<T, D>(plan, p, 1, scan_bufs(p, L, 1), S_T_rev, 1, 3, 2, 2, acc, cu);
+        plan_bidir<T, D>(plan, p, S_T_rev, L);
     }
     for (int s = 1; s < kStreams; ++s) plan.wait(0, plan.record(s));
     return GDN_OK;

@@ -105,14 +105,19 @@ struct OutArgs {
     int B, T, H, NC, reverse;
     const int *cu;      // sequence table [B + 1] or null
     int c_begin;        // chunk = c_begin + blockIdx.x
-    int mode;           // 0: write y; 1: write this scan's y to acc (fp32); 2: y = acc + this scan's y
+    int mode;           // 0: write y; 1: bidirectional sum (below)
+    // mode 1: the token rows this scan reaches before the other scan does
+    // (sequence position t < t_mid for the forward scan, t >= t_mid for the
+    // reversed one) write this scan's output to acc (fp32); the others add
+    // acc, which the other scan has written, and store y
+    int t_mid;
     const void *rec;    // chunk records (QP, O0)
     const void *sc;     // chunk-entry states
     const void *gate;
     const float *norm_w;  // [H][D] or null
     float eps;
-    void *out;          // y [B][T][H][D] (modes 0, 2)
-    float *acc;         // [B][T][H][D] fp32 (modes 1, 2)
+    void *out;          // y [B][T][H][D]
+    float *acc;         // [B][T][H][D] fp32 (mode 1)
 };
 
 // 8 consecutive values as float
@@ -1012,6 +1017,7 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_out_kernel(OutArgs a) {
     constexpr int PASSES = 64 / TPP;
     const int cg = tid % G;
     size_t roff[PASSES];
+    bool first[PASSES];  // mode 1: this scan reaches the row first (writes acc)
     float gv[PASSES][8], prev[PASSES][8];
 #pragma unroll
     for (int pass = 0; pass < PASSES; ++pass) {
@@ -1020,7 +1026,8 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_out_kernel(OutArgs a) {
         const int t = a.reverse ? sq.len - 1 - sc_ : sc_;
         roff[pass] = (((size_t)sq.off + t) * a.H + h) * D + 8 * cg;
         load8_nt(static_cast<const T *>(a.gate) + roff[pass], gv[pass]);
-        if (a.mode == 2) load8_nt(a.acc + roff[pass], prev[pass]);
+        first[pass] = a.reverse ? t >= a.t_mid : t < a.t_mid;
+        if (a.mode == 1 && !first[pass]) load8_nt(a.acc + roff[pass], prev[pass]);
     }
     float wv[8];  // norm weights (4-byte aligned)
     if (a.norm_w) {
@@ -1064,10 +1071,10 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_out_kernel(OutArgs a) {
         float y[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) y[i] = ov[i] * inv * wv[i] * silu(gv[pass][i]);
-        if (a.mode == 1) {
+        if (a.mode == 1 && first[pass]) {
             store8_nt(a.acc + off, y);
         } else {
-            if (a.mode == 2) {
+            if (a.mode == 1) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) y[i] += prev[pass][i];
             }

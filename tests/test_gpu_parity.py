@@ -257,3 +257,15 @@ def test_varlen_multi_range(reverse):
         check(f"S_T[{i}]", s[i:i + 1], rs, "bf16")
         y1, s1 = run_gpu(seq, "bf16", reverse=reverse)
         assert np.array_equal(ys, y1) and np.array_equal(s[i:i + 1], s1), f"sequence {i} differs from gdn_fwd alone"
+
+
+@pytest.mark.parametrize("T,B", [(1, 1), (64, 1), (100, 2), (64 * 9, 1), (64 * 9 + 24, 2), (64 * 300 + 24, 1),
+                                 (64 * 520 + 5, 1)])
+def test_bidir_shapes(T, B):
+    """The bidirectional variant (both scans co-scheduled, outputs summed in
+    fp32 and stored once, each scan writing the accumulator on the half of
+    the tokens it reaches first): one chunk range and several, lengths that
+    are and are not multiples of 64 (the two scans' chunk boundaries differ),
+    a batch of two."""
+    w = W[4]
+    compare_workload(w, T=T, H=2, B=B)
