@@ -8,13 +8,20 @@ d=128, bf16 I/O with an fp32 state, seeded synthetic inputs already resident
 in device memory.
 
 Prints ONE JSON line on stdout.  Beside the headline tokens/s it reports:
-  roofline     -- the dominant kernel's algorithmic bytes per launch over its
-                  average duration (HIP events recorded on the launch stream
-                  around each kernel, live in this run) against the MI355X
-                  HBM peak of 8 TB/s;
-  layer        -- the whole call against the layer's algorithmic HBM floor of
-                  1288 B per token-head (q, k, v, gate in, y out in bf16, plus
-                  fp32 log a and b);
+  roofline     -- the dominant kernel (largest summed time per call) on the
+                  layer's per-unit basis: 1288 B per token-head (q, k, v,
+                  gate in and y out in bf16, plus fp32 log a and b) times the
+                  token-heads one launch covers, over that kernel's average
+                  launch duration (HIP events recorded on the launch stream
+                  around each kernel, live in this run), against the MI355X
+                  HBM peak of 8 TB/s; `traffic` is the kernel's measured HBM
+                  bytes per launch (copy-calibrated FETCH_SIZE + WRITE_SIZE
+                  from the committed rocprofv3 summary, null when that
+                  summary was taken on other kernel sources);
+  layer        -- the whole call against the same floor (1288 B per
+                  token-head; a bidirectional call reads its inputs and
+                  writes y once at best, so the same floor), and the measured
+                  traffic of the whole call over those algorithmic bytes;
   cpu_baseline -- the fp64 oracle (the test yardstick) timed on this host's
                   cores on the same workload, and the parity of the last timed
                   GPU output against it.
@@ -253,34 +260,44 @@ def main() -> int:
     launches_per_call = {nm: names.count(nm) for nm in set(names)}
     es = 2 if w.dtype == "bf16" else 4
     kernels = {}
-    token_heads = B * T * H * (2 if w.bidirectional else 1)
+    token_heads = B * T * H * (2 if w.bidirectional else 1)   # per direction scanned
+    tag = f"T{T}_H{H}_d{D}_{w.dtype}" + ("_bidir" if w.bidirectional else "") + (f"_B{B}" if B > 1 else "")
     for nm in per_launch:
         per_launch_ms = float(np.mean(per_launch[nm]))
         call_ms = float(np.mean(per_call[nm]))
-        bytes_per_call = kernel_bytes_per_token_head(D, es)[nm] * token_heads
+        own_bytes = kernel_bytes_per_token_head(D, es)[nm] * token_heads
         if nm == "gdn_out_kernel" and w.bidirectional:  # + fp32 accumulator write and read
-            bytes_per_call += 2 * 4 * D * B * T * H
+            own_bytes += 2 * 4 * D * B * T * H
         kernels[nm] = {"launches_per_call": launches_per_call[nm], "avg_ms": per_launch_ms,
-                       "ms_per_call": call_ms, "bytes_per_launch": bytes_per_call / launches_per_call[nm],
-                       "GBps": bytes_per_call / (call_ms * 1e-3) / 1e9}
+                       "ms_per_call": call_ms, "own_io_bytes_per_launch": own_bytes / launches_per_call[nm],
+                       "own_io_GBps": own_bytes / (call_ms * 1e-3) / 1e9,
+                       "traffic_per_launch": profiled_traffic(nm, f"gdn_kernels_{tag}")}
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_call"])
     kd = kernels[dom]
-    tag = f"T{T}_H{H}_d{D}_{w.dtype}" + ("_bidir" if w.bidirectional else "") + (f"_B{B}" if B > 1 else "")
-    traffic = profiled_traffic(dom, f"gdn_kernels_{tag}")
-    achieved = kd["bytes_per_launch"] / (kd["avg_ms"] * 1e-3) / 1e9  # algorithmic bytes per launch / avg launch
+    # the layer's per-unit figure times the token-heads one launch of the dominant kernel covers
+    unit_bytes = layer_bytes_per_token_head(D, es)
+    alg_per_launch = unit_bytes * token_heads / kd["launches_per_call"]
+    achieved = alg_per_launch / (kd["avg_ms"] * 1e-3) / 1e9
+    traffic = kd["traffic_per_launch"]
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": None if traffic is None else round(traffic),
+                "traffic_over_algorithmic": None if traffic is None else round(traffic / alg_per_launch, 3),
+                "algorithmic_bytes_per_launch": round(alg_per_launch),
+                "token_heads_per_launch": token_heads // kd["launches_per_call"],
                 "avg_launch_ms": round(kd["avg_ms"], 5)}
-    call_ms = ms_per_step
-    # bidirectional: two whole passes, plus the second pass reading the first one's output
-    lb = 2 * layer_bytes_per_token_head(D, es) + D * es if w.bidirectional else layer_bytes_per_token_head(D, es)
-    layer_bytes = lb * B * T * H
+    # the whole call: one read of the inputs and one write of y per token-head, either direction count
+    layer_bytes = unit_bytes * B * T * H
+    call_traffic = None
+    if all(k["traffic_per_launch"] is not None for k in kernels.values()):
+        call_traffic = sum(k["traffic_per_launch"] * k["launches_per_call"] for k in kernels.values())
     layer = {"algorithmic_bytes": layer_bytes, "floor_ms": layer_bytes / (HBM_PEAK_GBS * 1e9) * 1e3,
-             "frac_of_hbm_roofline": round(layer_bytes / (HBM_PEAK_GBS * 1e9) * 1e3 / ms_per_step, 4)}
+             "frac_of_hbm_roofline": round(layer_bytes / (HBM_PEAK_GBS * 1e9) * 1e3 / ms_per_step, 4),
+             "traffic_per_call": None if call_traffic is None else round(call_traffic),
+             "traffic_over_algorithmic": None if call_traffic is None else round(call_traffic / layer_bytes, 3)}
     for nm, k in kernels.items():
         log(f"  {nm}: {k['avg_ms']:.4f} ms/launch x{k['launches_per_call']} = {k['ms_per_call']:.4f} ms/call, "
-            f"{k['GBps']:.0f} GB/s")
+            f"own I/O {k['own_io_GBps']:.0f} GB/s")
 
     # ---- CPU baseline: the fp64 oracle on this host, same workload
     cpu = None
