@@ -796,12 +796,12 @@ template <class T, int D> struct StateOps {
 // chunks [c_begin, c_end).  Compute wave w keeps S^T rows w KQ .. (w+1) KQ - 1
 // (fp32, in registers) and, per chunk:
 //   A: stores its rows of the chunk-entry state for the output kernel, and
-//      forms its partial -W[:, rows] S^T[rows] for all 4 token tiles (U~
-//      entering the partial of the tiles it reduces), publishing the other
-//      waves' tiles in LDS;                                      barrier;
-//   B: sums the partials of its token tiles into U, stored as bf16/fp32
-//      B fragments in LDS;                                       barrier;
-//   C: S^T[rows] <- e^{g_C} S^T[rows] + (D K)^T[rows] U.
+//      forms its partial -W[:, rows] S^T[rows] for all 4 token tiles,
+//      publishing them in LDS;                                   barrier;
+//   B: adds U~ and the partials of its token tiles into U, stored as
+//      bf16/fp32 B fragments in LDS;                             barrier;
+//   C: S^T[rows] <- e^{g_C} S^T[rows] + (D K)^T[rows] U (the decay applied
+//      in phase A).
 // Its operand fragments come straight from the chunk records in HBM into
 // registers, NB chunks ahead (four register sets used in turn; a set's -W
 // and U~ are reloaded right after phase A has used them, before the first
@@ -871,26 +871,13 @@ __global__ __launch_bounds__((StateCfg<T, D>::THREADS)) void gdn_state_kernel(St
         S[mt] = a.S_in ? *reinterpret_cast<const floatx4 *>(a.S_in + (bh * D + vcol) * D + row0 + 16 * mt + 4 * g) : zero4();
     T *sc_base = static_cast<T *>(a.sc) + (bh * a.NC * NV + vb) * (size_t)ScLayout<T, D>::PER_VB;
 
-    // U~ of the tiles this wave reduces starts their partials; the others start
-    // at zero.  bf16: through the matrix unit as I16 U~ (exact in fp32), with
-    // an identity or zero A operand per tile; fp32: U~ times 1 or 0.
-    typename K16<T>::frag ident[4];
-    float own[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-        own[tt] = tt / TPW == w ? 1.f : 0.f;
-        if constexpr (sizeof(T) == 2) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ident[tt][i] = (T)(n == 4 * g + i ? own[tt] : 0.f);
-        }
-    }
-
     const int last = c_end - 1;
 #pragma unroll
     for (int j = 0; j < C::NB; ++j) load_ops(ops[j], min(a.c_begin + j, last));
     lds_barrier();  // e^{g_C} staged
 
     auto step = [&](Ops &o, int c) {
+        const float gc = sm.gcs[c - a.c_begin];
         // ---- A: entry state out, partial U
         frag sB[KBQ];
 #pragma unroll
@@ -900,6 +887,10 @@ __global__ __launch_bounds__((StateCfg<T, D>::THREADS)) void gdn_state_kernel(St
                 const int e = kb * KPL + j;
                 fset(sB[kb], j, S[e >> 2][e & 3]);
             }
+        // the decay of the update, applied while the entry state is at hand
+        // (off the path from the second barrier to the next chunk)
+#pragma unroll
+        for (int mt = 0; mt < MQ; ++mt) S[mt] *= gc;
         T *scp = sc_base + (size_t)c * NV * ScLayout<T, D>::PER_VB;
 #pragma unroll
         for (int kb = 0; kb < KBQ; ++kb)
@@ -907,24 +898,25 @@ __global__ __launch_bounds__((StateCfg<T, D>::THREADS)) void gdn_state_kernel(St
         floatx4 up[4];
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-            if constexpr (sizeof(T) == 2)
-                up[tt] = K16<T>::mma(ident[tt], o.ut[tt % TPW], zero4());
-            else
-                up[tt] = Vec4<T>::widen(o.ut[tt % TPW]) * own[tt];
+            up[tt] = zero4();
 #pragma unroll
             for (int kb = 0; kb < KBQ; ++kb) up[tt] = M::mma(o.wf[tt][kb], sB[kb], up[tt]);
             sm.part[w][tt][lane] = up[tt];
         }
+        // U~ of this wave's token tiles, widened before its registers are reloaded
+        floatx4 uw[TPW];
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) uw[j] = Vec4<T>::widen(o.ut[j]);
         // this register set's -W and U~ now take chunk c + NB (issued before the barrier wait)
         load_w(o, min(c + C::NB, last));
         lds_barrier();
-        // ---- B: U for this wave's token tiles (every wave's partial, its own included)
+        // ---- B: U for this wave's token tiles: U~ plus every wave's partial
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
             const int tt = w * TPW + j;
-            floatx4 u = sm.part[0][tt][lane];
+            floatx4 u = uw[j];
 #pragma unroll
-            for (int w2 = 1; w2 < C::NW; ++w2) u += sm.part[w2][tt][lane];
+            for (int w2 = 0; w2 < C::NW; ++w2) u += sm.part[w2][tt][lane];
             store4(&sm.ub[lane * 16 + 4 * tt], u);
         }
         lds_barrier();
@@ -932,30 +924,23 @@ __global__ __launch_bounds__((StateCfg<T, D>::THREADS)) void gdn_state_kernel(St
         frag uB[KBC];
 #pragma unroll
         for (int kb = 0; kb < KBC; ++kb) uB[kb] = *reinterpret_cast<const frag *>(&sm.ub[lane * 16 + kb * KPL]);
-        const float gc = sm.gcs[c - a.c_begin];
 #pragma unroll
-        for (int mt = 0; mt < MQ; ++mt) {
-            S[mt] *= gc;
+        for (int mt = 0; mt < MQ; ++mt)
 #pragma unroll
             for (int kb = 0; kb < KBC; ++kb) S[mt] = M::mma(o.dkf[mt][kb], uB[kb], S[mt]);
-        }
         // and its (D K)^T (past the range: the last chunk again, unused)
         load_dk(o, min(c + C::NB, last));
     };
     // whole groups of NB chunks (one back edge, so the loads in flight at the
     // top of the loop are the same on every entry), then the rest
-    static_assert(C::NB == 4, "the loop below is written for four register sets");
     const int n_ch = c_end - a.c_begin, full = n_ch / C::NB * C::NB;
     for (int c = a.c_begin; c < a.c_begin + full; c += C::NB) {
-        step(ops[0], c);
-        step(ops[1], c + 1);
-        step(ops[2], c + 2);
-        step(ops[3], c + 3);
+#pragma unroll
+        for (int j = 0; j < C::NB; ++j) step(ops[j], c + j);
     }
-    const int rest = n_ch - full;
-    if (rest > 0) step(ops[0], a.c_begin + full);
-    if (rest > 1) step(ops[1], a.c_begin + full + 1);
-    if (rest > 2) step(ops[2], a.c_begin + full + 2);
+#pragma unroll
+    for (int j = 0; j < C::NB - 1; ++j)
+        if (full + j < n_ch) step(ops[j], a.c_begin + full + j);
     // the sequence's final state if it ends in this range, else the hand-off
     float *S_dst = c_end == nc_seq ? a.S_T : a.S_out;
     if (S_dst) {

@@ -72,6 +72,25 @@ def test_f32_d128_full_length():
     compare_workload(F32_D128)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("T", [65, 128, 192, 64 * 129 + 5, 64 * 257])
+def test_chunk_count_shapes(D, T):
+    """bf16 chunk counts that exercise the state chain's loop (register sets
+    used in turn) and its range hand-over: 2 chunks with a 1-token second
+    chunk (65), 2 and 3 full chunks (128, 192), two ranges (130 chunks),
+    three ranges (257 chunks); two heads, a random initial state, forward and
+    reversed."""
+    w = gdn_inputs.Workload(93, f"bf16 d{D}", 1, T, 2, D, "bf16")
+    for reverse in (False, True):
+        inp = gdn_inputs.generate(w, seed=500 + T + D)
+        inp["S0"] = (0.05 * np.random.default_rng(T).standard_normal((1, 2, D, D))).astype(np.float32)
+        say(f"case: chunk counts T={T} D={D} reverse={reverse}")
+        y, s = run_gpu(inp, "bf16", reverse=reverse)
+        ry, rs, _ = oracle.inputs_for(inp, reverse=reverse)
+        check("y", y, ry, "bf16")
+        check("S_T", s, rs, "bf16")
+
+
 @pytest.mark.parametrize("wid", [0, 1])
 def test_reverse_scan(wid):
     compare_workload(W[wid], T=64 * 3 + 5, H=2, reverse=True)
