@@ -72,6 +72,16 @@ def test_f32_d128_full_length():
     compare_workload(F32_D128)
 
 
+@pytest.mark.parametrize("dtype,D", [("f32", 64), ("f32", 128), ("bf16", 64)])
+@pytest.mark.parametrize("T", [64 * 5 + 37, 64 * 140 + 11])
+def test_bidir_dtypes(dtype, D, T):
+    """The bidirectional plan with the other operand types and head sizes
+    (one range, and two ranges of 70 and 71 chunks), two heads, a random
+    initial state shared by both directions."""
+    w = gdn_inputs.Workload(94, f"bidir {dtype} d{D}", 1, T, 2, D, dtype, has_S0=True, bidirectional=True)
+    compare_workload(w, seed=700 + T + D)
+
+
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("T", [65, 128, 192, 64 * 129 + 5, 64 * 257])
 def test_chunk_count_shapes(D, T):
