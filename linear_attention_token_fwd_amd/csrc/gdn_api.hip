@@ -326,16 +326,20 @@ gdn_status run_plan(const Plan &plan, hipStream_t caller, hipEvent_t *timing, bo
     return enqueue_ops(plan, streams, r, timing);
 }
 
-// Chunk ranges of a scan: ~128 chunks each, at most 16 ranges unless a range
-// would exceed the state kernel's limit.  Measured at T = 32760 (512 chunks),
-// H = 12, d = 128: ranges of 32 / 64 / 96 / 128 / 192 chunks take 0.765 /
-// 0.696 / 0.683 / 0.677 / 0.663 ms per call; 192 is slower than 128 at
-// T = 75600 (1.482 against 1.467 ms) and at H = 24 (0.912 against 0.901).
-// Each chain launch pays for filling its operand registers and for the
-// hand-over of the state; the first prep range and the last output range run
-// alone.
-int n_ranges(int NC) {
-    int R = (NC + 127) / 128;
+// Chunk ranges of a scan: R = ceil(NC / target) ranges of equal size, at
+// most 16 unless a range would exceed the state kernel's limit.  Each chain
+// launch pays for filling its operand registers and for the hand-over of the
+// state, and the first prep range and the last output range run alone.
+// Measured (MI355X, H = 12, d = 128), one scan with the launch graph
+// replayed: T = 32760 (512 chunks) 4 ranges of 128 0.622 ms, 3 of 171 0.625,
+// 2 of 256 0.633; T = 75600 (1182 chunks) ranges of 128 1.367-1.374 ms, of
+// 169 1.344-1.352, of 197 1.384; T = 27280 with H = 24: 4 or 3 ranges 0.804.
+// Both scans co-scheduled (launched directly), T = 126360 (1975 chunks):
+// ranges of 123 4.60 ms, 165 4.45, 200 4.35, 247 4.30, 330 4.25, 395 4.25.
+constexpr int kRangeTarget = 170;       // one scan
+constexpr int kRangeTargetBidir = 400;  // both scans co-scheduled
+int n_ranges(int NC, int target = kRangeTarget) {
+    int R = (NC + target - 1) / target;
     R = R < 1 ? 1 : (R > 16 ? 16 : R);
     const int need = (NC + gdn::kStateMaxRange - 1) / gdn::kStateMaxRange;
     return R < need ? need : R;
@@ -466,7 +470,7 @@ void plan_scan(Plan &plan, const gdn_fwd_params *p, int reverse, const ScanBufs 
 // Each also waits for its own chain range.
 template <class T, int D>
 void plan_bidir(Plan &plan, const gdn_fwd_params *p, float *S_T_rev, const Layout &L) {
-    const int NC = n_chunks(p->T), R = n_ranges(NC), Tn = p->T;
+    const int NC = n_chunks(p->T), R = n_ranges(NC, kRangeTargetBidir), Tn = p->T;
     const ScanBufs sb[2] = {scan_bufs(p, L, 0), scan_bufs(p, L, 1)};
     float *S_T[2] = {p->S_T, S_T_rev};
     float *acc = gdn_internal::at_offset<float>(p->workspace, L.acc);

@@ -83,12 +83,12 @@ def test_bidir_dtypes(dtype, D, T):
 
 
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("T", [65, 128, 192, 64 * 129 + 5, 64 * 257])
+@pytest.mark.parametrize("T", [65, 128, 192, 64 * 199 + 5, 64 * 345])
 def test_chunk_count_shapes(D, T):
     """bf16 chunk counts that exercise the state chain's loop (register sets
     used in turn) and its range hand-over: 2 chunks with a 1-token second
-    chunk (65), 2 and 3 full chunks (128, 192), two ranges (130 chunks),
-    three ranges (257 chunks); two heads, a random initial state, forward and
+    chunk (65), 2 and 3 full chunks (128, 192), two ranges (200 chunks),
+    three ranges (345 chunks); two heads, a random initial state, forward and
     reversed."""
     w = gdn_inputs.Workload(93, f"bf16 d{D}", 1, T, 2, D, "bf16")
     for reverse in (False, True):
@@ -240,14 +240,15 @@ def test_varlen_long_and_short():
         check(f"S_T[{i}]", s[i:i + 1], rs, "bf16")
 
 
-MULTI_RANGE_LENGTHS = [20000, 37, 9000, 64]
+MULTI_RANGE_LENGTHS = [30000, 37, 12000, 64]
 
 
 @pytest.mark.parametrize("reverse", [False, True])
 def test_varlen_multi_range(reverse):
     """A variable-length batch whose longest sequence spans several chunk
     ranges of the launch plan while the others end inside the first and the
-    second range: lengths 20000, 37, 9000 and 64 at the model's shape
+    second range: lengths 30000 (3 ranges of about 156 chunks), 37, 12000
+    (ends in the second range) and 64 at the model's shape
     (H = 12, d = 128, bf16), as in a batch of two videos of different lengths
     with two short prompts.  Each sequence against the oracle on that
     sequence alone, and bit-identical to gdn_fwd on it alone (the final state
