@@ -328,21 +328,35 @@ __device__ __forceinline__ void conv_silu_norm(const PrepArgs &a, const Raw8<T> 
 // Short conv + SiLU (+ L2 normalisation for q and k) of the chunk's 64 scan
 // positions into LDS.  Thread layout: G = D/8 threads per token row (8
 // channels each); each thread owns RUN consecutive tokens and loads its
-// RUN + 3 input rows (3 rows of causal history) once.  The head's conv
-// weights are copied straight into LDS (the A storage, unused until A is
-// formed), so every load of the prologue is in flight at once; `mid` runs
-// after the loads are issued and must end with a barrier that follows a
-// wait for them (the weights are read from LDS afterwards).
-template <class T, int D, class Mid>
+// RUN + 3 input rows (3 rows of causal history) once.  Every load of the
+// prologue is in flight at once, in this order: the gates (`issue`, wave 0),
+// the head's conv weights (copied straight into LDS, into the A storage,
+// unused until A is formed), then the raw rows of q, then k, then v.  A
+// counted wait then covers the gates and the weight copies only (the RAW_LOADS
+// row loads issued after them may still be in flight; the compiler's own
+// waits would cover everything, since LDS copies and register loads pending
+// together make it wait for zero), `mid` runs, and after the barrier the conv
+// of q can start while the rows of k and v arrive.
+template <class T, int D> struct PrologueShape {
+    static constexpr int G = D / 8;
+    static constexpr int RUN = 64 / (kThreads / G);
+    static constexpr int ROWS = RUN + 3;
+    // vector memory instructions per thread for the raw rows (Raw8::load: one
+    // 16-byte load for bf16, two for fp32)
+    static constexpr int RAW_LOADS = 3 * ROWS * (sizeof(T) == 2 ? 1 : 2);
+    static_assert(RAW_LOADS <= 63, "the counted wait below needs the row loads within the vmcnt range");
+};
+template <class T, int D, class Issue, class Mid>
 __device__ __forceinline__ void prologue(const PrepArgs &a, PrepSmem<T, D> &sm, unsigned char *smem, int c, int h,
-                                         SeqSpan sq, Mid mid) {
-    constexpr int G = D / 8;
-    constexpr int RUN = 64 / (kThreads / G);
-    constexpr int ROWS = RUN + 3;
+                                         SeqSpan sq, Issue issue, Mid mid) {
+    typedef PrologueShape<T, D> PS;
+    constexpr int G = PS::G, RUN = PS::RUN, ROWS = PS::ROWS;
     const int tid = threadIdx.x, cg = tid % G, run = tid / G;
     const int s0 = c * 64 + run * RUN;
     const T *src[3] = {static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v)};
     T *dst[3] = {sm.Qs, sm.Ks, sm.Vs};
+    issue();
+    __builtin_amdgcn_sched_barrier(0);
     // weights [3][D][4] fp32: 1 KB units of 64 channels, 16 B per lane
     float4 *wlds = reinterpret_cast<float4 *>(sm.Am);
     {
@@ -357,19 +371,28 @@ __device__ __forceinline__ void prologue(const PrepArgs &a, PrepSmem<T, D> &sm, 
                                              16, 0, 0);
         }
     }
+    __builtin_amdgcn_sched_barrier(0);
     Raw8<T> raw[3][ROWS];
     bool rv[ROWS];
+    size_t off[ROWS];
 #pragma unroll
     for (int rr = 0; rr < ROWS; ++rr) {
         const int sp = s0 - 3 + rr;
         rv[rr] = sp >= 0 && sp < sq.len;
         int si = a.reverse ? sq.len - 1 - sp : sp;
         si = si < 0 ? 0 : (si >= sq.len ? sq.len - 1 : si);
-        const size_t off = (((size_t)sq.off + si) * a.H + h) * D + 8 * cg;
-#pragma unroll
-        for (int x = 0; x < 3; ++x) raw[x][rr].load(src[x] + off);
+        off[rr] = (((size_t)sq.off + si) * a.H + h) * D + 8 * cg;
     }
+#pragma unroll
+    for (int x = 0; x < 3; ++x)
+#pragma unroll
+        for (int rr = 0; rr < ROWS; ++rr) raw[x][rr].load(src[x] + off[rr]);
+    __builtin_amdgcn_sched_barrier(0);
+    // the gates and the weight copies (issued before the RAW_LOADS row loads)
+    // have landed; the rows may still be in flight
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(PS::RAW_LOADS));
     mid();
+    lds_barrier();
     // chunks away from both ends of the sequence need no masking
     if (c > 0 && (c + 1) * 64 <= sq.len)
         conv_silu_norm<T, D, false>(a, raw, rv, wlds, dst, s0, cg, run, sq.len);
@@ -397,15 +420,20 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_prep_kernel(PrepArgs a) {
     if (c * 64 >= sq.len) return;  // past this sequence's end (variable lengths)
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, n = lane % 16, g = lane / 16;
 
-    // ---- gates (b and the cumulative log decay g inside the chunk), loaded
-    // after the prologue's loads are issued
-    auto gates = [&] {
+    // ---- gates (b and the cumulative log decay g inside the chunk): loaded
+    // first, scanned once the prologue's other loads are issued
+    float la = 0.f, be = 0.f;
+    auto gates_issue = [&] {
         if (tid < 64) {
             const int s = c * 64 + tid;
             const bool valid = s < sq.len;
             const int src = a.reverse ? sq.len - 1 - s : s;
-            float la = valid ? a.log_a[((size_t)sq.off + src) * a.H + h] : 0.f;
-            float be = valid ? a.beta[((size_t)sq.off + src) * a.H + h] : 0.f;
+            la = valid ? a.log_a[((size_t)sq.off + src) * a.H + h] : 0.f;
+            be = valid ? a.beta[((size_t)sq.off + src) * a.H + h] : 0.f;
+        }
+    };
+    auto gates = [&] {
+        if (tid < 64) {
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 float y = __shfl_up(la, off, 64);
@@ -416,10 +444,8 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_prep_kernel(PrepArgs a) {
             sm.eg[tid] = expf(la);
             sm.dk[tid] = expf(__shfl(la, 63, 64) - la);
         }
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's weight copies have landed
-        __syncthreads();
     };
-    prologue<T, D>(a, sm, smem_raw, c, h, sq, gates);
+    prologue<T, D>(a, sm, smem_raw, c, h, sq, gates_issue, gates);
     __syncthreads();
 
     // ---- A = strictly lower (b_i e^{g_i - g_j} k_i . k_j), rows 16w.. of this wave
