@@ -1010,8 +1010,10 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_out_kernel(OutArgs a) {
         constexpr int UNITS = SL::PER_CHUNK * (int)sizeof(T) / 1024;
         static_assert(UNITS % kWaves == 0, "state staging units per wave");
 #pragma unroll
-        for (int u = w; u < UNITS; u += kWaves)
+        for (int j = 0; j < UNITS / kWaves; ++j) {
+            const int u = w + j * kWaves;
             __builtin_amdgcn_global_load_lds(src + u * 1024 + lane * 16, smem_raw + u * 1024, 16, 0, 0);
+        }
     }
     const T *rec = static_cast<const T *>(a.rec) + (bh * a.NC + c) * (size_t)Rec<D>::SIZE;
     frag qp[KBD];
