@@ -161,6 +161,14 @@ struct Plan {
         ops.push_back(Op{Op::LAUNCH, stream, (int)launches.size()});
         launches.push_back(L);
     }
+    void launch_ext(int stream, const gdn_internal::ExtLaunch &e) {
+        Launch L = {};
+        L.fn = e.fn; L.grid = e.grid; L.block = e.block; L.smem = e.smem; L.name = e.name;
+        static_assert(sizeof(e.args) == sizeof(L.args), "argument buffers");
+        memcpy(L.args, e.args, sizeof(L.args));
+        ops.push_back(Op{Op::LAUNCH, stream, (int)launches.size()});
+        launches.push_back(L);
+    }
     int record(int stream) {
         ops.push_back(Op{Op::RECORD, stream, n_events});
         return n_events++;
@@ -415,13 +423,21 @@ gdn::OutArgs out_args(const gdn_fwd_params *p, int reverse, const ScanBufs &sb, 
     return oa;
 }
 
+// Launches woven into a scan's plan (see fwd_call_staged), or none.
+struct Staged {
+    const std::vector<std::vector<gdn_internal::ExtLaunch>> *post = nullptr;
+    int stream = 3;
+};
+
 // One scan's range-pipelined launches: preps on `prep_stream`, the state
 // chain on `state_stream` (range i waits for prep i), and the output of each
 // range on `out_stream` (waits for state i).  out_mode: see OutArgs.  cu: the
 // device copy of the sequence table of a variable-length batch, or null.
+// staged: launches on staged.stream, post[i] after output i (waiting for it).
 template <class T, int D>
 void plan_scan(Plan &plan, const gdn_fwd_params *p, int reverse, const ScanBufs &sb, float *S_T, int prep_stream,
-               int state_stream, int out_stream, int out_mode, float *acc, const int *cu) {
+               int state_stream, int out_stream, int out_mode, float *acc, const int *cu,
+               const Staged &staged = Staged()) {
     const int NC = n_chunks(p->T), R = n_ranges(NC);
     const void *prep = reinterpret_cast<const void *>(&gdn::gdn_prep_kernel<T, D>);
     const void *state = reinterpret_cast<const void *>(&gdn::gdn_state_kernel<T, D>);
@@ -449,6 +465,10 @@ void plan_scan(Plan &plan, const gdn_fwd_params *p, int reverse, const ScanBufs 
         plan.wait(out_stream, state_done[i]);
         plan.launch(out_stream, "gdn_out_kernel", out, dim3(c1 - c0, p->H, p->B), dim3(gdn::kThreads),
                     sizeof(gdn::OutSmem<T, D>), out_args<T, D>(p, reverse, sb, c0, out_mode, acc, cu));
+        if (staged.post) {
+            plan.wait(staged.stream, plan.record(out_stream));
+            for (const gdn_internal::ExtLaunch &e : (*staged.post)[i]) plan.launch_ext(staged.stream, e);
+        }
     }
 }
 
@@ -533,12 +553,13 @@ void plan_bidir(Plan &plan, const gdn_fwd_params *p, float *S_T_rev, const Layou
 }
 
 template <class T, int D>
-gdn_status plan_fwd(Plan &plan, const gdn_fwd_params *p, float *S_T_rev, bool bidir, const int *cu) {
+gdn_status plan_fwd(Plan &plan, const gdn_fwd_params *p, float *S_T_rev, bool bidir, const int *cu,
+                    const Staged &staged) {
     const Layout L = layout(p, bidir ? 2 : 1, cu != nullptr);
     const int start = plan.record(0);
     for (int s = 1; s < kStreams; ++s) plan.wait(s, start);
     if (!bidir) {
-        plan_scan<T, D>(plan, p, p->reverse, scan_bufs(p, L, 0), p->S_T, 1, 0, 2, 0, nullptr, cu);
+        plan_scan<T, D>(plan, p, p->reverse, scan_bufs(p, L, 0), p->S_T, 1, 0, 2, 0, nullptr, cu, staged);
     } else {
         plan_bidir<T, D>(plan, p, S_T_rev, L);
     }
@@ -546,11 +567,12 @@ gdn_status plan_fwd(Plan &plan, const gdn_fwd_params *p, float *S_T_rev, bool bi
     return GDN_OK;
 }
 
-gdn_status make_plan(Plan &plan, const gdn_fwd_params *p, float *S_T_rev, bool bidir, const int *cu = nullptr) {
-    if (p->io_dtype == GDN_BF16 && p->Dk == 128) return plan_fwd<bf16, 128>(plan, p, S_T_rev, bidir, cu);
-    if (p->io_dtype == GDN_BF16 && p->Dk == 64) return plan_fwd<bf16, 64>(plan, p, S_T_rev, bidir, cu);
-    if (p->io_dtype == GDN_F32 && p->Dk == 128) return plan_fwd<float, 128>(plan, p, S_T_rev, bidir, cu);
-    if (p->io_dtype == GDN_F32 && p->Dk == 64) return plan_fwd<float, 64>(plan, p, S_T_rev, bidir, cu);
+gdn_status make_plan(Plan &plan, const gdn_fwd_params *p, float *S_T_rev, bool bidir, const int *cu = nullptr,
+                     const Staged &staged = Staged()) {
+    if (p->io_dtype == GDN_BF16 && p->Dk == 128) return plan_fwd<bf16, 128>(plan, p, S_T_rev, bidir, cu, staged);
+    if (p->io_dtype == GDN_BF16 && p->Dk == 64) return plan_fwd<bf16, 64>(plan, p, S_T_rev, bidir, cu, staged);
+    if (p->io_dtype == GDN_F32 && p->Dk == 128) return plan_fwd<float, 128>(plan, p, S_T_rev, bidir, cu, staged);
+    if (p->io_dtype == GDN_F32 && p->Dk == 64) return plan_fwd<float, 64>(plan, p, S_T_rev, bidir, cu, staged);
     return GDN_ERR_UNSUPPORTED;
 }
 
@@ -713,6 +735,28 @@ gdn_status gdn_internal::fwd_check(const gdn_fwd_params *p) {
 
 gdn_status gdn_internal::fwd_call(const gdn_fwd_params *p, hipEvent_t *timing, int n_timing, hipStream_t s) {
     return call(p, nullptr, false, timing, n_timing, s);
+}
+
+void gdn_internal::scan_range_bounds(const gdn_fwd_params *p, std::vector<int> &bounds) {
+    const int NC = n_chunks(p->T), R = n_ranges(NC);
+    bounds.resize(R + 1);
+    for (int i = 0; i <= R; ++i) bounds[i] = range_begin(NC, R, i);
+}
+
+gdn_status gdn_internal::fwd_call_staged(const gdn_fwd_params *p, const std::vector<std::vector<ExtLaunch>> &post,
+                                         hipStream_t s) {
+    if (!sizes_ok(p)) return GDN_ERR_INVALID_ARG;
+    gdn_status st = validate(p, nullptr, 1, (size_t)p->B * p->T, false);
+    if (st != GDN_OK) return st;
+    if ((int)post.size() != n_ranges(n_chunks(p->T))) return GDN_ERR_INVALID_ARG;
+    Staged staged;
+    staged.post = &post;
+    Plan plan;
+    st = make_plan(plan, p, nullptr, false, nullptr, staged);
+    if (st != GDN_OK) return st;
+    st = set_attributes();
+    if (st != GDN_OK) return st;
+    return run_plan(plan, s, nullptr, true);
 }
 
 extern "C" {

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "../../include/gdn.h"
 
 namespace gdn_internal {
@@ -30,8 +32,28 @@ inline int dtype_code(const gdn_dtype &d) {
     return v;
 }
 
+// A kernel launch of another part of the library, placed inside a layer
+// call's launch plan (the argument bytes are copied).
+struct ExtLaunch {
+    const void *fn;
+    dim3 grid, block;
+    size_t smem;
+    unsigned char args[160];
+    const char *name;
+};
+
 // Every check gdn_fwd makes, without launching anything.
 GDN_HIDDEN gdn_status fwd_check(const gdn_fwd_params *p);
+// The chunk ranges a one-scan layer call runs: R + 1 bounds in chunks, 0 first
+// and ceil(T / 64) last; range i is chunks [bounds[i], bounds[i+1]) of every
+// batch row.
+GDN_HIDDEN void scan_range_bounds(const gdn_fwd_params *p, std::vector<int> &bounds);
+// gdn_fwd (one scan, equal lengths) with other launches woven into its plan:
+// post[i] (one entry per range) runs after the output kernel of range i, on
+// a library stream, in range order.  Nothing is checked here beyond what
+// gdn_fwd checks.
+GDN_HIDDEN gdn_status fwd_call_staged(const gdn_fwd_params *p, const std::vector<std::vector<ExtLaunch>> &post,
+                                      hipStream_t s);
 // gdn_fwd / gdn_fwd_timed (timing: NULL, or 2 events per launch).
 GDN_HIDDEN gdn_status fwd_call(const gdn_fwd_params *p, hipEvent_t *timing, int n_timing, hipStream_t s);
 

@@ -223,3 +223,40 @@ def test_mixer_batch_d128_no_bias():
     inp = gdn_inputs.generate_mixer(w, bias=False, seed=31)
     say(f"case: mixer {w.name}, no bias")
     compare_mixer(inp, w.H, w.D)
+
+
+def test_mixer_staged_equals_three_stages():
+    """The mixer runs its out-projection beside the layer, split by the
+    layer's chunk ranges and batch rows; its outputs must equal, bit for bit,
+    the three stages called one after another (gdn_in_proj, gdn_fwd,
+    gdn_out_proj).  B = 2, T = 24349 (381 chunks: three ranges and a ragged
+    last chunk), H = 3, d = 64, C = 192, with a random initial state; on a
+    side stream, three calls in a row (launched directly, recorded as a
+    launch graph, replayed)."""
+    w = gdn_inputs.MixerWorkload(97, "B2 T24349 H3 d64 C192", 2, 24349, 3, 64, 192)
+    inp = gdn_inputs.generate_mixer(w, seed=41)
+    H, D = w.H, w.D
+    B, T, C = inp["x"].shape
+    say(f"case: mixer {w.name}, against its three stages")
+    x, w_in, w_out = (_dev(inp[n], torch.bfloat16) for n in ("x", "w_in", "w_out"))
+    A_log, b_in, b_out, norm_w = (_dev(inp[n]) for n in ("A_log", "b_in", "b_out", "norm_w"))
+    conv_q, conv_k, conv_v = (_dev(inp[n]) for n in ("conv_q", "conv_k", "conv_v"))
+    S0 = _dev((0.05 * np.random.default_rng(42).standard_normal((B, H, D, D))).astype(np.float32))
+    q, k, v, g, beta, log_a = gdn.gdn_in_proj(x, w_in, A_log, H, D, b_in=b_in)
+    y, s_ref = gdn.gdn_fwd(q, k, v, log_a, beta, g, conv_q, conv_k, conv_v, norm_w, S0)
+    o_ref = gdn.gdn_out_proj(y, w_out, b_out)
+    torch.cuda.synchronize()
+    ws = torch.empty(gdn.gdn_mixer_workspace_bytes(B, T, H, D, C), dtype=torch.uint8, device="cuda")
+    out, S_T = torch.empty_like(o_ref), torch.empty_like(s_ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for rep in range(3):
+        out.fill_(float("nan"))
+        S_T.fill_(float("nan"))
+        torch.cuda.synchronize()
+        with torch.cuda.stream(side):
+            gdn.gdn_mixer_fwd(x, w_in, A_log, conv_q, conv_k, conv_v, w_out, H, D, b_in=b_in, b_out=b_out,
+                              norm_w=norm_w, S0=S0, out=out, S_T=S_T, workspace=ws, stream=side)
+        torch.cuda.synchronize()
+        assert torch.equal(out, o_ref) and torch.equal(S_T, s_ref), f"call {rep} differs from the three stages"
+    say("  3 calls equal to the three stages, bit for bit")
