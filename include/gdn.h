@@ -52,8 +52,8 @@
  * memory and is not meant for capture.
  *
  * Graph cache.  Outside a capture, on a stream other than the null stream,
- * gdn_fwd, gdn_fwd_varlen and the layer stage of gdn_mixer_fwd record their
- * launches as a HIP graph (a capture of `stream`, in thread-local mode,
+ * gdn_fwd, gdn_fwd_varlen and gdn_mixer_fwd (its layer and out-projection)
+ * record their launches as a HIP graph (a capture of `stream`, in thread-local mode,
  * inside the call) the second time a call has the same launches (the same
  * sizes, pointers and scalars; the first such call launches directly), and
  * replay the graph for every later such call.  The result is the same as
@@ -271,8 +271,12 @@ gdn_status gdn_out_proj(const gdn_out_proj_params *p, struct ihipStream_t *strea
 
 /*
  * The whole token mixer: gdn_in_proj, then the layer (gdn_fwd, forward scan,
- * bf16), then gdn_out_proj, all on `stream`:
+ * bf16), then gdn_out_proj, as one call ordered on `stream`:
  *   out = out_proj( GDN layer( in_proj(x) ) )
+ * The out-projection runs in parts, one per chunk range of the layer's launch
+ * plan, each on a library stream right after the layer's output kernel of
+ * that range (so beside the layer's later ranges); the result is the same,
+ * bit for bit, as the three stages called one after another.
  * The intermediates (q, k, v, gate, b, log a and the layer output y) live in
  * the caller's workspace, of at least gdn_mixer_workspace_bytes() bytes,
  * 256-byte aligned (that function reads B, T, H, D, C only and returns 0 for
