@@ -165,6 +165,9 @@ __global__ __launch_bounds__(gemm::THREADS, 2) void gdn_gemm_kernel(GemmArgs a) 
     // the 8 X fragments of kb.  W fragments are read two groups ahead, the X
     // fragments of kb = 1 during kb = 0.
     frag xf[2][8], wf[3];
+    // 16-column tiles of this wave that hold output columns (fewer only in
+    // the last column tile: N = 4 H D + 2 H leaves its gate columns there)
+    const int live_tiles = min(4, max(0, (a.N - (n0 + 64 * wn) + 15) / 16));
     for (int s = 0; s < S; ++s) {
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         lds_barrier();
@@ -188,8 +191,10 @@ __global__ __launch_bounds__(gemm::THREADS, 2) void gdn_gemm_kernel(GemmArgs a) 
                 xf[1][2 * q + 1] = xfrag(1, 2 * q + 1);
             }
             __builtin_amdgcn_sched_barrier(0);
+            if ((q & 3) < live_tiles) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[q & 3][j] = Mf::mma(wf[q % 3], xf[q >> 2][j], acc[q & 3][j]);
+                for (int j = 0; j < 8; ++j) acc[q & 3][j] = Mf::mma(wf[q % 3], xf[q >> 2][j], acc[q & 3][j]);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     }
